@@ -1,0 +1,174 @@
+"""CPU oracle for the fp16 GEMM (+ bias, + erf-GELU) -- TEST INFRASTRUCTURE ONLY.
+
+Only the test suite, ``__graft_entry__.smoke()`` and the ``cpu_baseline`` leg of
+``bench.py`` may import this package.  The product path (the HIP library and its
+Python binding) never imports, links or calls it, and the two share no code.
+
+The arithmetic lives in ``gemm_oracle.c`` (plain C, fp64 accumulation, its own
+binary16 codec, ``erf``/``erfc`` from the host libm); this module only builds it with
+gcc and marshals numpy arrays through ctypes.  What it computes follows "Designing
+High-Performance GPU Kernels with TileLang: Tensor-Core GEMM, Fused Softmax,
+FlashAttention, and Autotuning": the thecryptopost.io page, section 2 ("Memory
+hierarchy - tiled tensor-core GEMM", ``make_matmul``: A (M, K), B (K, N), C (M, N)
+float16 row-major) for the product, and the ainovat.com page's fused-epilogue
+paragraph for ``GELU(acc + bias)`` before the single fp16 write.
+
+Every function here is pinned by ``tests/test_oracle.py`` (closed forms, exhaustive
+codec checks against numpy, exact rational brute force); none is "parity unpinned".
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+SOURCE = os.path.join(_HERE, "gemm_oracle.c")
+LIBRARY = os.path.join(_HERE, "liboracle_gemm.so")
+
+EPI_NONE, EPI_BIAS, EPI_BIAS_GELU = 0, 1, 2
+EPILOGUES = {"none": EPI_NONE, "bias": EPI_BIAS, "bias_gelu": EPI_BIAS_GELU}
+
+_lib = None
+
+
+def compile_command(source: str = SOURCE, output: str = LIBRARY) -> list[str]:
+    return ["gcc", "-O2", "-fopenmp", "-ffp-contract=off", "-fPIC", "-shared",
+            "-std=c11", "-Wall", "-Wextra", source, "-o", output, "-lm"]
+
+
+def build(source: str = SOURCE, output: str = LIBRARY) -> str:
+    """Compile the oracle into a shared library (always recompiles)."""
+    tmp = output + ".tmp%d" % os.getpid()
+    subprocess.run(compile_command(source, tmp), check=True)
+    os.replace(tmp, output)
+    return output
+
+
+def load(path: str | None = None, rebuild_if_missing: bool = True) -> ctypes.CDLL:
+    """Load the oracle library (building it first if it is not there)."""
+    global _lib
+    if path is None and _lib is not None:
+        return _lib
+    target = path or LIBRARY
+    if not os.path.exists(target):
+        if not rebuild_if_missing:
+            raise FileNotFoundError(target)
+        build(output=target)
+    lib = ctypes.CDLL(target)
+    _declare(lib)
+    if path is None:
+        _lib = lib
+    return lib
+
+
+def _declare(lib: ctypes.CDLL) -> None:
+    i64, p = ctypes.c_int64, ctypes.c_void_p
+    lib.oracle_gemm.argtypes = [i64, i64, i64, p, p, p, ctypes.c_int, p]
+    lib.oracle_gemm.restype = ctypes.c_int
+    lib.oracle_gemm_sampled.argtypes = [i64, i64, i64, p, p, p, ctypes.c_int, i64, p, p, p]
+    lib.oracle_gemm_sampled.restype = ctypes.c_int
+    for name in ("oracle_f16_to_f64_array", "oracle_f64_to_f16_array", "oracle_gelu_array"):
+        getattr(lib, name).argtypes = [i64, p, p]
+        getattr(lib, name).restype = None
+
+
+def _ptr(a: np.ndarray | None):
+    return None if a is None else a.ctypes.data_as(ctypes.c_void_p)
+
+
+def _bits(a) -> np.ndarray:
+    """Accept a numpy float16/uint16 array or a CPU torch float16 tensor; return the
+    contiguous uint16 bit pattern."""
+    if hasattr(a, "detach"):  # torch tensor, kept optional so numpy-only callers work
+        a = a.detach().cpu().contiguous().view(dtype=_torch_int16()).numpy()
+    a = np.ascontiguousarray(a)
+    if a.dtype == np.float16:
+        a = a.view(np.uint16)
+    elif a.dtype == np.int16:
+        a = a.view(np.uint16)
+    if a.dtype != np.uint16:
+        raise TypeError("expected float16 / uint16 bit patterns, got %s" % a.dtype)
+    return a
+
+
+def _torch_int16():
+    import torch
+    return torch.int16
+
+
+def f16_to_f64(bits, lib=None) -> np.ndarray:
+    lib = lib or load()
+    b = _bits(bits)
+    out = np.empty(b.shape, dtype=np.float64)
+    lib.oracle_f16_to_f64_array(b.size, _ptr(b), _ptr(out))
+    return out
+
+
+def f64_to_f16(x, lib=None) -> np.ndarray:
+    """Round fp64 values to fp16 (RNE); returns uint16 bit patterns."""
+    lib = lib or load()
+    x = np.ascontiguousarray(x, dtype=np.float64)
+    out = np.empty(x.shape, dtype=np.uint16)
+    lib.oracle_f64_to_f16_array(x.size, _ptr(x), _ptr(out))
+    return out
+
+
+def gelu(x, lib=None) -> np.ndarray:
+    lib = lib or load()
+    x = np.ascontiguousarray(x, dtype=np.float64)
+    out = np.empty(x.shape, dtype=np.float64)
+    lib.oracle_gelu_array(x.size, _ptr(x), _ptr(out))
+    return out
+
+
+def _epi_code(epilogue) -> int:
+    if isinstance(epilogue, str):
+        return EPILOGUES[epilogue]
+    return int(epilogue)
+
+
+def gemm(A, B, bias=None, epilogue="none", lib=None) -> np.ndarray:
+    """C = fp16(epi(A @ B [+ bias])) with fp64 accumulation; returns uint16 bits (M, N)."""
+    lib = lib or load()
+    a, b = _bits(A), _bits(B)
+    if a.ndim != 2 or b.ndim != 2 or a.shape[1] != b.shape[0]:
+        raise ValueError("shape mismatch %s x %s" % (a.shape, b.shape))
+    M, K = a.shape
+    N = b.shape[1]
+    epi = _epi_code(epilogue)
+    bb = _bits(bias) if bias is not None else None
+    if epi != EPI_NONE and (bb is None or bb.size != N):
+        raise ValueError("bias of length N required for epilogue %r" % (epilogue,))
+    out = np.empty((M, N), dtype=np.uint16)
+    rc = lib.oracle_gemm(M, N, K, _ptr(a), _ptr(b), _ptr(bb), epi, _ptr(out))
+    if rc != 0:
+        raise ValueError("oracle_gemm rejected its arguments (rc=%d)" % rc)
+    return out
+
+
+def gemm_sampled(A, B, rows, cols, bias=None, epilogue="none", lib=None) -> np.ndarray:
+    """Selected output elements C[rows[s], cols[s]] (uint16 bits), each computed exactly
+    as the full product computes it."""
+    lib = lib or load()
+    a, b = _bits(A), _bits(B)
+    M, K = a.shape
+    N = b.shape[1]
+    if b.shape[0] != K:
+        raise ValueError("shape mismatch %s x %s" % (a.shape, b.shape))
+    epi = _epi_code(epilogue)
+    bb = _bits(bias) if bias is not None else None
+    if epi != EPI_NONE and (bb is None or bb.size != N):
+        raise ValueError("bias of length N required for epilogue %r" % (epilogue,))
+    r = np.ascontiguousarray(rows, dtype=np.int64)
+    c = np.ascontiguousarray(cols, dtype=np.int64)
+    if r.shape != c.shape:
+        raise ValueError("rows and cols differ in shape")
+    out = np.empty(r.shape, dtype=np.uint16)
+    rc = lib.oracle_gemm_sampled(M, N, K, _ptr(a), _ptr(b), _ptr(bb), epi, r.size,
+                                 _ptr(r), _ptr(c), _ptr(out))
+    if rc != 0:
+        raise ValueError("oracle_gemm_sampled rejected its arguments (rc=%d)" % rc)
+    return out

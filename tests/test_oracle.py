@@ -1,0 +1,386 @@
+"""Pins for the CPU oracle (runs without a GPU).
+
+Each test ties the oracle to something other than itself: numpy's own binary16
+conversions (exhaustive), IEEE 754 rounding cases, normal-CDF table values and scipy's
+``ndtr``, exact rational arithmetic (``fractions.Fraction``) on tiny shapes, numpy's
+fp64 matmul, and closed forms (all-ones, selection and permutation matrices, zero
+operands, transposition).  ``test_oracle_mutants.py`` checks that plausible mistakes
+planted in the oracle's C source fail at least one of these pins.
+"""
+from __future__ import annotations
+
+import bisect
+import os
+from fractions import Fraction
+
+import numpy as np
+import pytest
+from scipy.special import ndtr
+
+import oracle
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+ALL_BITS = np.arange(1 << 16, dtype=np.uint32).astype(np.uint16)
+
+
+def _lib(request):
+    return getattr(request, "param", None) or oracle.load()
+
+
+# ---------------------------------------------------------------- fp16 codec --------
+
+def test_decode_exhaustive_matches_numpy(oracle_lib):
+    got = oracle.f16_to_f64(ALL_BITS, lib=oracle_lib)
+    ref = ALL_BITS.view(np.float16).astype(np.float64)
+    nan = np.isnan(ref)
+    assert np.array_equal(np.isnan(got), nan)
+    assert np.array_equal(got[~nan], ref[~nan])
+    # signs of zero too
+    assert np.array_equal(np.signbit(got[~nan]), np.signbit(ref[~nan]))
+
+
+def test_encode_roundtrip_every_finite_pattern(oracle_lib):
+    vals = ALL_BITS.view(np.float16).astype(np.float64)
+    finite = np.isfinite(vals)
+    back = oracle.f64_to_f16(vals[finite], lib=oracle_lib)
+    assert np.array_equal(back, ALL_BITS[finite])
+    inf_bits = oracle.f64_to_f16(np.array([np.inf, -np.inf]), lib=oracle_lib)
+    assert list(inf_bits) == [0x7C00, 0xFC00]
+    assert oracle.f64_to_f16(np.array([np.nan]), lib=oracle_lib)[0] & 0x7FFF > 0x7C00
+
+
+def _midpoints():
+    """Midpoints between adjacent finite fp16 values (both signs), and each midpoint
+    nudged one fp64 ulp either way."""
+    pos = np.arange(0, 0x7C00, dtype=np.uint32).astype(np.uint16).view(np.float16)
+    v = pos.astype(np.float64)
+    mids = (v[:-1] + v[1:]) / 2.0          # exact in fp64
+    mids = np.concatenate([mids, [65520.0]])
+    allm = np.concatenate([mids, -mids])
+    return np.concatenate([allm, np.nextafter(allm, np.inf), np.nextafter(allm, -np.inf)])
+
+
+def test_encode_midpoints_match_numpy(oracle_lib):
+    x = _midpoints()
+    got = oracle.f64_to_f16(x, lib=oracle_lib)
+    with np.errstate(over="ignore"):
+        ref = x.astype(np.float16).view(np.uint16)
+    assert np.array_equal(got, ref)
+
+
+def test_encode_random_doubles_match_numpy(oracle_lib):
+    rng = np.random.default_rng(1234)
+    mag = np.exp2(rng.uniform(-30, 17, size=400_000))
+    x = mag * rng.choice([-1.0, 1.0], size=mag.size)
+    got = oracle.f64_to_f16(x, lib=oracle_lib)
+    with np.errstate(over="ignore"):
+        ref = x.astype(np.float16).view(np.uint16)
+    assert np.array_equal(got, ref)
+
+
+def _parse_float(tok: str) -> float:
+    return float.fromhex(tok) if "0x" in tok else float(tok)
+
+
+def test_encode_ieee_golden_cases(oracle_lib):
+    rows = []
+    with open(os.path.join(GOLDEN, "f16_rounding_cases.txt")) as f:
+        for line in f:
+            if line.startswith("#") or not line.strip():
+                continue
+            tok = line.split()
+            rows.append((_parse_float(tok[0]), int(tok[1], 16), line.strip()))
+    assert len(rows) >= 15
+    got = oracle.f64_to_f16(np.array([r[0] for r in rows]), lib=oracle_lib)
+    for (x, want, line), g in zip(rows, got):
+        assert int(g) == want, line
+
+
+# ---------------------------------------------------------------- GELU --------------
+
+def _gelu_points():
+    pts = []
+    with open(os.path.join(GOLDEN, "gelu_points.txt")) as f:
+        for line in f:
+            if line.startswith("#") or not line.strip():
+                continue
+            x, phi = (float(t) for t in line.split())
+            pts.append((x, phi))
+    return pts
+
+
+def test_gelu_table_points(oracle_lib):
+    pts = _gelu_points()
+    x = np.array([p[0] for p in pts])
+    want = x * np.array([p[1] for p in pts])
+    got = oracle.gelu(x, lib=oracle_lib)
+    assert got[x == 0.0][0] == 0.0
+    np.testing.assert_allclose(got, want, rtol=4e-15, atol=0)  # a few ulp of libm erf
+
+
+def test_gelu_matches_scipy_ndtr_on_a_dense_grid(oracle_lib):
+    x = np.linspace(-12.0, 12.0, 200_001)
+    got = oracle.gelu(x, lib=oracle_lib)
+    want = x * ndtr(x)
+    # relative agreement wherever the value is not deep in the underflowing tail
+    big = np.abs(want) > 1e-300
+    np.testing.assert_allclose(got[big], want[big], rtol=1e-13, atol=0)
+
+
+def test_gelu_odd_part_identity_and_minimum(oracle_lib):
+    x = np.linspace(0.0, 8.0, 4001)
+    d = oracle.gelu(x, lib=oracle_lib) - oracle.gelu(-x, lib=oracle_lib)
+    np.testing.assert_allclose(d, x, rtol=0, atol=4e-15)
+    grid = np.linspace(-3, 0, 300_001)
+    g = oracle.gelu(grid, lib=oracle_lib)
+    i = int(np.argmin(g))
+    assert abs(grid[i] - (-0.7517915)) < 2e-5
+    assert abs(g[i] - (-0.1699712)) < 1e-6
+
+
+def test_gelu_fp16_large_x_limits_exhaustive(oracle_lib):
+    """Over every finite fp16 x: fp16(GELU(x)) == x for x >= 3.5, and -0 for x <=
+    -5.7265625; everywhere, the oracle agrees with numpy's rounding of x*ndtr(x) except
+    at fp16 near-ties."""
+    x = ALL_BITS.view(np.float16).astype(np.float64)
+    fin = np.isfinite(x)
+    xs = x[fin]
+    g = oracle.gelu(xs, lib=oracle_lib)
+    bits = oracle.f64_to_f16(g, lib=oracle_lib)
+    big = xs >= 3.5
+    assert np.array_equal(bits[big], ALL_BITS[fin][big])
+    neg = xs <= -5.7265625
+    assert np.all(bits[neg] == 0x8000)
+    ref = (xs * ndtr(xs)).astype(np.float16).view(np.uint16)
+    diff = np.nonzero(bits != ref)[0]
+    for i in diff:  # only near-ties may differ: check the two fp64 values straddle a midpoint
+        a, b = g[i], xs[i] * ndtr(xs[i])
+        assert abs(a - b) <= 1e-13 * max(abs(a), 1e-300), (xs[i], a, b)
+
+
+# ---------------------------------------------------------------- GEMM core ---------
+
+def _f16_table():
+    bits = np.arange(0, 0x7C00, dtype=np.uint32).astype(np.uint16)
+    vals = [Fraction(float(v)) for v in bits.view(np.float16).astype(np.float64)]
+    return vals, bits
+
+
+_TABLE = None
+
+
+def fraction_to_f16(x: Fraction):
+    """Correctly rounded (ties to even) fp16 bits of an exact rational; also returns
+    the distance to the nearest fp16 midpoint, relative to |x| (for near-tie checks)."""
+    global _TABLE
+    if _TABLE is None:
+        _TABLE = _f16_table()
+    vals, bits = _TABLE
+    sign = 0x8000 if x < 0 else 0
+    a = -x if x < 0 else x
+    if a >= 65520:
+        return sign | 0x7C00, Fraction(1)
+    j = bisect.bisect_left(vals, a)
+    if j < len(vals) and vals[j] == a:
+        return sign | int(bits[j]), Fraction(1)
+    lo, hi = vals[j - 1], (vals[j] if j < len(vals) else Fraction(65536))
+    mid = (lo + hi) / 2
+    if a < mid:
+        pick = j - 1
+    elif a > mid:
+        pick = j
+    else:
+        pick = j - 1 if int(bits[j - 1]) % 2 == 0 else j
+    out = int(bits[pick]) if pick < len(bits) else 0x7C00
+    dist = abs(a - mid) / a if a else Fraction(1)
+    return sign | out, dist
+
+
+def _random_f16(rng, shape, with_subnormals=True):
+    x = rng.standard_normal(shape) * np.exp2(rng.integers(-6, 4, size=shape))
+    h = x.astype(np.float16)
+    if with_subnormals:
+        sub = rng.random(shape) < 0.1
+        h[sub] = (rng.integers(-1023, 1024, size=int(sub.sum())) * 2.0 ** -24).astype(np.float16)
+    return h
+
+
+def _exact_product(A, B, bias=None):
+    A64 = A.astype(np.float64)
+    B64 = B.astype(np.float64)
+    M, K = A.shape
+    N = B.shape[1]
+    out = [[None] * N for _ in range(M)]
+    mag = [[None] * N for _ in range(M)]
+    for i in range(M):
+        for j in range(N):
+            s = Fraction(0)
+            m = 0.0
+            for k in range(K):
+                s += Fraction(float(A64[i, k])) * Fraction(float(B64[k, j]))
+                m += abs(float(A64[i, k]) * float(B64[k, j]))
+            if bias is not None:
+                s += Fraction(float(bias.astype(np.float64)[j]))
+                m += abs(float(bias.astype(np.float64)[j]))
+            out[i][j] = s
+            mag[i][j] = m
+    return out, mag
+
+
+@pytest.mark.parametrize("shape", [(1, 1, 1), (2, 3, 5), (3, 2, 7), (5, 7, 3), (7, 5, 16),
+                                   (16, 16, 16), (3, 16, 1), (1, 7, 16)])
+@pytest.mark.parametrize("epi", ["none", "bias"])
+def test_gemm_matches_exact_rational_bruteforce(oracle_lib, shape, epi):
+    M, N, K = shape
+    rng = np.random.default_rng(M * 100 + N * 10 + K)
+    A = _random_f16(rng, (M, K))
+    B = _random_f16(rng, (K, N))
+    bias = _random_f16(rng, (N,)) if epi == "bias" else None
+    got = oracle.gemm(A, B, bias, epi, lib=oracle_lib)
+    exact, mag = _exact_product(A, B, bias)
+    for i in range(M):
+        for j in range(N):
+            want, dist = fraction_to_f16(exact[i][j])
+            if int(got[i, j]) == want:
+                continue
+            # fp64 summation may only flip a correctly rounded result at a near-tie:
+            # |fp64 sum - exact| <= (K+1) * 2^-53 * sum|terms|
+            bound = (K + 2) * 2.0 ** -53 * mag[i][j]
+            assert exact[i][j] != 0 and float(dist) * abs(float(exact[i][j])) <= bound, \
+                (shape, i, j, hex(int(got[i, j])), hex(want))
+
+
+def test_gemm_bias_gelu_against_exact_sum_and_ndtr(oracle_lib):
+    rng = np.random.default_rng(99)
+    M, N, K = 6, 9, 13
+    A, B, bias = _random_f16(rng, (M, K)), _random_f16(rng, (K, N)), _random_f16(rng, (N,))
+    got = oracle.gemm(A, B, bias, "bias_gelu", lib=oracle_lib)
+    exact, _ = _exact_product(A, B, bias)
+    for i in range(M):
+        for j in range(N):
+            x = float(exact[i][j])
+            ref_val = x * float(ndtr(x))
+            want = int(np.array([ref_val]).astype(np.float16).view(np.uint16)[0])
+            if int(got[i, j]) != want:
+                # allowed only when ref_val lies within 1e-12 (relative) of a midpoint
+                _, dist = fraction_to_f16(Fraction(ref_val))
+                assert float(dist) < 1e-12, (i, j, x)
+
+
+@pytest.mark.parametrize("shape", [(256, 256, 256), (1000, 3000, 777)])
+def test_gemm_matches_numpy_fp64_matmul(oracle_lib, shape):
+    """Library special case: numpy's fp64 matmul rounded once to fp16.  Only near-ties
+    (where the two fp64 sums straddle an fp16 midpoint) may differ."""
+    import workloads
+    M, N, K = shape
+    A, B, _ = workloads.make_inputs(M, N, K, "uniform" if K == 777 else "normal", seed=3)
+    A = A.numpy()
+    B = B.numpy()
+    got = oracle.gemm(A, B, lib=oracle_lib)
+    A64, B64 = A.astype(np.float64), B.astype(np.float64)
+    s = A64 @ B64
+    ref = s.astype(np.float16).view(np.uint16)
+    bad = np.nonzero(got != ref)
+    n_bad = bad[0].size
+    assert n_bad <= 1e-4 * M * N
+    if n_bad:
+        mag = np.abs(A64) @ np.abs(B64)
+        g = got[bad].view(np.float16).astype(np.float64)
+        r = ref[bad].view(np.float16).astype(np.float64)
+        mid = (g + r) / 2.0
+        assert np.all(np.abs(s[bad] - mid) <= 2 * K * 2.0 ** -53 * mag[bad])
+        # and the two candidates are adjacent fp16 values
+        assert np.all(np.abs(got[bad].astype(np.int32) - ref[bad].astype(np.int32)) == 1)
+
+
+@pytest.mark.parametrize("K", [1, 256, 777, 2048, 8192])
+def test_all_ones_gives_K(oracle_lib, K):
+    M, N = 3, 5
+    A = np.ones((M, K), np.float16)
+    B = np.ones((K, N), np.float16)
+    got = oracle.gemm(A, B, lib=oracle_lib).view(np.float16)
+    assert np.all(got.astype(np.float64) == float(K))
+
+
+def test_selection_matrices_copy_rows_and_columns(oracle_lib):
+    rng = np.random.default_rng(7)
+    M, N, K = 37, 29, 11
+    B = _random_f16(rng, (K, N))
+    A_sel = np.zeros((M, K), np.float16)
+    A_sel[np.arange(M), np.arange(M) % K] = 1
+    got = oracle.gemm(A_sel, B, lib=oracle_lib)
+    assert np.array_equal(got, B.view(np.uint16)[np.arange(M) % K])
+    A = _random_f16(rng, (M, K))
+    B_sel = np.zeros((K, N), np.float16)
+    B_sel[np.arange(N) % K, np.arange(N)] = 1
+    got = oracle.gemm(A, B_sel, lib=oracle_lib)
+    assert np.array_equal(got, A.view(np.uint16)[:, np.arange(N) % K])
+
+
+def test_identity_and_permutation(oracle_lib):
+    rng = np.random.default_rng(8)
+    n = 24
+    B = _random_f16(rng, (n, 17))
+    eye = np.eye(n, dtype=np.float16)
+    assert np.array_equal(oracle.gemm(eye, B, lib=oracle_lib), B.view(np.uint16))
+    perm = rng.permutation(n)
+    P = eye[perm]
+    assert np.array_equal(oracle.gemm(P, B, lib=oracle_lib), B.view(np.uint16)[perm])
+    A = _random_f16(rng, (9, n))
+    assert np.array_equal(oracle.gemm(A, eye, lib=oracle_lib), A.view(np.uint16))
+
+
+def test_zero_operand_and_empty_k(oracle_lib):
+    rng = np.random.default_rng(9)
+    A = np.zeros((5, 8), np.float16)
+    B = _random_f16(rng, (8, 6))
+    bias = _random_f16(rng, (6,))
+    got = oracle.gemm(A, B, lib=oracle_lib).view(np.float16)
+    assert np.all(got == 0)
+    # A = 0 reduces the epilogue to a function of the bias alone: column j gets bias[j]
+    got_b = oracle.gemm(A, B, bias, "bias", lib=oracle_lib)
+    assert np.array_equal(got_b, np.broadcast_to(bias.view(np.uint16), (5, 6)))
+    got_g = oracle.gemm(A, B, bias, "bias_gelu", lib=oracle_lib)
+    bx = bias.astype(np.float64)
+    want = (bx * ndtr(bx)).astype(np.float16).view(np.uint16)
+    assert np.array_equal(got_g, np.broadcast_to(want, (5, 6)))
+    # K = 0: an empty sum, C = epi(bias or 0)
+    A0 = np.zeros((4, 0), np.float16)
+    B0 = np.zeros((0, 6), np.float16)
+    assert np.all(oracle.gemm(A0, B0, lib=oracle_lib) == 0)
+    assert np.array_equal(oracle.gemm(A0, B0, bias, "bias_gelu", lib=oracle_lib),
+                          np.broadcast_to(want, (4, 6)))
+
+
+def test_transpose_and_row_permutation_invariance(oracle_lib):
+    rng = np.random.default_rng(10)
+    A = _random_f16(rng, (23, 31))
+    B = _random_f16(rng, (31, 19))
+    C = oracle.gemm(A, B, lib=oracle_lib)
+    Ct = oracle.gemm(np.ascontiguousarray(B.T), np.ascontiguousarray(A.T), lib=oracle_lib)
+    assert np.array_equal(C.T, Ct)
+    perm = rng.permutation(23)
+    assert np.array_equal(oracle.gemm(A[perm], B, lib=oracle_lib), C[perm])
+
+
+def test_sampled_equals_full(oracle_lib):
+    import workloads
+    A, B, bias = workloads.make_inputs(70, 90, 130, "normal", with_bias=True, seed=5)
+    for epi in ("none", "bias", "bias_gelu"):
+        full = oracle.gemm(A, B, bias, epi, lib=oracle_lib)
+        rng = np.random.default_rng(1)
+        r = rng.integers(0, 70, 500)
+        c = rng.integers(0, 90, 500)
+        s = oracle.gemm_sampled(A, B, r, c, bias, epi, lib=oracle_lib)
+        assert np.array_equal(s, full[r, c])
+
+
+def test_rejects_bad_arguments(oracle_lib):
+    A = np.zeros((2, 3), np.float16)
+    B = np.zeros((3, 4), np.float16)
+    with pytest.raises(ValueError):
+        oracle.gemm(A, B, None, "bias", lib=oracle_lib)
+    with pytest.raises(ValueError):
+        oracle.gemm(A, np.zeros((2, 4), np.float16), lib=oracle_lib)
+    with pytest.raises(ValueError):
+        oracle.gemm_sampled(A, B, [2], [0], lib=oracle_lib)

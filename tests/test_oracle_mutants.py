@@ -1,0 +1,70 @@
+"""Plant plausible mistakes in the oracle's C source and check that the pins in
+``test_oracle.py`` catch every one of them (runs on the CPU only).
+
+Each mutant is a textual edit of ``oracle/gemm_oracle.c`` compiled into a temporary
+directory; the pins run against it in a child process (a mutant that reads out of bounds
+may crash, which also counts as caught).
+"""
+from __future__ import annotations
+
+import os
+import subprocess
+import sys
+
+import pytest
+
+import oracle
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+# (name, [(old, new), ...]); every "old" must occur in the source.
+MUTANTS = [
+    ("drop_first_k_term", [("for (int64_t k = 0; k < K; ++k)", "for (int64_t k = 1; k < K; ++k)")]),
+    ("drop_last_k_term", [("for (int64_t k = 0; k < K; ++k)", "for (int64_t k = 0; k + 1 < K; ++k)")]),
+    ("transposed_B", [("Bd[k * N + j]", "Bd[j * K + k]"), ("B[k * N + j]", "B[j * K + k]")]),
+    ("transposed_A", [("Ad[i * K + k]", "Ad[k * M + i]"),
+                      ("A[i * K + k]", "A[k * (N + 0) + i]")]),
+    ("bias_by_row", [("oracle_f16_to_f64(bias[j])", "oracle_f16_to_f64(bias[i % N])")]),
+    ("gelu_erfc_sign", [("erfc(-x / sqrt(2.0))", "erfc(x / sqrt(2.0))")]),
+    ("gelu_tanh_form", [("0.5 * x * (1.0 + erf(x / sqrt(2.0)))",
+                         "0.5 * x * (1.0 + tanh(0.7978845608028654 * (x + 0.044715 * x * x * x)))")]),
+    ("gelu_missing", [("if (epi == 2) v = oracle_gelu(v);", "if (epi == 3) v = oracle_gelu(v);")]),
+    ("bias_missing", [("double v = s + bias_j;", "double v = s + 0.0 * bias_j;")]),
+    ("gelu_before_bias", [("double v = s + bias_j;\n    if (epi == 2) v = oracle_gelu(v);",
+                           "double v = s;\n    if (epi == 2) v = oracle_gelu(v);\n    v += bias_j;")]),
+    ("ties_away_from_zero", [("return (fmod(fl, 2.0) == 0.0) ? fl : fl + 1.0;", "return fl + 1.0;")]),
+    ("truncate_not_round", [("if (d > 0.5) return fl + 1.0;", "if (d > 1.5) return fl + 1.0;")]),
+    ("decode_exponent_bias", [("e - 25", "e - 24")]),
+    ("decode_subnormal_scale", [("ldexp((double)f, -24)", "ldexp((double)f, -25)")]),
+    ("decode_drops_sign", [("return sign ? -v : v;", "return v;")]),
+    ("overflow_unhandled", [("if (a >= 65520.0)", "if (a >= 1.0e300)")]),
+    ("subnormal_encode_flush", [("double n = round_half_even(ldexp(a, 24));", "double n = 0.0;")]),
+    ("fp32_accumulation", [("double s = 0.0;", "float s = 0.0f;"),
+                           ("for (int64_t j = 0; j < N; ++j) acc[j] += a * Bd[k * N + j];",
+                            "for (int64_t j = 0; j < N; ++j) acc[j] = (float)(acc[j] + a * Bd[k * N + j]);")]),
+]
+
+
+def test_every_mutation_applies():
+    src = open(oracle.SOURCE).read()
+    for name, edits in MUTANTS:
+        for old, _ in edits:
+            assert old in src, (name, old)
+
+
+@pytest.mark.parametrize("name,edits", MUTANTS, ids=[m[0] for m in MUTANTS])
+def test_pins_catch_mutant(tmp_path, name, edits):
+    src = open(oracle.SOURCE).read()
+    for old, new in edits:
+        src = src.replace(old, new)
+    csrc = tmp_path / "mutant.c"
+    csrc.write_text(src)
+    lib = tmp_path / "libmutant.so"
+    subprocess.run(oracle.compile_command(str(csrc), str(lib)), check=True,
+                   stdout=subprocess.DEVNULL, stderr=subprocess.DEVNULL)
+    env = dict(os.environ, ORACLE_LIB=str(lib), OMP_NUM_THREADS="4")
+    r = subprocess.run([sys.executable, "-m", "pytest", "-x", "-q", "-p", "no:cacheprovider",
+                        os.path.join(ROOT, "tests", "test_oracle.py")],
+                       cwd=ROOT, env=env, stdout=subprocess.PIPE, stderr=subprocess.STDOUT,
+                       timeout=600)
+    assert r.returncode != 0, "mutant %s survived every pin:\n%s" % (name, r.stdout.decode()[-2000:])
