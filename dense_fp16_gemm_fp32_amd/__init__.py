@@ -1,0 +1,211 @@
+"""Python binding of the mi355gemm C ABI (``include/mi355gemm.h``).
+
+Argument marshalling only: every step of the computation runs in the HIP kernels of
+``libmi355gemm.so``.  The ``mi355gemm_*`` functions mirror the C entry points one to one
+(raw integers for pointers and the stream); ``gemm()`` is the torch-tensor convenience
+wrapper that allocates ``out`` when it is not given, as the tutorial's kernels allocate
+their output (thecryptopost.io page, section 2, ``out_idx=[-1]``).
+
+There is no fallback: if the library is not built, or a call fails, an exception is
+raised.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch  # loaded first, so the library binds to the same HIP runtime as torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIBRARY = os.path.join(_PKG, "libmi355gemm.so")
+
+OK, EINVAL, EUNSUPPORTED, EHIP = 0, 1, 2, 3
+EPI_NONE, EPI_BIAS, EPI_BIAS_GELU = 0, 1, 2
+EPILOGUES = {"none": EPI_NONE, "bias": EPI_BIAS, "bias_gelu": EPI_BIAS_GELU}
+STATUS_NAMES = {OK: "OK", EINVAL: "EINVAL", EUNSUPPORTED: "EUNSUPPORTED", EHIP: "EHIP"}
+
+# Every symbol include/mi355gemm.h declares.
+EXPORTS = (
+    "mi355gemm_gemm", "mi355gemm_gemm_config", "mi355gemm_select", "mi355gemm_num_configs",
+    "mi355gemm_config_name", "mi355gemm_config_info", "mi355gemm_lds_budget",
+    "mi355gemm_last_error", "mi355gemm_version",
+)
+
+
+class GemmError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__("%s: %s" % (STATUS_NAMES.get(status, status), message))
+        self.status = status
+
+
+class ConfigDesc(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int) for n in (
+        "block_m", "block_n", "block_k", "stages", "waves_m", "waves_n", "threads",
+        "lds_bytes", "a_vector", "bc_vector", "group_m")]
+
+    def as_dict(self) -> dict:
+        return {n: getattr(self, n) for n, _ in self._fields_}
+
+
+_lib = None
+
+
+def library() -> ctypes.CDLL:
+    """The loaded ``libmi355gemm.so``; raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIBRARY):
+            raise ImportError(
+                "%s is not built; run `python -m dense_fp16_gemm_fp32_amd.build` "
+                "(or __graft_entry__.build()) first" % LIBRARY)
+        lib = ctypes.CDLL(LIBRARY)
+        i64, p, ci = ctypes.c_int64, ctypes.c_void_p, ctypes.c_int
+        lib.mi355gemm_gemm.argtypes = [i64, i64, i64, p, p, p, p, ci, p]
+        lib.mi355gemm_gemm.restype = ci
+        lib.mi355gemm_gemm_config.argtypes = [i64, i64, i64, p, p, p, p, ci, p, ci]
+        lib.mi355gemm_gemm_config.restype = ci
+        lib.mi355gemm_select.argtypes = [i64, i64, i64, ci, p, p, p, p]
+        lib.mi355gemm_select.restype = ci
+        lib.mi355gemm_num_configs.argtypes = []
+        lib.mi355gemm_num_configs.restype = ci
+        lib.mi355gemm_config_name.argtypes = [ci]
+        lib.mi355gemm_config_name.restype = ctypes.c_char_p
+        lib.mi355gemm_config_info.argtypes = [ci, ctypes.POINTER(ConfigDesc)]
+        lib.mi355gemm_config_info.restype = ci
+        lib.mi355gemm_lds_budget.argtypes = []
+        lib.mi355gemm_lds_budget.restype = ci
+        lib.mi355gemm_last_error.argtypes = []
+        lib.mi355gemm_last_error.restype = ctypes.c_char_p
+        lib.mi355gemm_version.argtypes = []
+        lib.mi355gemm_version.restype = ctypes.c_char_p
+        _lib = lib
+    return _lib
+
+
+# ---- the C entry points, same names, raw arguments --------------------------------
+
+def mi355gemm_gemm(M, N, K, A, B, C, bias, epi, stream) -> int:
+    return library().mi355gemm_gemm(M, N, K, A, B, C, bias, epi, stream)
+
+
+def mi355gemm_gemm_config(M, N, K, A, B, C, bias, epi, stream, config_id) -> int:
+    return library().mi355gemm_gemm_config(M, N, K, A, B, C, bias, epi, stream, config_id)
+
+
+def mi355gemm_select(M, N, K, epi, A, B, C, bias) -> int:
+    return library().mi355gemm_select(M, N, K, epi, A, B, C, bias)
+
+
+def mi355gemm_num_configs() -> int:
+    return library().mi355gemm_num_configs()
+
+
+def mi355gemm_config_name(config_id: int) -> str | None:
+    r = library().mi355gemm_config_name(config_id)
+    return None if r is None else r.decode()
+
+
+def mi355gemm_config_info(config_id: int) -> dict:
+    d = ConfigDesc()
+    st = library().mi355gemm_config_info(config_id, ctypes.byref(d))
+    if st != OK:
+        raise GemmError(st, mi355gemm_last_error())
+    return d.as_dict()
+
+
+def mi355gemm_lds_budget() -> int:
+    return library().mi355gemm_lds_budget()
+
+
+def mi355gemm_last_error() -> str:
+    return library().mi355gemm_last_error().decode()
+
+
+def mi355gemm_version() -> str:
+    return library().mi355gemm_version().decode()
+
+
+# ---- torch convenience layer -------------------------------------------------------
+
+def configs() -> list[dict]:
+    out = []
+    for i in range(mi355gemm_num_configs()):
+        d = mi355gemm_config_info(i)
+        d["id"] = i
+        d["name"] = mi355gemm_config_name(i)
+        out.append(d)
+    return out
+
+
+def config_id(name: str) -> int:
+    for i in range(mi355gemm_num_configs()):
+        if mi355gemm_config_name(i) == name:
+            return i
+    raise KeyError(name)
+
+
+def _check_tensor(t, name, ndim):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError("%s must be a torch.Tensor" % name)
+    if t.dtype != torch.float16:
+        raise TypeError("%s must be float16, got %s" % (name, t.dtype))
+    if t.device.type != "cuda":
+        raise ValueError("%s must be on a GPU device" % name)
+    if t.dim() != ndim or not t.is_contiguous():
+        raise ValueError("%s must be a contiguous %d-D tensor" % (name, ndim))
+
+
+def _epi(epilogue) -> int:
+    if isinstance(epilogue, str):
+        if epilogue not in EPILOGUES:
+            raise ValueError("epilogue must be one of %s" % sorted(EPILOGUES))
+        return EPILOGUES[epilogue]
+    return int(epilogue)
+
+
+def gemm(a: torch.Tensor, b: torch.Tensor, bias: torch.Tensor | None = None,
+         epilogue="none", out: torch.Tensor | None = None, config: int | str | None = None,
+         stream: torch.cuda.Stream | None = None) -> torch.Tensor:
+    """``out = epilogue(a @ b [+ bias])`` on the GPU; a (M,K), b (K,N), bias (N,), fp16."""
+    _check_tensor(a, "a", 2)
+    _check_tensor(b, "b", 2)
+    M, K = a.shape
+    if b.shape[0] != K:
+        raise ValueError("inner dimensions differ: a %s, b %s" % (tuple(a.shape), tuple(b.shape)))
+    N = b.shape[1]
+    if b.device != a.device:
+        raise ValueError("a and b are on different devices")
+    epi = _epi(epilogue)
+    if bias is not None:
+        _check_tensor(bias, "bias", 1)
+        if bias.shape[0] != N or bias.device != a.device:
+            raise ValueError("bias must have N=%d elements on %s" % (N, a.device))
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.float16, device=a.device)
+    else:
+        _check_tensor(out, "out", 2)
+        if tuple(out.shape) != (M, N) or out.device != a.device:
+            raise ValueError("out must be (%d, %d) on %s" % (M, N, a.device))
+    s = stream if stream is not None else torch.cuda.current_stream(a.device)
+    bptr = bias.data_ptr() if bias is not None else None
+    with torch.cuda.device(a.device):
+        if config is None:
+            st = mi355gemm_gemm(M, N, K, a.data_ptr(), b.data_ptr(), out.data_ptr(), bptr, epi,
+                                s.cuda_stream)
+        else:
+            cid = config_id(config) if isinstance(config, str) else int(config)
+            st = mi355gemm_gemm_config(M, N, K, a.data_ptr(), b.data_ptr(), out.data_ptr(), bptr,
+                                       epi, s.cuda_stream, cid)
+    if st != OK:
+        raise GemmError(st, mi355gemm_last_error())
+    return out
+
+
+def select(a: torch.Tensor, b: torch.Tensor, bias=None, epilogue="none", out=None) -> int:
+    """Configuration id ``gemm`` would use for these tensors (host-only decision)."""
+    M, K = a.shape
+    N = b.shape[1]
+    cid = mi355gemm_select(M, N, K, _epi(epilogue), a.data_ptr(), b.data_ptr(),
+                           out.data_ptr() if out is not None else 256,
+                           bias.data_ptr() if bias is not None else None)
+    return cid

@@ -1,0 +1,265 @@
+// C ABI of the gfx950 fp16 GEMM library: argument validation, the shape-keyed
+// configuration selector and the kernel launches.  The operation and the conventions
+// are documented in include/mi355gemm.h.
+#include "mi355gemm.h"
+
+#include <hip/hip_runtime.h>
+
+#include <stdarg.h>
+#include <stdint.h>
+#include <stdio.h>
+
+#include "gemm_kernel.hpp"
+
+namespace {
+
+using namespace mi355;
+
+thread_local char g_last_error[512] = "";
+
+mi355gemm_status fail(mi355gemm_status st, const char *fmt, ...)
+{
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_last_error, sizeof(g_last_error), fmt, ap);
+    va_end(ap);
+    return st;
+}
+
+typedef void (*KernelFn)(GemmArgs);
+
+struct Config {
+    const char *name;
+    int bm, bn, bk, stages, waves_m, waves_n, threads, lds_bytes;
+    bool a_vec, bc_vec;
+    int group_m;
+    KernelFn fn[3];   // per epilogue
+};
+
+template <class T, bool AV, bool BV>
+constexpr Config make_config(const char *name, int group_m)
+{
+    return Config{name, T::BM, T::BN, T::BK, T::STAGES, T::WAVES_M, T::WAVES_N, T::NT,
+                  T::LDS_BYTES, AV, BV, group_m,
+                  {gemm_kernel<T, AV, BV, 0>, gemm_kernel<T, AV, BV, 1>, gemm_kernel<T, AV, BV, 2>}};
+}
+
+using T64 = Tile<64, 64, 64, 2, 1>;       // 2 waves of 32x64
+using T128 = Tile<128, 128, 64, 2, 2>;    // 4 waves of 64x64
+using T256x128 = Tile<256, 128, 64, 2, 2>;  // 4 waves of 128x64
+using T256 = Tile<256, 256, 64, 2, 2>;    // 4 waves of 128x128
+
+const Config kConfigs[] = {
+    make_config<T256, true, true>("256x256x64_w2x2_av_bv", 8),
+    make_config<T256x128, true, true>("256x128x64_w2x2_av_bv", 8),
+    make_config<T128, true, true>("128x128x64_w2x2_av_bv", 8),
+    make_config<T128, true, false>("128x128x64_w2x2_av_bn", 8),
+    make_config<T128, false, true>("128x128x64_w2x2_an_bv", 8),
+    make_config<T128, false, false>("128x128x64_w2x2_an_bn", 8),
+    make_config<T64, true, true>("64x64x64_w2x1_av_bv", 8),
+    make_config<T64, true, false>("64x64x64_w2x1_av_bn", 8),
+    make_config<T64, false, true>("64x64x64_w2x1_an_bv", 8),
+    make_config<T64, false, false>("64x64x64_w2x1_an_bn", 8),
+};
+constexpr int kNumConfigs = (int)(sizeof(kConfigs) / sizeof(kConfigs[0]));
+
+constexpr int kLdsBudget = 160 * 1024;
+// Per-tile buffer descriptors hold 32-bit byte offsets below 2^31: BM*K, BK*N and BM*N
+// halves must stay under 2^30, so K and N are capped at 2^22.
+constexpr int64_t kMaxKN = (int64_t)1 << 22;
+
+bool aligned(const void *p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
+
+struct Request {
+    int64_t M, N, K;
+    const void *A, *B, *bias;
+    void *C;
+    int epi;
+};
+
+// Validation shared by every entry point; makes no HIP call.
+mi355gemm_status validate(const Request &r)
+{
+    if (r.M < 0 || r.N < 0 || r.K < 0)
+        return fail(MI355GEMM_EINVAL, "negative size (M=%lld N=%lld K=%lld)",
+                    (long long)r.M, (long long)r.N, (long long)r.K);
+    if (r.epi < MI355GEMM_EPI_NONE || r.epi > MI355GEMM_EPI_BIAS_GELU)
+        return fail(MI355GEMM_EINVAL, "unknown epilogue %d", r.epi);
+    if (r.M == 0 || r.N == 0) return MI355GEMM_OK;
+    if (r.C == nullptr) return fail(MI355GEMM_EINVAL, "C is NULL");
+    if (r.K > 0 && (r.A == nullptr || r.B == nullptr))
+        return fail(MI355GEMM_EINVAL, "A or B is NULL with K=%lld", (long long)r.K);
+    if (r.epi != MI355GEMM_EPI_NONE && r.bias == nullptr)
+        return fail(MI355GEMM_EINVAL, "epilogue %d needs a bias pointer", r.epi);
+    if (!aligned(r.C, 2) || (r.K > 0 && (!aligned(r.A, 2) || !aligned(r.B, 2))) ||
+        (r.epi != MI355GEMM_EPI_NONE && !aligned(r.bias, 2)))
+        return fail(MI355GEMM_EINVAL, "fp16 pointers must be 2-byte aligned");
+    if (r.K >= kMaxKN || r.N >= kMaxKN)
+        return fail(MI355GEMM_EUNSUPPORTED, "K and N must be below 2^22 (K=%lld N=%lld)",
+                    (long long)r.K, (long long)r.N);
+    if (r.M >= ((int64_t)1 << 31))
+        return fail(MI355GEMM_EUNSUPPORTED, "M must be below 2^31");
+    return MI355GEMM_OK;
+}
+
+bool a_vector_ok(const Request &r) { return r.K % 8 == 0 && (r.K == 0 || aligned(r.A, 16)); }
+
+bool bc_vector_ok(const Request &r)
+{
+    return r.N % 8 == 0 && aligned(r.C, 16) && (r.K == 0 || aligned(r.B, 16)) &&
+           (r.epi == MI355GEMM_EPI_NONE || aligned(r.bias, 8));
+}
+
+int64_t tiles(const Request &r, int bm, int bn)
+{
+    return ((r.M + bm - 1) / bm) * ((r.N + bn - 1) / bn);
+}
+
+int find_config(int bm, int bn, bool av, bool bv)
+{
+    for (int i = 0; i < kNumConfigs; ++i) {
+        const Config &c = kConfigs[i];
+        if (c.bm == bm && c.bn == bn && c.a_vec == av && c.bc_vec == bv) return i;
+    }
+    return -1;
+}
+
+// Shape-keyed choice (host only).  Larger tiles need fewer bytes per flop from L2/LDS,
+// but a launch must still cover the 256 compute units: take the largest tile that keeps
+// at least one full wave of workgroups, and fall back to 128x128 / 64x64 for small or
+// unaligned problems (the wide tiles only exist with 16-byte loads).
+int choose(const Request &r)
+{
+    const bool av = a_vector_ok(r), bv = bc_vector_ok(r);
+    constexpr int64_t kCUs = 256;
+    if (av && bv) {
+        if (tiles(r, 256, 256) >= 2 * kCUs) return find_config(256, 256, true, true);
+        if (tiles(r, 256, 128) >= 2 * kCUs) return find_config(256, 128, true, true);
+    }
+    if (tiles(r, 128, 128) >= kCUs / 2) return find_config(128, 128, av, bv);
+    return find_config(64, 64, av, bv);
+}
+
+// Can configuration c serve request r?
+mi355gemm_status check_config(const Config &c, const Request &r)
+{
+    if (c.lds_bytes > kLdsBudget)
+        return fail(MI355GEMM_EUNSUPPORTED, "config %s needs %d B of LDS, over the %d B budget",
+                    c.name, c.lds_bytes, kLdsBudget);
+    if (c.a_vec && !a_vector_ok(r))
+        return fail(MI355GEMM_EUNSUPPORTED,
+                    "config %s loads A in 16-byte vectors: needs K %% 8 == 0 and a 16-byte aligned A",
+                    c.name);
+    if (c.bc_vec && !bc_vector_ok(r))
+        return fail(MI355GEMM_EUNSUPPORTED,
+                    "config %s moves B and C in vectors: needs N %% 8 == 0, 16-byte aligned B and C "
+                    "and an 8-byte aligned bias", c.name);
+    return MI355GEMM_OK;
+}
+
+mi355gemm_status launch(const Config &c, const Request &r, hipStream_t stream)
+{
+    GemmArgs a;
+    a.A = static_cast<const f16 *>(r.A);
+    a.B = static_cast<const f16 *>(r.B);
+    a.C = static_cast<f16 *>(r.C);
+    a.bias = static_cast<const f16 *>(r.bias);
+    a.M = (int)r.M;
+    a.N = (int)r.N;
+    a.K = (int)r.K;
+    a.tiles_m = (int)((r.M + c.bm - 1) / c.bm);
+    a.tiles_n = (int)((r.N + c.bn - 1) / c.bn);
+    a.group_m = c.group_m;
+    const int64_t grid = (int64_t)a.tiles_m * a.tiles_n;
+    if (grid >= ((int64_t)1 << 31))
+        return fail(MI355GEMM_EUNSUPPORTED, "too many tiles (%lld)", (long long)grid);
+    hipLaunchKernelGGL(c.fn[r.epi], dim3((unsigned)grid), dim3(c.threads), 0, stream, a);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess)
+        return fail(MI355GEMM_EHIP, "launch of %s failed: %s", c.name, hipGetErrorString(e));
+    return MI355GEMM_OK;
+}
+
+mi355gemm_status run(const Request &r, void *stream, int forced)
+{
+    mi355gemm_status st = validate(r);
+    if (st != MI355GEMM_OK) return st;
+    if (forced >= kNumConfigs || forced < -1)
+        return fail(MI355GEMM_EINVAL, "unknown config id %d", forced);
+    if (forced >= 0) {
+        st = check_config(kConfigs[forced], r);
+        if (st != MI355GEMM_OK) return st;
+    }
+    if (r.M == 0 || r.N == 0) return MI355GEMM_OK;
+    const int id = forced >= 0 ? forced : choose(r);
+    if (id < 0) return fail(MI355GEMM_EUNSUPPORTED, "no configuration serves this request");
+    return launch(kConfigs[id], r, static_cast<hipStream_t>(stream));
+}
+
+}  // namespace
+
+extern "C" {
+
+mi355gemm_status mi355gemm_gemm(int64_t M, int64_t N, int64_t K, const void *A, const void *B,
+                                void *C, const void *bias, int epi, void *stream)
+{
+    g_last_error[0] = 0;
+    return run(Request{M, N, K, A, B, bias, C, epi}, stream, -1);
+}
+
+mi355gemm_status mi355gemm_gemm_config(int64_t M, int64_t N, int64_t K, const void *A,
+                                       const void *B, void *C, const void *bias, int epi,
+                                       void *stream, int config_id)
+{
+    g_last_error[0] = 0;
+    if (config_id < 0) return fail(MI355GEMM_EINVAL, "unknown config id %d", config_id);
+    return run(Request{M, N, K, A, B, bias, C, epi}, stream, config_id);
+}
+
+int mi355gemm_select(int64_t M, int64_t N, int64_t K, int epi, const void *A, const void *B,
+                     const void *C, const void *bias)
+{
+    g_last_error[0] = 0;
+    const Request r{M, N, K, A, B, bias, const_cast<void *>(C), epi};
+    if (validate(r) != MI355GEMM_OK) return -1;
+    if (M == 0 || N == 0) {
+        fail(MI355GEMM_OK, "empty problem: no launch");
+        return -1;
+    }
+    return choose(r);
+}
+
+int mi355gemm_num_configs(void) { return kNumConfigs; }
+
+const char *mi355gemm_config_name(int config_id)
+{
+    if (config_id < 0 || config_id >= kNumConfigs) return nullptr;
+    return kConfigs[config_id].name;
+}
+
+mi355gemm_status mi355gemm_config_info(int config_id, mi355gemm_config_desc *out)
+{
+    if (config_id < 0 || config_id >= kNumConfigs || out == nullptr)
+        return fail(MI355GEMM_EINVAL, "unknown config id %d or NULL out", config_id);
+    const Config &c = kConfigs[config_id];
+    out->block_m = c.bm;
+    out->block_n = c.bn;
+    out->block_k = c.bk;
+    out->stages = c.stages;
+    out->waves_m = c.waves_m;
+    out->waves_n = c.waves_n;
+    out->threads = c.threads;
+    out->lds_bytes = c.lds_bytes;
+    out->a_vector = c.a_vec;
+    out->bc_vector = c.bc_vec;
+    out->group_m = c.group_m;
+    return MI355GEMM_OK;
+}
+
+int mi355gemm_lds_budget(void) { return kLdsBudget; }
+
+const char *mi355gemm_last_error(void) { return g_last_error; }
+
+const char *mi355gemm_version(void) { return "mi355gemm 0.1.0 (gfx950)"; }
+
+}  // extern "C"

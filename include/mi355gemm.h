@@ -1,0 +1,134 @@
+/*
+ * mi355gemm -- half-precision GEMM with fp32 accumulation and an optional fused
+ * bias + erf-GELU epilogue, written for AMD Instinct MI355X (gfx950, CDNA4).
+ *
+ * C ABI (C99).  No torch or HIP types appear in the signatures: device buffers are
+ * plain pointers, the stream is an opaque pointer (a hipStream_t, NULL for the
+ * default stream).
+ *
+ * The operation follows "Designing High-Performance GPU Kernels with TileLang:
+ * Tensor-Core GEMM, Fused Softmax, FlashAttention, and Autotuning":
+ *   - thecryptopost.io page, section 2 "Memory hierarchy - tiled tensor-core GEMM",
+ *     make_matmul: A is (M, K), B is (K, N), C is (M, N), all float16 and row-major,
+ *     the accumulator is "float" (fp32);
+ *   - ainovat.com page, the fused-epilogue paragraph: bias addition and GELU are
+ *     applied to the register-resident accumulator before the single write of C.
+ *
+ *   epilogue NONE       C[i][j] = fp16( sum_k A[i][k] B[k][j] )
+ *   epilogue BIAS       C[i][j] = fp16( sum_k A[i][k] B[k][j] + bias[j] )
+ *   epilogue BIAS_GELU  C[i][j] = fp16( GELU( sum_k A[i][k] B[k][j] + bias[j] ) )
+ *   with GELU(x) = x * Phi(x) = 0.5 x (1 + erf(x / sqrt 2)) (the exact, erf form),
+ *   the sum and the epilogue in fp32, and one round-to-nearest-even to fp16 at the
+ *   store.  The order of the fp32 additions over k is unspecified.
+ */
+#ifndef MI355GEMM_H
+#define MI355GEMM_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    MI355GEMM_EPI_NONE = 0,
+    MI355GEMM_EPI_BIAS = 1,
+    MI355GEMM_EPI_BIAS_GELU = 2
+} mi355gemm_epilogue;
+
+typedef enum {
+    MI355GEMM_OK = 0,
+    MI355GEMM_EINVAL = 1,       /* bad argument: negative size, null pointer, bad enum */
+    MI355GEMM_EUNSUPPORTED = 2, /* legal request this build cannot serve */
+    MI355GEMM_EHIP = 3          /* the HIP runtime reported an error (see last_error) */
+} mi355gemm_status;
+
+/*
+ * C = epilogue(A . B [+ bias]), enqueued on `stream`.
+ *
+ * M, N, K  problem sizes (>= 0).  M == 0 or N == 0: nothing to do, returns OK without
+ *          a launch.  K == 0: C = epilogue(bias or 0) (an empty sum).
+ * A        device pointer, M x K fp16, row-major, leading dimension K.
+ * B        device pointer, K x N fp16, row-major, leading dimension N.
+ * C        device pointer, M x N fp16, row-major, leading dimension N; written, never
+ *          read.  Memory outside the M x N window is not touched.
+ * bias     device pointer to N fp16 values (one per output column), required for the
+ *          BIAS and BIAS_GELU epilogues, ignored (may be NULL) for NONE.
+ * epi      a mi355gemm_epilogue value.
+ * stream   hipStream_t to enqueue on; NULL is the default stream.
+ *
+ * Ownership: the caller owns every buffer; the library allocates nothing, keeps no
+ * per-call state and needs no workspace.  The call is asynchronous (it returns after
+ * the enqueue) and thread-safe.  C must not overlap A, B or bias (not checked).
+ * Every pointer must be at least 2-byte aligned; shapes or pointers that are not
+ * 16-byte friendly are served by narrow-load kernels, never rejected.
+ *
+ * Errors: EINVAL for negative sizes, null pointers with work to do, an unknown
+ * epilogue, a bias epilogue with bias == NULL, or a misaligned pointer; EUNSUPPORTED
+ * if K or N exceeds 2^21 (the per-tile 32-bit buffer offsets); EHIP if the launch
+ * fails.  A non-OK return leaves C untouched and sets mi355gemm_last_error().
+ */
+mi355gemm_status mi355gemm_gemm(int64_t M, int64_t N, int64_t K,
+                                const void *A, const void *B, void *C, const void *bias,
+                                int epi, void *stream);
+
+/*
+ * As mi355gemm_gemm, but with the kernel configuration forced to `config_id`
+ * (0 <= id < mi355gemm_num_configs()).  For sweeps and tests: a configuration that
+ * cannot serve this shape or these pointers (for instance a 16-byte-load configuration
+ * with K % 8 != 0) returns EUNSUPPORTED, like the tutorial's schedule sweep skipping
+ * candidates over the shared-memory budget (thecryptopost.io page, section 3 "Knobs -
+ * sweeping the schedule by hand").
+ */
+mi355gemm_status mi355gemm_gemm_config(int64_t M, int64_t N, int64_t K,
+                                       const void *A, const void *B, void *C,
+                                       const void *bias, int epi, void *stream,
+                                       int config_id);
+
+/*
+ * The configuration mi355gemm_gemm would launch for these arguments, or -1 (with
+ * last_error set) if the arguments are invalid.  Host-only: makes no HIP call.
+ * The choice is keyed on the shape and on pointer/leading-dimension alignment; the
+ * tutorial notes the best schedule depends on the architecture and the shape
+ * (thecryptopost.io page, section 3).
+ */
+int mi355gemm_select(int64_t M, int64_t N, int64_t K, int epi,
+                     const void *A, const void *B, const void *C, const void *bias);
+
+/* Description of one compiled kernel configuration. */
+typedef struct {
+    int block_m, block_n, block_k;  /* macro-tile of C per workgroup and K step */
+    int stages;                     /* LDS buffers in the K pipeline */
+    int waves_m, waves_n;           /* wavefront grid inside a workgroup */
+    int threads;                    /* threads per workgroup (64 per wavefront) */
+    int lds_bytes;                  /* LDS the configuration occupies per workgroup */
+    int a_vector;                   /* 1: A loaded in 16-byte vectors (needs K % 8 == 0) */
+    int bc_vector;                  /* 1: B loaded and C stored in vectors (N % 8 == 0) */
+    int group_m;                    /* tile-rows per group in the tile order */
+} mi355gemm_config_desc;
+
+/* Number of compiled configurations (ids 0 .. n-1). Host-only. */
+int mi355gemm_num_configs(void);
+
+/* Static name of a configuration ("128x128x64_w2x2_av_bv", ...), or NULL. Host-only. */
+const char *mi355gemm_config_name(int config_id);
+
+/* Fill *out for config_id; EINVAL for an unknown id or NULL out. Host-only. */
+mi355gemm_status mi355gemm_config_info(int config_id, mi355gemm_config_desc *out);
+
+/* LDS bytes one workgroup may use on gfx950 (the budget every configuration is checked
+ * against; 160 KiB). Host-only. */
+int mi355gemm_lds_budget(void);
+
+/* Message for the last non-OK status returned on this thread ("" if none). The string
+ * stays valid until the next call on the same thread. */
+const char *mi355gemm_last_error(void);
+
+/* Library version string. */
+const char *mi355gemm_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MI355GEMM_H */

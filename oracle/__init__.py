@@ -70,6 +70,8 @@ def _declare(lib: ctypes.CDLL) -> None:
     lib.oracle_gemm.restype = ctypes.c_int
     lib.oracle_gemm_sampled.argtypes = [i64, i64, i64, p, p, p, ctypes.c_int, i64, p, p, p]
     lib.oracle_gemm_sampled.restype = ctypes.c_int
+    lib.oracle_num_threads.argtypes = []
+    lib.oracle_num_threads.restype = ctypes.c_int
     for name in ("oracle_f16_to_f64_array", "oracle_f64_to_f16_array", "oracle_gelu_array"):
         getattr(lib, name).argtypes = [i64, p, p]
         getattr(lib, name).restype = None
@@ -122,6 +124,11 @@ def gelu(x, lib=None) -> np.ndarray:
     out = np.empty(x.shape, dtype=np.float64)
     lib.oracle_gelu_array(x.size, _ptr(x), _ptr(out))
     return out
+
+
+def num_threads(lib=None) -> int:
+    """OpenMP threads the oracle's loops use."""
+    return (lib or load()).oracle_num_threads()
 
 
 def _epi_code(epilogue) -> int:

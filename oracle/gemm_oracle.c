@@ -34,8 +34,15 @@
  * Build: gcc -O2 -fopenmp -ffp-contract=off -fPIC -shared (see oracle/__init__.py).
  */
 #include <math.h>
+#include <omp.h>
 #include <stdint.h>
 #include <stdlib.h>
+
+/* Threads the OpenMP loops below will use (reported with CPU timings). */
+int oracle_num_threads(void)
+{
+    return omp_get_max_threads();
+}
 
 /* binary16 -> double, exact for every bit pattern. */
 double oracle_f16_to_f64(uint16_t h)

@@ -1,0 +1,176 @@
+"""Host-side checks of the C ABI (no GPU needed, no kernel launched).
+
+The library must load and export every symbol ``include/mi355gemm.h`` declares;
+argument validation and the configuration selector run before any HIP call, so their
+decisions are checked here with fake (never dereferenced) pointer values.
+"""
+from __future__ import annotations
+
+import os
+import re
+import subprocess
+
+import pytest
+
+import dense_fp16_gemm_fp32_amd as g
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "mi355gemm.h")
+
+# fake device addresses: only their alignment matters to the host logic
+P16 = 0x7f0000000000          # 16-byte aligned
+P2 = P16 + 2                  # only 2-byte aligned
+
+
+def header_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(mi355gemm_\w+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_symbol():
+    declared = header_functions()
+    assert len(declared) == 9
+    assert sorted(g.EXPORTS) == declared
+    lib = g.library()
+    for name in declared:
+        assert hasattr(lib, name), name
+    out = subprocess.run(["nm", "-D", "--defined-only", g.LIBRARY], stdout=subprocess.PIPE,
+                         text=True, check=True).stdout
+    exported = set(re.findall(r"\bT (mi355gemm_\w+)", out))
+    assert set(declared) <= exported
+
+
+def test_version_and_budget():
+    assert "gfx950" in g.mi355gemm_version()
+    assert g.mi355gemm_lds_budget() == 160 * 1024
+
+
+def test_config_table_is_consistent():
+    cfgs = g.configs()
+    assert len(cfgs) == g.mi355gemm_num_configs() >= 4
+    names = [c["name"] for c in cfgs]
+    assert len(set(names)) == len(names)
+    for c in cfgs:
+        # two LDS stages of BM and BN rows of BK halves plus a 16-byte pad per row
+        assert c["lds_bytes"] == c["stages"] * (c["block_m"] + c["block_n"]) * (c["block_k"] + 8) * 2
+        assert c["lds_bytes"] <= g.mi355gemm_lds_budget()
+        assert c["threads"] == 64 * c["waves_m"] * c["waves_n"]
+        assert c["block_m"] % (32 * c["waves_m"]) == 0 and c["block_n"] % (32 * c["waves_n"]) == 0
+        assert c["block_k"] % 16 == 0
+    assert g.mi355gemm_config_name(-1) is None
+    assert g.mi355gemm_config_name(len(cfgs)) is None
+    with pytest.raises(g.GemmError):
+        g.mi355gemm_config_info(len(cfgs))
+
+
+def _status(M, N, K, A=P16, B=P16, C=P16, bias=None, epi=0, config=None):
+    if config is None:
+        return g.mi355gemm_gemm(M, N, K, A, B, C, bias, epi, None)
+    return g.mi355gemm_gemm_config(M, N, K, A, B, C, bias, epi, None, config)
+
+
+@pytest.mark.parametrize("args,want", [
+    (dict(M=-1, N=4, K=4), g.EINVAL),
+    (dict(M=4, N=-1, K=4), g.EINVAL),
+    (dict(M=4, N=4, K=-1), g.EINVAL),
+    (dict(M=4, N=4, K=4, epi=3), g.EINVAL),
+    (dict(M=4, N=4, K=4, epi=-1), g.EINVAL),
+    (dict(M=4, N=4, K=4, C=None), g.EINVAL),
+    (dict(M=4, N=4, K=4, A=None), g.EINVAL),
+    (dict(M=4, N=4, K=4, B=None), g.EINVAL),
+    (dict(M=4, N=4, K=4, epi=1), g.EINVAL),          # bias epilogue without bias
+    (dict(M=4, N=4, K=4, epi=2), g.EINVAL),
+    (dict(M=4, N=4, K=4, A=P16 + 1), g.EINVAL),      # odd address
+    (dict(M=4, N=4, K=4, C=P16 + 1), g.EINVAL),
+    (dict(M=4, N=4, K=4, bias=P16 + 1, epi=2), g.EINVAL),
+    (dict(M=4, N=4, K=1 << 22), g.EUNSUPPORTED),
+    (dict(M=4, N=1 << 22, K=4), g.EUNSUPPORTED),
+    (dict(M=4, N=4, K=4, config=99), g.EINVAL),
+    (dict(M=4, N=4, K=4, config=-5), g.EINVAL),
+])
+def test_validation_errors(args, want):
+    assert _status(**args) == want
+    assert g.mi355gemm_last_error() != ""
+
+
+def test_empty_problems_are_ok_without_launch():
+    # M == 0 or N == 0: nothing to compute, OK even with NULL pointers
+    assert _status(0, 16, 16, A=None, B=None, C=None) == g.OK
+    assert _status(16, 0, 16, A=None, B=None, C=None) == g.OK
+    assert _status(0, 0, 0, A=None, B=None, C=None, epi=2) == g.OK
+    assert g.mi355gemm_last_error() == ""
+
+
+def test_forced_vector_config_rejects_unaligned_shapes():
+    vec = [c for c in g.configs() if c["a_vector"]]
+    bc = [c for c in g.configs() if c["bc_vector"]]
+    assert vec and bc
+    assert _status(100, 64, 777, config=vec[0]["id"]) == g.EUNSUPPORTED       # K % 8 != 0
+    assert "K % 8" in g.mi355gemm_last_error()
+    assert _status(100, 64, 64, A=P2, config=vec[0]["id"]) == g.EUNSUPPORTED  # A misaligned
+    assert _status(100, 60, 64, config=bc[0]["id"]) == g.EUNSUPPORTED        # N % 8 != 0
+    assert _status(100, 64, 64, C=P2, config=bc[0]["id"]) == g.EUNSUPPORTED
+
+
+def _select(M, N, K, epi=0, A=P16, B=P16, C=P16, bias=P16):
+    return g.mi355gemm_select(M, N, K, epi, A, B, C, bias)
+
+
+def _cfg(i):
+    return g.mi355gemm_config_info(i)
+
+
+def test_select_for_the_workload_shapes():
+    import workloads
+    for w in workloads.WORKLOADS:
+        for epi_name in w.epilogues:
+            epi = g.EPILOGUES[epi_name]
+            i = _select(w.M, w.N, w.K, epi)
+            assert i >= 0, w.name
+            c = _cfg(i)
+            if w.K % 8 == 0:
+                assert c["a_vector"] == 1, w.name
+            else:
+                assert c["a_vector"] == 0, w.name     # ragged K: 2-byte loads for A
+            assert c["bc_vector"] == (1 if w.N % 8 == 0 else 0), w.name
+    # large square problems take the widest tile; 2048^3 must still fill 256 CUs
+    big = _cfg(_select(8192, 8192, 8192))
+    assert (big["block_m"], big["block_n"]) == (256, 256)
+    mid = _cfg(_select(2048, 2048, 2048))
+    tiles = (2048 // mid["block_m"]) * (2048 // mid["block_n"])
+    assert tiles >= 256
+
+
+def test_select_routes_misaligned_pointers_to_narrow_loads():
+    c = _cfg(_select(512, 512, 512, A=P2))
+    assert c["a_vector"] == 0 and c["bc_vector"] == 1
+    c = _cfg(_select(512, 512, 512, B=P2))
+    assert c["bc_vector"] == 0
+    c = _cfg(_select(512, 512, 512, C=P2))
+    assert c["bc_vector"] == 0
+    c = _cfg(_select(512, 512, 512, epi=2, bias=P16 + 4))  # bias only 4-byte aligned
+    assert c["bc_vector"] == 0
+    c = _cfg(_select(512, 500, 512))                      # N % 8 != 0
+    assert c["bc_vector"] == 0
+
+
+def test_select_rejects_invalid_and_empty():
+    assert _select(-1, 4, 4) == -1
+    assert _select(4, 4, 4, epi=7) == -1
+    assert _select(0, 4, 4) == -1
+
+
+def test_selected_config_always_passes_its_own_checks():
+    # every choice the selector makes must be one the forced path accepts; probe with a
+    # forced call that fails validation late (bad epilogue) to stay launch-free
+    for shape in [(1, 1, 1), (33, 65, 17), (1000, 3000, 777), (2048, 2048, 2048),
+                  (8192, 8192, 8192), (4096, 1024, 4096), (100, 8, 8)]:
+        for A in (P16, P2):
+            i = _select(*shape, A=A)
+            c = _cfg(i)
+            M, N, K = shape
+            if c["a_vector"]:
+                assert K % 8 == 0 and A % 16 == 0
+            if c["bc_vector"]:
+                assert N % 8 == 0

@@ -1,0 +1,256 @@
+"""GPU parity: the HIP path through the C ABI against the CPU oracle.
+
+Inputs come from ``workloads`` (seeded, host-side); the same fp16 bits go to both sides.
+Random inputs are compared to the tolerance bar in ``parity.py``; structured inputs
+whose sums are exact (all-ones, selection matrices, small integers) must match the
+oracle bit for bit.
+"""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+import dense_fp16_gemm_fp32_amd as g
+import oracle
+import workloads
+from parity import assert_bitexact, assert_parity
+
+pytestmark = pytest.mark.gpu
+
+DEV = torch.device("cuda:0")
+EPIS = ("none", "bias", "bias_gelu")
+
+
+def _dev(t):
+    return None if t is None else t.to(DEV)
+
+
+def _run(A, B, bias, epi, config=None, out=None):
+    C = g.gemm(_dev(A), _dev(B), _dev(bias) if epi != "none" else None, epilogue=epi,
+               config=config, out=out)
+    torch.cuda.synchronize()
+    return C
+
+
+def _compatible(cfg, M, N, K):
+    if cfg["a_vector"] and K % 8:
+        return False
+    if cfg["bc_vector"] and N % 8:
+        return False
+    return True
+
+
+ALL_CONFIGS = None
+
+
+def all_configs():
+    global ALL_CONFIGS
+    if ALL_CONFIGS is None:
+        ALL_CONFIGS = g.configs()
+    return ALL_CONFIGS
+
+
+def test_device_is_gfx950():
+    props = torch.cuda.get_device_properties(0)
+    print("device:", props.name, getattr(props, "gcnArchName", "?"), props.multi_processor_count,
+          "CUs", flush=True)
+    assert "gfx950" in getattr(props, "gcnArchName", "gfx950")
+
+
+# ---- one MFMA block: pins the operand and result lane maps ---------------------------
+
+def _small_int_inputs(M, N, K):
+    i = torch.arange(M).view(M, 1)
+    k = torch.arange(K).view(1, K)
+    A = ((i * 7 + k * 3) % 9 - 4).to(torch.float16)
+    kk = torch.arange(K).view(K, 1)
+    j = torch.arange(N).view(1, N)
+    B = ((kk * 5 + j * 11) % 7 - 3).to(torch.float16)
+    return A.contiguous(), B.contiguous()
+
+
+@pytest.mark.parametrize("shape", [(32, 32, 16), (64, 64, 64), (96, 160, 48)])
+def test_small_integer_products_bitexact_every_config(shape):
+    """|C| <= K*4*3 stays an exactly representable fp16 integer, so every correct
+    summation order gives the same bits; a wrong lane map does not."""
+    M, N, K = shape
+    A, B = _small_int_inputs(M, N, K)
+    ref = oracle.gemm(A, B)
+    for cfg in all_configs():
+        if not _compatible(cfg, M, N, K):
+            continue
+        print("config", cfg["name"], shape, flush=True)
+        C = _run(A, B, None, "none", config=cfg["id"])
+        assert_bitexact(C, ref, "%s %s" % (cfg["name"], shape))
+
+
+# ---- structured inputs at every workload shape: exact results --------------------------
+
+@pytest.mark.parametrize("w", workloads.WORKLOADS, ids=[w.name for w in workloads.WORKLOADS])
+def test_all_ones_gives_K_exactly(w):
+    A = torch.ones((w.M, w.K), dtype=torch.float16)
+    B = torch.ones((w.K, w.N), dtype=torch.float16)
+    print("all-ones", w.name, flush=True)
+    C = _run(A, B, None, "none")
+    assert torch.all(C == float(w.K)).item(), "all-ones product is not K everywhere"
+
+
+@pytest.mark.parametrize("w", workloads.WORKLOADS, ids=[w.name for w in workloads.WORKLOADS])
+def test_selection_matrices_copy_rows_and_columns(w):
+    M, N, K = w.M, w.N, w.K
+    Ar, Br, _ = workloads.make_inputs(M, N, K, w.dist, seed=11)
+    # A selects rows of B: C[i, :] = B[i mod K, :]
+    A_sel = torch.zeros((M, K), dtype=torch.float16)
+    A_sel[torch.arange(M), torch.arange(M) % K] = 1
+    print("row selection", w.name, flush=True)
+    C = _run(A_sel, Br, None, "none")
+    want = Br[torch.arange(M) % K]
+    assert torch.equal(C.cpu(), want), "row selection mismatch"
+    # B selects columns of A: C[:, j] = A[:, j mod K]
+    B_sel = torch.zeros((K, N), dtype=torch.float16)
+    B_sel[torch.arange(N) % K, torch.arange(N)] = 1
+    print("column selection", w.name, flush=True)
+    C = _run(Ar, B_sel, None, "none")
+    want = Ar[:, torch.arange(N) % K]
+    assert torch.equal(C.cpu(), want), "column selection mismatch"
+
+
+# ---- random inputs at small and ragged shapes, every config, every epilogue -----------
+
+SMALL_SHAPES = [(1, 1, 1), (1, 8, 8), (7, 9, 5), (33, 65, 17), (64, 64, 64), (130, 264, 200),
+                (257, 129, 72), (300, 500, 136), (129, 257, 777), (200, 96, 1), (500, 264, 1000)]
+
+
+@pytest.mark.parametrize("shape", SMALL_SHAPES, ids=["%dx%dx%d" % s for s in SMALL_SHAPES])
+def test_random_parity_every_config_and_epilogue(shape):
+    M, N, K = shape
+    A, B, bias = workloads.make_inputs(M, N, K, "normal", with_bias=True, seed=M + N + K)
+    refs = {e: oracle.gemm(A, B, bias, e) for e in EPIS}
+    for cfg in all_configs():
+        if not _compatible(cfg, M, N, K):
+            continue
+        for e in EPIS:
+            print("config", cfg["name"], shape, e, flush=True)
+            C = _run(A, B, bias, e, config=cfg["id"])
+            assert_parity(C, refs[e], "%s %s %s" % (cfg["name"], shape, e))
+
+
+# ---- the workloads at full size, in the launch configuration the benchmark uses --------
+
+def _workload_cases():
+    cases = []
+    for w in workloads.WORKLOADS:
+        for e in w.epilogues:
+            cases.append((w, e))
+        if w.name == "gemm_256" or w.name == "gemm_2048_bias_gelu":
+            cases.append((w, "bias"))
+    return cases
+
+
+CASES = _workload_cases()
+
+
+@pytest.mark.parametrize("w,epi", CASES, ids=["%s-%s" % (w.name, e) for w, e in CASES])
+def test_workload_parity(w, epi):
+    A, B, bias = workloads.make_inputs(w.M, w.N, w.K, w.dist, with_bias=True, seed=w.seed)
+    print("workload", w.name, epi, "config", g.mi355gemm_config_name(
+        g.select(_dev(A), _dev(B), _dev(bias), epi)), flush=True)
+    C = _run(A, B, bias, epi)
+    if w.M * w.N * w.K <= 2048 ** 3:
+        ref = oracle.gemm(A, B, bias, epi)
+        rep = assert_parity(C, ref, w.name + " " + epi)
+    else:
+        # full size: sampled elements, including every tile-boundary row and column
+        rng = np.random.default_rng(0)
+        edge = np.array([0, 1, 127, 128, 255, 256, w.M - 1])
+        rows = np.concatenate([rng.integers(0, w.M, 6000), np.repeat(edge, 64)])
+        cols = np.concatenate([rng.integers(0, w.N, 6000), rng.integers(0, w.N, edge.size * 64)])
+        rows2 = np.repeat(rng.integers(0, w.M, 64), edge.size)
+        cols2 = np.tile(np.array([0, 1, 127, 128, 255, 256, w.N - 1]), 64)
+        rows = np.concatenate([rows, rows2])
+        cols = np.concatenate([cols, cols2])
+        ref = oracle.gemm_sampled(A, B, rows, cols, bias, epi)
+        got = C.cpu()[torch.from_numpy(rows), torch.from_numpy(cols)]
+        rep = assert_parity(got, ref, w.name + " " + epi + " (sampled)")
+    print("   ", rep, flush=True)
+
+
+# ---- memory outside C is never touched -------------------------------------------------
+
+@pytest.mark.parametrize("shape", [(1000, 3000, 777), (130, 264, 200), (33, 65, 17), (257, 136, 64)])
+def test_guard_bands_untouched(shape):
+    M, N, K = shape
+    A, B, bias = workloads.make_inputs(M, N, K, "uniform", with_bias=True, seed=3)
+    pad = 4096
+    for cfg in all_configs():
+        if not _compatible(cfg, M, N, K):
+            continue
+        buf = torch.full((M * N + 2 * pad,), float("nan"), dtype=torch.float16, device=DEV)
+        out = buf[pad:pad + M * N].view(M, N)
+        print("guard", cfg["name"], shape, flush=True)
+        _run(A, B, bias, "bias_gelu", config=cfg["id"], out=out)
+        assert torch.isnan(buf[:pad]).all().item() and torch.isnan(buf[pad + M * N:]).all().item()
+        assert not torch.isnan(out).any().item()
+
+
+# ---- degenerate shapes -------------------------------------------------------------------
+
+def test_empty_and_zero_k():
+    A = torch.zeros((0, 16), dtype=torch.float16, device=DEV)
+    B = torch.zeros((16, 8), dtype=torch.float16, device=DEV)
+    assert g.gemm(A, B).shape == (0, 8)
+    A = torch.zeros((8, 16), dtype=torch.float16, device=DEV)
+    B = torch.zeros((16, 0), dtype=torch.float16, device=DEV)
+    assert g.gemm(A, B).shape == (8, 0)
+    # K == 0: an empty sum, C = epi(bias or 0)
+    _, _, bias = workloads.make_inputs(1, 40, 1, "normal", with_bias=True, seed=4)
+    A0 = torch.zeros((24, 0), dtype=torch.float16)
+    B0 = torch.zeros((0, 40), dtype=torch.float16)
+    for e in EPIS:
+        out = torch.full((24, 40), 7.0, dtype=torch.float16, device=DEV)
+        C = _run(A0, B0, bias, e, out=out)
+        ref = oracle.gemm(A0, B0, bias, e)
+        assert_parity(C, ref, "K=0 " + e)
+
+
+def test_misaligned_operands_use_narrow_loads():
+    M, N, K = 200, 136, 96
+    A, B, bias = workloads.make_inputs(M, N, K, "normal", with_bias=True, seed=6)
+    # views one element into larger buffers: 2-byte aligned only
+    Ab = torch.zeros(M * K + 1, dtype=torch.float16, device=DEV)
+    Ab[1:] = A.reshape(-1).to(DEV)
+    Ad = Ab[1:].view(M, K)
+    Cb = torch.zeros(M * N + 1, dtype=torch.float16, device=DEV)
+    Cd = Cb[1:].view(M, N)
+    cid = g.select(Ad, B.to(DEV), bias.to(DEV), "bias_gelu", out=Cd)
+    info = g.mi355gemm_config_info(cid)
+    assert info["a_vector"] == 0 and info["bc_vector"] == 0
+    g.gemm(Ad, B.to(DEV), bias.to(DEV), "bias_gelu", out=Cd)
+    torch.cuda.synchronize()
+    assert_parity(Cd, oracle.gemm(A, B, bias, "bias_gelu"), "misaligned")
+
+
+def test_runs_on_a_side_stream():
+    M, N, K = 512, 512, 512
+    A, B, bias = workloads.make_inputs(M, N, K, "normal", with_bias=True, seed=8)
+    s = torch.cuda.Stream(device=DEV)
+    Ad, Bd, bd = A.to(DEV), B.to(DEV), bias.to(DEV)
+    torch.cuda.synchronize()
+    with torch.cuda.stream(s):
+        C = g.gemm(Ad, Bd, bd, "bias_gelu")
+    s.synchronize()
+    assert_parity(C, oracle.gemm(A, B, bias, "bias_gelu"), "side stream")
+
+
+def test_rejects_bad_tensors():
+    A = torch.zeros((8, 16), dtype=torch.float16, device=DEV)
+    B = torch.zeros((16, 8), dtype=torch.float16, device=DEV)
+    with pytest.raises(TypeError):
+        g.gemm(A.float(), B)
+    with pytest.raises(ValueError):
+        g.gemm(A, B.t())
+    with pytest.raises(ValueError):
+        g.gemm(A, torch.zeros((15, 8), dtype=torch.float16, device=DEV))
+    with pytest.raises(g.GemmError):
+        g.gemm(A, B, None, "bias_gelu")
