@@ -1,0 +1,169 @@
+// Pieces shared by the gfx950 GEMM kernels: types, kernel arguments, buffer descriptors,
+// the tile order, and the register epilogue (bias, erf-GELU, fp16 rounding, masked store).
+//
+// The operation is C (M x N) = epi(A (M x K) . B (K x N) [+ bias]), all fp16 row-major with
+// fp32 accumulation, as stated by "Designing High-Performance GPU Kernels with TileLang:
+// Tensor-Core GEMM, Fused Softmax, FlashAttention, and Autotuning" (thecryptopost.io page,
+// section 2, make_matmul), with the epilogue of the same tutorial's fused-epilogue
+// paragraph (ainovat.com page): bias and GELU applied to the accumulator in registers,
+// then one write of C.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace mi355 {
+
+typedef _Float16 f16;
+typedef f16 f16x4 __attribute__((ext_vector_type(4)));
+typedef f16 f16x8 __attribute__((ext_vector_type(8)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+// A buffer offset no descriptor here ever covers (every num_records is below 2^31): a
+// load from it returns zeros and a store to it is discarded by the hardware range check.
+constexpr uint32_t kOutOfRange = 0x80000000u;
+// Buffer resource word 3 for gfx9-family raw buffers (32-bit data format, no swizzle).
+constexpr int kRsrcWord3 = 0x00020000;
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, uint32_t bytes)
+{
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), 0, (int)bytes, kRsrcWord3);
+}
+
+// Valid offsets stay below 2^31, so setting bit 31 turns an offset into an out-of-range
+// one without a branch.
+__device__ __forceinline__ uint32_t masked_offset(uint32_t off, bool valid)
+{
+    return off | ((uint32_t)!valid << 31);
+}
+
+struct GemmArgs {
+    const f16 *A;
+    const f16 *B;
+    f16 *C;
+    const f16 *bias;
+    int M, N, K;
+    int tiles_m, tiles_n;
+    int group_m;
+};
+
+// ---------------------------------------------------------------- tile order --------
+// Workgroups are handed to the 8 XCDs round-robin (id % 8).  Renumber them so each XCD
+// owns one contiguous range of the logical order; the logical order sweeps GROUP_M
+// tile-rows column by column, so tiles resident at the same time share A row-panels and
+// B column-panels in that XCD's L2.
+__device__ __forceinline__ void tile_coords(int bid, int tiles_m, int tiles_n, int group_m,
+                                            int &tm, int &tn)
+{
+    const int total = tiles_m * tiles_n;
+    const int xcd = bid & 7, idx = bid >> 3;
+    const int per = total >> 3, rem = total & 7;
+    const int lid = (xcd < rem) ? xcd * (per + 1) + idx
+                                : rem * (per + 1) + (xcd - rem) * per + idx;
+    const int width = group_m * tiles_n;
+    const int g = lid / width;
+    const int first_m = g * group_m;
+    const int gsz = min(tiles_m - first_m, group_m);
+    const int r = lid - g * width;
+    tm = first_m + r % gsz;
+    tn = r / gsz;
+}
+
+// ---------------------------------------------------------------- epilogue ----------
+// GELU(x) = x * Phi(x), Phi(x) = 1 - erfc(x/sqrt2)/2 for x >= 0 and erfc(|x|/sqrt2)/2
+// for x < 0; one erfc evaluation, no cancellation on the negative side.
+__device__ __forceinline__ float gelu_erf(float x)
+{
+    const float q = erfcf(fabsf(x) * 0.70710678118654752f);
+    const float phi = (x >= 0.0f) ? 1.0f - 0.5f * q : 0.5f * q;
+    return x * phi;
+}
+
+template <int EPI>
+__device__ __forceinline__ float epilogue_op(float acc, float b)
+{
+    if constexpr (EPI == 0) {
+        return acc;
+    } else if constexpr (EPI == 1) {
+        return acc + b;
+    } else {
+        return gelu_erf(acc + b);
+    }
+}
+
+// Accumulator layout of v_mfma_f32_32x32x16_f16 with the B fragment as the first operand
+// and the A fragment as the second: register r of lane l holds
+// C[m = l % 32][n = 8*(r / 4) + 4*(l / 32) + r % 4] of its 32x32 block, so each lane owns
+// four consecutive columns per register quad and writes them as one 8-byte store.
+//
+// Stores the FM x FN blocks of one wavefront whose sub-tile starts at (row0, col0) inside
+// the workgroup tile at (m0, n0).  Rows >= M are dropped by the C descriptor's range,
+// columns >= N by an explicit mask.
+// tile_rows = min(BM, M - m0) (at most 256, so tile_rows * N stays below 2^30).
+template <int FM, int FN, bool BV, int EPI>
+__device__ __forceinline__ void store_tile(const f32x16 (&acc)[FM][FN], const GemmArgs &p,
+                                           int m0, int n0, int tile_rows, int row0, int col0,
+                                           int lane)
+{
+    const int cols_valid = p.N - n0;
+    // C covers rows [m0, m0 + tile_rows) from column n0
+    const __amdgpu_buffer_rsrc_t c_rs =
+        make_rsrc(p.C + (int64_t)m0 * p.N + n0, (uint32_t)(tile_rows * p.N - n0) * 2u);
+    // bias covers columns [n0, N); with no epilogue it is never read
+    const __amdgpu_buffer_rsrc_t b_rs =
+        make_rsrc(EPI != 0 ? p.bias + n0 : p.C, EPI != 0 ? (uint32_t)cols_valid * 2u : 0u);
+
+    const int frag_row = lane & 31;
+    const int lane_n = 4 * (lane >> 5);
+#pragma unroll
+    for (int j = 0; j < FN; ++j) {
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+            const int n = col0 + j * 32 + 8 * g + lane_n;   // relative to n0
+            float bv[4] = {0.f, 0.f, 0.f, 0.f};
+            if constexpr (EPI != 0) {
+                if constexpr (BV) {
+                    const u32x2 raw = __builtin_amdgcn_raw_buffer_load_b64(b_rs, (uint32_t)n * 2u, 0, 0);
+                    const f16x4 h = __builtin_bit_cast(f16x4, raw);
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) bv[e] = (float)h[e];
+                } else {
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const uint16_t raw =
+                            __builtin_amdgcn_raw_buffer_load_b16(b_rs, (uint32_t)(n + e) * 2u, 0, 0);
+                        bv[e] = (float)__builtin_bit_cast(f16, raw);
+                    }
+                }
+            }
+#pragma unroll
+            for (int i = 0; i < FM; ++i) {
+                const int m = row0 + i * 32 + frag_row;     // relative to m0
+                // fp32 -> fp16 with round-to-nearest-even, kept as raw bit patterns
+                uint32_t hb[4];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const f16 h = (f16)epilogue_op<EPI>(acc[i][j][4 * g + e], bv[e]);
+                    hb[e] = __builtin_bit_cast(uint16_t, h);
+                }
+                if constexpr (BV) {
+                    const uint32_t off = masked_offset((uint32_t)(m * p.N + n) * 2u, n < cols_valid);
+                    const u32x2 packed = {hb[0] | (hb[1] << 16), hb[2] | (hb[3] << 16)};
+                    __builtin_amdgcn_raw_buffer_store_b64(packed, c_rs, off, 0, 0);
+                } else {
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const uint32_t off =
+                            masked_offset((uint32_t)(m * p.N + n + e) * 2u, n + e < cols_valid);
+                        __builtin_amdgcn_raw_buffer_store_b16((uint16_t)hb[e], c_rs, off, 0, 0);
+                    }
+                }
+            }
+        }
+    }
+}
+
+}  // namespace mi355

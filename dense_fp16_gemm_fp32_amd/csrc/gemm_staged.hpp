@@ -1,56 +1,21 @@
-// fp16 GEMM with fp32 accumulation and a fused bias + erf-GELU epilogue for gfx950.
+// Register-staged GEMM kernel for gfx950: serves every alignment (2-byte loads where a
+// row is not 16-byte aligned); the selector uses it for ragged and unaligned problems.
 //
-// C (M x N) = epi(A (M x K) . B (K x N) [+ bias]), all fp16 row-major, as stated by
-// "Designing High-Performance GPU Kernels with TileLang: Tensor-Core GEMM, Fused Softmax,
-// FlashAttention, and Autotuning" (thecryptopost.io page, section 2, make_matmul) with the
-// epilogue of the same tutorial's fused-epilogue paragraph (ainovat.com page).
-//
-// One workgroup computes one BM x BN macro-tile of C.  Inside it:
-//   1. tile order    -- workgroup id -> (tile row, tile column): XCD-contiguous ranges,
-//                       then GROUP_M tile-rows swept together (L2 reuse);
-//   2. loader        -- buffer loads HBM -> VGPR (16-byte vectors where the layout allows,
-//                       2-byte loads otherwise; out-of-range lanes read 0 through the buffer
-//                       descriptor's range check), then VGPR -> LDS into a 2-stage ring;
-//                       B is transposed 4x8 in registers on the way so both LDS tiles are
-//                       k-contiguous, which is what the MFMA operands want;
-//   3. MFMA loop     -- each wavefront owns a WTM x WTN sub-tile made of 32x32 blocks and
-//                       chains v_mfma_f32_32x32x16_f16 into fp32 accumulators;
-//   4. epilogue      -- + bias[n], GELU(x) = x * Phi(x) via erfc, round-to-nearest-even to
-//                       fp16, masked stores (out-of-range lanes dropped by the descriptor).
+// One workgroup computes one BM x BN macro-tile of C:
+//   1. tile order  -- tile_coords();
+//   2. loader      -- buffer loads HBM -> VGPR (16-byte vectors where the layout allows,
+//                     2-byte loads otherwise; out-of-range lanes read 0 through the buffer
+//                     descriptor's range check), then VGPR -> LDS into a 2-stage padded
+//                     ring; B is transposed 4x8 in registers on the way so both LDS tiles
+//                     are k-contiguous, as the MFMA operands want;
+//   3. MFMA loop   -- each wavefront owns a WTM x WTN sub-tile of 32x32 blocks and chains
+//                     v_mfma_f32_32x32x16_f16 into fp32 accumulators;
+//   4. epilogue    -- store_tile(): bias, GELU, fp16 rounding, masked stores.
 #pragma once
 
-#include <hip/hip_runtime.h>
-#include <stdint.h>
+#include "gemm_common.hpp"
 
 namespace mi355 {
-
-typedef _Float16 f16;
-typedef f16 f16x4 __attribute__((ext_vector_type(4)));
-typedef f16 f16x8 __attribute__((ext_vector_type(8)));
-typedef float f32x16 __attribute__((ext_vector_type(16)));
-typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-
-// A buffer offset no descriptor here ever covers (every num_records is below 2^31): a
-// load from it returns zeros and a store to it is discarded by the hardware range check.
-constexpr uint32_t kOutOfRange = 0x80000000u;
-// Buffer resource word 3 for gfx9-family raw buffers (32-bit data format, no swizzle).
-constexpr int kRsrcWord3 = 0x00020000;
-
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, uint32_t bytes)
-{
-    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), 0, (int)bytes, kRsrcWord3);
-}
-
-struct GemmArgs {
-    const f16 *A;
-    const f16 *B;
-    f16 *C;
-    const f16 *bias;
-    int M, N, K;
-    int tiles_m, tiles_n;
-    int group_m;
-};
 
 template <int BM_, int BN_, int BK_, int WAVES_M_, int WAVES_N_>
 struct Tile {
@@ -68,29 +33,7 @@ struct Tile {
     static_assert(LDS_BYTES <= 160 * 1024, "over the gfx950 LDS budget");
 };
 
-// ---------------------------------------------------------------- tile order (1) ----
-// Workgroups are handed to the 8 XCDs round-robin (id % 8).  Renumber them so each XCD
-// owns one contiguous range of the logical order; the logical order sweeps GROUP_M
-// tile-rows column by column, so tiles resident at the same time share A row-panels and
-// B column-panels in that XCD's L2.
-__device__ __forceinline__ void tile_coords(int bid, int tiles_m, int tiles_n, int group_m,
-                                            int &tm, int &tn)
-{
-    const int total = tiles_m * tiles_n;
-    const int xcd = bid & 7, idx = bid >> 3;
-    const int per = total >> 3, rem = total & 7;
-    const int lid = (xcd < rem) ? xcd * (per + 1) + idx
-                                : rem * (per + 1) + (xcd - rem) * per + idx;
-    const int width = group_m * tiles_n;
-    const int g = lid / width;
-    const int first_m = g * group_m;
-    const int gsz = min(tiles_m - first_m, group_m);
-    const int r = lid - g * width;
-    tm = first_m + r % gsz;
-    tn = r / gsz;
-}
-
-// ---------------------------------------------------------------- loader (2) --------
+// ---------------------------------------------------------------- loader ----------
 // A tile: BM rows x BK halves, stored in LDS as [row][k] (k contiguous).
 template <class T, bool VEC>
 struct ALoader {
@@ -107,15 +50,15 @@ struct ALoader {
             const int v = tid + i * T::NT;
             const int row = v / VPR, k = k0 + 8 * (v % VPR);
             if constexpr (VEC) {
-                const uint32_t off = (k < K) ? (uint32_t)(row * K + k) * 2u : kOutOfRange;
+                const uint32_t off = masked_offset((uint32_t)(row * K + k) * 2u, k < K);
                 r[i] = __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, 0);
             } else {
                 uint32_t w[4];
 #pragma unroll
                 for (int s = 0; s < 4; ++s) {
                     const int ka = k + 2 * s, kb = ka + 1;
-                    const uint32_t oa = (ka < K) ? (uint32_t)(row * K + ka) * 2u : kOutOfRange;
-                    const uint32_t ob = (kb < K) ? (uint32_t)(row * K + kb) * 2u : kOutOfRange;
+                    const uint32_t oa = masked_offset((uint32_t)(row * K + ka) * 2u, ka < K);
+                    const uint32_t ob = masked_offset((uint32_t)(row * K + kb) * 2u, kb < K);
                     const uint32_t lo = __builtin_amdgcn_raw_buffer_load_b16(rs, oa, 0, 0);
                     const uint32_t hi = __builtin_amdgcn_raw_buffer_load_b16(rs, ob, 0, 0);
                     w[s] = lo | (hi << 16);
@@ -163,16 +106,15 @@ struct BLoader {
             for (int j = 0; j < 4; ++j) {
                 const int row = 4 * q + j;
                 if constexpr (VEC) {
-                    const uint32_t off =
-                        (8 * c < cols) ? (uint32_t)(row * N + 8 * c) * 2u : kOutOfRange;
+                    const uint32_t off = masked_offset((uint32_t)(row * N + 8 * c) * 2u, 8 * c < cols);
                     r[i][j] = __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, 0);
                 } else {
                     uint32_t w[4];
 #pragma unroll
                     for (int s = 0; s < 4; ++s) {
                         const int na = 8 * c + 2 * s, nb = na + 1;
-                        const uint32_t oa = (na < cols) ? (uint32_t)(row * N + na) * 2u : kOutOfRange;
-                        const uint32_t ob = (nb < cols) ? (uint32_t)(row * N + nb) * 2u : kOutOfRange;
+                        const uint32_t oa = masked_offset((uint32_t)(row * N + na) * 2u, na < cols);
+                        const uint32_t ob = masked_offset((uint32_t)(row * N + nb) * 2u, nb < cols);
                         const uint32_t lo = __builtin_amdgcn_raw_buffer_load_b16(rs, oa, 0, 0);
                         const uint32_t hi = __builtin_amdgcn_raw_buffer_load_b16(rs, ob, 0, 0);
                         w[s] = lo | (hi << 16);
@@ -206,37 +148,13 @@ struct BLoader {
     }
 };
 
-// ---------------------------------------------------------------- epilogue (4) ------
-// GELU(x) = x * Phi(x), Phi(x) = 1 - erfc(x/sqrt2)/2 for x >= 0 and erfc(|x|/sqrt2)/2
-// for x < 0; one erfc evaluation, no cancellation on the negative side.
-__device__ __forceinline__ float gelu_erf(float x)
-{
-    const float q = erfcf(fabsf(x) * 0.70710678118654752f);
-    const float phi = (x >= 0.0f) ? 1.0f - 0.5f * q : 0.5f * q;
-    return x * phi;
-}
-
-template <int EPI>
-__device__ __forceinline__ float epilogue_op(float acc, float b)
-{
-    if constexpr (EPI == 0) {
-        return acc;
-    } else if constexpr (EPI == 1) {
-        return acc + b;
-    } else {
-        return gelu_erf(acc + b);
-    }
-}
-
 // ---------------------------------------------------------------- kernel ------------
-// MFMA operand/result layout for v_mfma_f32_32x32x16_f16 as used here: operand lane l
-// holds 8 consecutive-k values of row (l % 32) at k offset 8*(l / 32) -- the same k map
-// for both operands, which is all the product needs.  With the B fragment as the first
-// operand and the A fragment as the second, result register r of lane l is
-// C[m = l % 32][n = 8*(r / 4) + 4*(l / 32) + r % 4], so each lane owns four consecutive
-// columns per register quad and stores them as one 8-byte write.
+// MFMA operand layout for v_mfma_f32_32x32x16_f16 as used here: operand lane l holds 8
+// consecutive-k values of row (l % 32) at k offset 8*(l / 32) -- the same k map for both
+// operands, which is all the product needs.  The result layout is described at
+// store_tile().
 template <class T, bool AV, bool BV, int EPI>
-__global__ void __launch_bounds__(T::NT) gemm_kernel(GemmArgs p)
+__global__ void __launch_bounds__(T::NT) gemm_staged(GemmArgs p)
 {
     __shared__ __attribute__((aligned(16))) f16 lds[T::STAGES * (T::A_STAGE + T::B_STAGE)];
     f16 *const As = lds;
@@ -250,7 +168,6 @@ __global__ void __launch_bounds__(T::NT) gemm_kernel(GemmArgs p)
     tile_coords(blockIdx.x, p.tiles_m, p.tiles_n, p.group_m, tm, tn);
     const int m0 = tm * T::BM, n0 = tn * T::BN;
     const int rows_valid = min(T::BM, p.M - m0);
-    const int cols_valid = p.N - n0;
 
     const __amdgpu_buffer_rsrc_t a_rs =
         make_rsrc(p.A + (int64_t)m0 * p.K, (uint32_t)(rows_valid * p.K) * 2u);
@@ -311,56 +228,7 @@ __global__ void __launch_bounds__(T::NT) gemm_kernel(GemmArgs p)
         __syncthreads();
     }
 
-    // ---- epilogue: bias, GELU, fp16 rounding, masked store ----
-    const __amdgpu_buffer_rsrc_t c_rs =
-        make_rsrc(p.C + (int64_t)m0 * p.N + n0, (uint32_t)(rows_valid * p.N - n0) * 2u);
-    // bias covers columns [n0, N); with no epilogue it is never read
-    const __amdgpu_buffer_rsrc_t b_rs =
-        make_rsrc(EPI != 0 ? p.bias + n0 : p.C, EPI != 0 ? (uint32_t)cols_valid * 2u : 0u);
-
-    const int lane_n = 4 * (lane >> 5);
-#pragma unroll
-    for (int j = 0; j < T::FN; ++j) {
-#pragma unroll
-        for (int g = 0; g < 4; ++g) {
-            const int n = wn * T::WTN + j * 32 + 8 * g + lane_n;   // relative to n0
-            float bv[4] = {0.f, 0.f, 0.f, 0.f};
-            if constexpr (EPI != 0) {
-                if constexpr (BV) {
-                    const u32x2 raw = __builtin_amdgcn_raw_buffer_load_b64(b_rs, (uint32_t)n * 2u, 0, 0);
-                    const f16x4 h = __builtin_bit_cast(f16x4, raw);
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) bv[e] = (float)h[e];
-                } else {
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        const uint16_t raw =
-                            __builtin_amdgcn_raw_buffer_load_b16(b_rs, (uint32_t)(n + e) * 2u, 0, 0);
-                        bv[e] = (float)__builtin_bit_cast(f16, raw);
-                    }
-                }
-            }
-#pragma unroll
-            for (int i = 0; i < T::FM; ++i) {
-                const int m = wm * T::WTM + i * 32 + frag_row;     // relative to m0
-                f16x4 h;
-#pragma unroll
-                for (int e = 0; e < 4; ++e)
-                    h[e] = (f16)epilogue_op<EPI>(acc[i][j][4 * g + e], bv[e]);
-                if constexpr (BV) {
-                    const uint32_t off = (n < cols_valid) ? (uint32_t)(m * p.N + n) * 2u : kOutOfRange;
-                    __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, h), c_rs, off, 0, 0);
-                } else {
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        const uint32_t off =
-                            (n + e < cols_valid) ? (uint32_t)(m * p.N + n + e) * 2u : kOutOfRange;
-                        __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(uint16_t, h[e]), c_rs, off, 0, 0);
-                    }
-                }
-            }
-        }
-    }
+    store_tile<T::FM, T::FN, BV, EPI>(acc, p, m0, n0, rows_valid, wm * T::WTM, wn * T::WTN, lane);
 }
 
 }  // namespace mi355

@@ -9,7 +9,34 @@
 #include <stdint.h>
 #include <stdio.h>
 
-#include "gemm_kernel.hpp"
+#include "gemm_direct.hpp"
+#include "gemm_staged.hpp"
+
+// direct-to-LDS tiles: BM, BN, BK, waves (M x N), LDS stages
+namespace mi355 {
+using D256 = DTile<256, 256, 64, 2, 2, 2>;       // 4 waves of 128x128, 128 KiB LDS
+using D256x128 = DTile<256, 128, 64, 2, 2, 3>;   // 4 waves of 128x64, 144 KiB
+using D128x256 = DTile<128, 256, 64, 2, 2, 3>;   // 4 waves of 64x128, 144 KiB
+using D128 = DTile<128, 128, 64, 2, 2, 4>;       // 4 waves of 64x64, 128 KiB
+using D128k32 = DTile<128, 128, 32, 2, 2, 4>;    // 4 waves of 64x64, 64 KiB
+// register-staged tiles (any alignment)
+using T64 = Tile<64, 64, 64, 2, 1>;              // 2 waves of 32x64
+using T128 = Tile<128, 128, 64, 2, 2>;           // 4 waves of 64x64
+using T256 = Tile<256, 256, 64, 2, 2>;           // 4 waves of 128x128
+
+// Explicit instantiations: every kernel the configuration table points at gets a host
+// launch stub.
+#define MI355_DIRECT(T)                                   \
+    template __global__ void gemm_direct<T, 0>(GemmArgs); \
+    template __global__ void gemm_direct<T, 1>(GemmArgs); \
+    template __global__ void gemm_direct<T, 2>(GemmArgs);
+MI355_DIRECT(D256)
+MI355_DIRECT(D256x128)
+MI355_DIRECT(D128x256)
+MI355_DIRECT(D128)
+MI355_DIRECT(D128k32)
+#undef MI355_DIRECT
+}  // namespace mi355
 
 namespace {
 
@@ -30,6 +57,7 @@ typedef void (*KernelFn)(GemmArgs);
 
 struct Config {
     const char *name;
+    bool direct;      // direct-to-LDS kernel (16-byte operands) or register-staged kernel
     int bm, bn, bk, stages, waves_m, waves_n, threads, lds_bytes;
     bool a_vec, bc_vec;
     int group_m;
@@ -37,29 +65,36 @@ struct Config {
 };
 
 template <class T, bool AV, bool BV>
-constexpr Config make_config(const char *name, int group_m)
+Config staged_config(const char *name, int group_m)
 {
-    return Config{name, T::BM, T::BN, T::BK, T::STAGES, T::WAVES_M, T::WAVES_N, T::NT,
+    return Config{name, false, T::BM, T::BN, T::BK, T::STAGES, T::WAVES_M, T::WAVES_N, T::NT,
                   T::LDS_BYTES, AV, BV, group_m,
-                  {gemm_kernel<T, AV, BV, 0>, gemm_kernel<T, AV, BV, 1>, gemm_kernel<T, AV, BV, 2>}};
+                  {gemm_staged<T, AV, BV, 0>, gemm_staged<T, AV, BV, 1>, gemm_staged<T, AV, BV, 2>}};
 }
 
-using T64 = Tile<64, 64, 64, 2, 1>;       // 2 waves of 32x64
-using T128 = Tile<128, 128, 64, 2, 2>;    // 4 waves of 64x64
-using T256x128 = Tile<256, 128, 64, 2, 2>;  // 4 waves of 128x64
-using T256 = Tile<256, 256, 64, 2, 2>;    // 4 waves of 128x128
+template <class T>
+Config direct_config(const char *name, int group_m)
+{
+    return Config{name, true, T::BM, T::BN, T::BK, T::STAGES, T::WAVES_M, T::WAVES_N, T::NT,
+                  T::LDS_BYTES, true, true, group_m,
+                  {gemm_direct<T, 0>, gemm_direct<T, 1>, gemm_direct<T, 2>}};
+}
 
 const Config kConfigs[] = {
-    make_config<T256, true, true>("256x256x64_w2x2_av_bv", 8),
-    make_config<T256x128, true, true>("256x128x64_w2x2_av_bv", 8),
-    make_config<T128, true, true>("128x128x64_w2x2_av_bv", 8),
-    make_config<T128, true, false>("128x128x64_w2x2_av_bn", 8),
-    make_config<T128, false, true>("128x128x64_w2x2_an_bv", 8),
-    make_config<T128, false, false>("128x128x64_w2x2_an_bn", 8),
-    make_config<T64, true, true>("64x64x64_w2x1_av_bv", 8),
-    make_config<T64, true, false>("64x64x64_w2x1_av_bn", 8),
-    make_config<T64, false, true>("64x64x64_w2x1_an_bv", 8),
-    make_config<T64, false, false>("64x64x64_w2x1_an_bn", 8),
+    direct_config<D256>("d256x256x64_w2x2_s2", 8),
+    direct_config<D256x128>("d256x128x64_w2x2_s3", 8),
+    direct_config<D128x256>("d128x256x64_w2x2_s3", 8),
+    direct_config<D128>("d128x128x64_w2x2_s4", 8),
+    direct_config<D128k32>("d128x128x32_w2x2_s4", 8),
+    staged_config<T256, true, true>("s256x256x64_w2x2_av_bv", 8),
+    staged_config<T128, true, true>("s128x128x64_w2x2_av_bv", 8),
+    staged_config<T128, true, false>("s128x128x64_w2x2_av_bn", 8),
+    staged_config<T128, false, true>("s128x128x64_w2x2_an_bv", 8),
+    staged_config<T128, false, false>("s128x128x64_w2x2_an_bn", 8),
+    staged_config<T64, true, true>("s64x64x64_w2x1_av_bv", 8),
+    staged_config<T64, true, false>("s64x64x64_w2x1_av_bn", 8),
+    staged_config<T64, false, true>("s64x64x64_w2x1_an_bv", 8),
+    staged_config<T64, false, false>("s64x64x64_w2x1_an_bn", 8),
 };
 constexpr int kNumConfigs = (int)(sizeof(kConfigs) / sizeof(kConfigs[0]));
 
@@ -115,11 +150,12 @@ int64_t tiles(const Request &r, int bm, int bn)
     return ((r.M + bm - 1) / bm) * ((r.N + bn - 1) / bn);
 }
 
-int find_config(int bm, int bn, bool av, bool bv)
+int find_config(bool direct, int bm, int bn, bool av, bool bv)
 {
     for (int i = 0; i < kNumConfigs; ++i) {
         const Config &c = kConfigs[i];
-        if (c.bm == bm && c.bn == bn && c.a_vec == av && c.bc_vec == bv) return i;
+        if (c.direct == direct && c.bm == bm && c.bn == bn && c.a_vec == av && c.bc_vec == bv)
+            return i;
     }
     return -1;
 }
@@ -133,11 +169,12 @@ int choose(const Request &r)
     const bool av = a_vector_ok(r), bv = bc_vector_ok(r);
     constexpr int64_t kCUs = 256;
     if (av && bv) {
-        if (tiles(r, 256, 256) >= 2 * kCUs) return find_config(256, 256, true, true);
-        if (tiles(r, 256, 128) >= 2 * kCUs) return find_config(256, 128, true, true);
+        if (tiles(r, 256, 256) >= 2 * kCUs) return find_config(true, 256, 256, true, true);
+        if (tiles(r, 256, 128) >= 2 * kCUs) return find_config(true, 256, 128, true, true);
+        if (tiles(r, 128, 128) >= kCUs / 2) return find_config(true, 128, 128, true, true);
     }
-    if (tiles(r, 128, 128) >= kCUs / 2) return find_config(128, 128, av, bv);
-    return find_config(64, 64, av, bv);
+    if (tiles(r, 128, 128) >= kCUs / 2) return find_config(false, 128, 128, av, bv);
+    return find_config(false, 64, 64, av, bv);
 }
 
 // Can configuration c serve request r?
@@ -253,6 +290,7 @@ mi355gemm_status mi355gemm_config_info(int config_id, mi355gemm_config_desc *out
     out->a_vector = c.a_vec;
     out->bc_vector = c.bc_vec;
     out->group_m = c.group_m;
+    out->direct = c.direct;
     return MI355GEMM_OK;
 }
 

@@ -105,6 +105,7 @@ typedef struct {
     int a_vector;                   /* 1: A loaded in 16-byte vectors (needs K % 8 == 0) */
     int bc_vector;                  /* 1: B loaded and C stored in vectors (N % 8 == 0) */
     int group_m;                    /* tile-rows per group in the tile order */
+    int direct;                     /* 1: HBM -> LDS copies without register staging */
 } mi355gemm_config_desc;
 
 /* Number of compiled configurations (ids 0 .. n-1). Host-only. */

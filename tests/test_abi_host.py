@@ -51,9 +51,15 @@ def test_config_table_is_consistent():
     assert len(cfgs) == g.mi355gemm_num_configs() >= 4
     names = [c["name"] for c in cfgs]
     assert len(set(names)) == len(names)
+    assert any(c["direct"] for c in cfgs) and any(not c["direct"] for c in cfgs)
     for c in cfgs:
-        # two LDS stages of BM and BN rows of BK halves plus a 16-byte pad per row
-        assert c["lds_bytes"] == c["stages"] * (c["block_m"] + c["block_n"]) * (c["block_k"] + 8) * 2
+        if c["direct"]:
+            # ring of STAGES buffers of the A (BM x BK) and B (BK x BN) tiles, XOR-swizzled
+            assert c["lds_bytes"] == c["stages"] * (c["block_m"] + c["block_n"]) * c["block_k"] * 2
+            assert c["a_vector"] == 1 and c["bc_vector"] == 1
+        else:
+            # two LDS stages of BM and BN rows of BK halves plus a 16-byte pad per row
+            assert c["lds_bytes"] == c["stages"] * (c["block_m"] + c["block_n"]) * (c["block_k"] + 8) * 2
         assert c["lds_bytes"] <= g.mi355gemm_lds_budget()
         assert c["threads"] == 64 * c["waves_m"] * c["waves_n"]
         assert c["block_m"] % (32 * c["waves_m"]) == 0 and c["block_n"] % (32 * c["waves_n"]) == 0
