@@ -18,6 +18,7 @@ typedef _Float16 f16;
 typedef f16 f16x4 __attribute__((ext_vector_type(4)));
 typedef f16 f16x8 __attribute__((ext_vector_type(8)));
 typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
@@ -99,11 +100,11 @@ __device__ __forceinline__ float epilogue_op(float acc, float b)
 // C[m = l % 32][n = 8*(r / 4) + 4*(l / 32) + r % 4] of its 32x32 block, so each lane owns
 // four consecutive columns per register quad and writes them as one 8-byte store.
 //
-// Stores the FM x FN blocks of one wavefront whose sub-tile starts at (row0, col0) inside
-// the workgroup tile at (m0, n0).  Rows >= M are dropped by the C descriptor's range,
+// Stores block rows I0 <= i < I1 of the FM x FN blocks of one wavefront whose sub-tile
+// starts at (row0, col0) inside the workgroup tile at (m0, n0).  Rows >= M are dropped by the C descriptor's range,
 // columns >= N by an explicit mask.
 // tile_rows = min(BM, M - m0) (at most 256, so tile_rows * N stays below 2^30).
-template <int FM, int FN, bool BV, int EPI>
+template <int FM, int FN, int I0, int I1, bool BV, int EPI>
 __device__ __forceinline__ void store_tile(const f32x16 (&acc)[FM][FN], const GemmArgs &p,
                                            int m0, int n0, int tile_rows, int row0, int col0,
                                            int lane)
@@ -140,7 +141,7 @@ __device__ __forceinline__ void store_tile(const f32x16 (&acc)[FM][FN], const Ge
                 }
             }
 #pragma unroll
-            for (int i = 0; i < FM; ++i) {
+            for (int i = I0; i < I1; ++i) {
                 const int m = row0 + i * 32 + frag_row;     // relative to m0
                 // fp32 -> fp16 with round-to-nearest-even, kept as raw bit patterns
                 uint32_t hb[4];

@@ -1,19 +1,24 @@
 // Direct-to-LDS GEMM kernel for gfx950: the fast path for 16-byte-friendly operands
 // (K % 8 == 0 and N % 8 == 0, 16-byte aligned A, B, C).
 //
-// One workgroup (WAVES_M x WAVES_N wavefronts) computes one BM x BN macro-tile of C:
+// One workgroup computes one BM x BN macro-tile of C with WAVES_M x WAVES_N x KGROUPS
+// wavefronts (two per SIMD in the shipped configurations, so one wave's LDS reads and
+// barrier waits are covered by the other's MFMAs):
 //   1. tile order  -- tile_coords(): XCD-contiguous ranges, GROUP_M tile-rows per sweep;
 //   2. loader      -- buffer_load_dwordx4 ... lds: HBM -> LDS with no VGPR staging, into a
-//                     ring of STAGES buffers (one __shared__ object per stage, so the
-//                     compiler can tell the stages apart); the copy for stage kt+STAGES-1
-//                     is in flight while stage kt is multiplied.  A lands k-contiguous,
-//                     B lands in its HBM order (n-contiguous); both are XOR-swizzled in
-//                     16-byte chunks so the fragment reads below hit distinct banks;
+//                     ring of STAGES buffers; the copy for stage kt+STAGES-1 is in flight
+//                     while stage kt is multiplied.  A lands k-contiguous, B lands in its
+//                     HBM order (n-contiguous); both are XOR-swizzled in 16-byte chunks so
+//                     the fragment reads below hit distinct banks;
 //   3. MFMA loop   -- A fragments come from ds_read_b128, B fragments from two
 //                     ds_read_b64_tr_b16 (gfx950's transposing LDS read turns four
-//                     n-contiguous rows into k-contiguous lane data); fragment reads for
-//                     the next k-step are issued before the MFMAs of the current one, and
-//                     the last k-step's MFMAs cover the barrier into the next stage;
+//                     n-contiguous rows into k-contiguous lane data).  With KGROUPS = 2 the
+//                     16-deep k-steps of a stage alternate between two groups of waves that
+//                     each own a full copy of the accumulator tile (a split of K inside the
+//                     workgroup, summed through LDS at the end): two waves per SIMD without
+//                     extra LDS traffic.  The instruction order inside a k-step is fixed in
+//                     the source: after each MFMA come the LDS reads for the next k-step and
+//                     a share of the HBM -> LDS copies, fenced with sched_barrier;
 //   4. epilogue    -- store_tile(): bias, erf-GELU, fp16 rounding, masked stores.
 //
 // Out-of-range rows, columns and the K tail read as zero through the buffer descriptors'
@@ -22,35 +27,48 @@
 #pragma once
 
 #include <type_traits>
+#include <utility>
 
 #include "gemm_common.hpp"
 
 namespace mi355 {
 
-template <int BM_, int BN_, int BK_, int WAVES_M_, int WAVES_N_, int STAGES_>
+template <int BM_, int BN_, int BK_, int WAVES_M_, int WAVES_N_, int KGROUPS_, int STAGES_>
 struct DTile {
     static constexpr int BM = BM_, BN = BN_, BK = BK_;
-    static constexpr int WAVES_M = WAVES_M_, WAVES_N = WAVES_N_, STAGES = STAGES_;
-    static constexpr int NW = WAVES_M * WAVES_N;
+    static constexpr int WAVES_M = WAVES_M_, WAVES_N = WAVES_N_;
+    static constexpr int KGROUPS = KGROUPS_, STAGES = STAGES_;
+    static constexpr int NWC = WAVES_M * WAVES_N;    // waves of one k-group
+    static constexpr int NW = NWC * KGROUPS;
     static constexpr int NT = 64 * NW;
     static constexpr int WTM = BM / WAVES_M, WTN = BN / WAVES_N;
     static constexpr int FM = WTM / 32, FN = WTN / 32;
-    static constexpr int KK = BK / 16;              // MFMA k-steps per stage
-    static constexpr int CA = BK / 8;               // 16-byte chunks per A row
-    static constexpr int CB = BN / 8;               // 16-byte chunks per B row
+    static constexpr int NMFMA = FM * FN;            // MFMAs per k-step per wave
+    static constexpr int NREAD = FM + 2 * FN;        // LDS reads per k-step per wave
+    static constexpr int KK = BK / 16;               // 16-deep k-steps per stage
+    static constexpr int Q = KK / KGROUPS;           // k-steps per stage per wave
+    static constexpr int CA = BK / 8;                // 16-byte chunks per A row
+    static constexpr int CB = BN / 8;                // 16-byte chunks per B row
     static constexpr int A_BYTES = BM * BK * 2, B_BYTES = BK * BN * 2;
+    static constexpr int STAGE_BYTES = A_BYTES + B_BYTES;
     static constexpr int GA = A_BYTES / (1024 * NW);   // 1 KiB LDS-DMA loads per wave
     static constexpr int GB = B_BYTES / (1024 * NW);
     static constexpr int G = GA + GB;
-    static constexpr int LDS_BYTES = STAGES * (A_BYTES + B_BYTES);
+    static constexpr int LDS_BYTES = STAGES * STAGE_BYTES;
+    // k-group exchange at the end: every wave hands half of its 32x32 fp32 blocks (4 KiB
+    // each) to its partner in the other group
+    static constexpr int RED_BYTES = KGROUPS > 1 ? NW * (NMFMA / 2) * 4096 : 0;
     static_assert(WTM % 32 == 0 && WTN % 32 == 0, "wave tile must be whole 32x32 blocks");
     static_assert(BK == 32 || BK == 64, "A swizzle assumes 4 or 8 chunks per row");
     static_assert(CB >= 16, "B swizzle assumes rows of at least 256 bytes");
     static_assert(A_BYTES % (1024 * NW) == 0 && B_BYTES % (1024 * NW) == 0,
                   "stage must split into whole 1 KiB loads per wave");
-    static_assert(STAGES >= 2 && STAGES <= 4 && G * (STAGES - 2) <= 63, "ring size / vmcnt range");
-    static_assert(KK % 2 == 0, "fragment double-buffer parity assumes an even k-step count");
+    static_assert(KGROUPS == 1 || (KGROUPS == 2 && FM % 2 == 0), "k-groups: 1, or 2 with even FM");
+    static_assert(KK % KGROUPS == 0, "k-steps must split evenly over the k-groups");
+    static_assert((STAGES * Q) % 2 == 0, "fragment double-buffer parity must repeat per ring turn");
+    static_assert(STAGES >= 2 && STAGES <= 5 && G * (STAGES - 2) <= 63, "ring size / vmcnt range");
     static_assert(LDS_BYTES <= 160 * 1024, "over the gfx950 LDS budget");
+    static_assert(RED_BYTES <= LDS_BYTES, "k-group exchange must fit in the ring");
 };
 
 template <class T>
@@ -102,8 +120,9 @@ __device__ __forceinline__ __attribute__((address_space(3))) void *lds_ptr(const
 // LDS at lds + 16*l.  Written as inline assembly on purpose: the compiler cannot tell the
 // ring slots apart once it has packed them into one LDS block, and would then wait for
 // every copy in flight before each LDS read.  The kernel waits for these copies itself
-// (wait_counts before each barrier) and for all of them before it ends.  Nothing else in
-// the kernels uses M0.
+// (wait_counts before each barrier) and for all of them before it ends.  M0 is a reserved
+// register the compiler sets right before each instruction of its own that reads it; the
+// kernels here have none, so writing it here disturbs nothing.
 __device__ __forceinline__ void lds_dma16(__amdgpu_buffer_rsrc_t rsrc, const void *lds,
                                           uint32_t voffset)
 {
@@ -118,7 +137,7 @@ __device__ __forceinline__ void lds_dma16(__amdgpu_buffer_rsrc_t rsrc, const voi
 template <class T>
 struct DirectWave {
     using St = Stage<T>;
-    int lane, wave, wm, wn;
+    int lane, wave, kg, wm, wn;
     int K, N, n0;
     const f16 *B;
     __amdgpu_buffer_rsrc_t a_rs;
@@ -126,11 +145,13 @@ struct DirectWave {
     int a_kc[T::GA];          // k of the chunk within the stage
     uint32_t b_off[T::GB];
     int a_row_byte[T::FM];
-    int a_chunk_byte[T::KK];
+    int a_chunk_byte[T::Q];   // per k-step of this wave
+    int b_k_byte[T::Q];
     int b_col_byte[T::FN];
     int b_row_byte;
     f32x16 acc[T::FM][T::FN];
-    f16x8 af[2][T::FM], bf[2][T::FN];
+    f16x8 af[2][T::FM];
+    s16x4 bl[2][T::FN], bh[2][T::FN];
 
     __device__ __forceinline__ void init(const GemmArgs &p, int m0, int n0_, int rows_valid,
                                          int cols_valid)
@@ -138,8 +159,10 @@ struct DirectWave {
         const int tid = threadIdx.x;
         lane = tid & 63;
         wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform: LDS-DMA base
-        wm = wave / T::WAVES_N;
-        wn = wave % T::WAVES_N;
+        kg = wave / T::NWC;
+        const int wc = wave % T::NWC;
+        wm = wc / T::WAVES_N;
+        wn = wc % T::WAVES_N;
         K = p.K;
         N = p.N;
         n0 = n0_;
@@ -165,14 +188,19 @@ struct DirectWave {
         }
         // A fragment: row wm*WTM + i*32 + r32, logical chunk 2*kk + h -> physical chunk
         // ^ swz_a(row); swz_a depends on the row only through r32 (WTM and 32 are
-        // multiples of 16 * rows-per-256-bytes).
+        // multiples of 16 * rows-per-256-bytes).  This wave's k-steps are kk = kg +
+        // KGROUPS * q.
         const int h = lane >> 5;
         const int r32 = lane & 31;
         const int sa = swz_a<T>(r32);
 #pragma unroll
         for (int i = 0; i < T::FM; ++i) a_row_byte[i] = (wm * T::WTM + i * 32 + r32) * T::BK * 2;
 #pragma unroll
-        for (int kk = 0; kk < T::KK; ++kk) a_chunk_byte[kk] = ((2 * kk + h) ^ sa) * 16;
+        for (int q = 0; q < T::Q; ++q) {
+            const int kk = kg + T::KGROUPS * q;
+            a_chunk_byte[q] = ((2 * kk + h) ^ sa) * 16;
+            b_k_byte[q] = (16 * kk) * T::BN * 2;
+        }
         // B fragment (transposing read): lane i of each 16-lane group points at k-row i/4
         // of its group's 4-row band and columns 4*(i%4) .. +3 of its 16-column half; lane j
         // then receives B[band + 0..3][half + j].  Band = 16*kk + 8*h + 4*t, t = 0 or 1.
@@ -191,63 +219,86 @@ struct DirectWave {
                 acc[i][j] = f32x16{};
     }
 
-    // HBM -> LDS copy of stage kt (A rows [m0, m0+BM) x k [k0, k0+BK), B k-rows x
-    // columns [n0, n0+BN)) into dst.  A stage past the end of K copies zeros (every
-    // offset falls out of range), which keeps the issue pattern, and so the counter
-    // arithmetic below, the same in every iteration.
-    __device__ __forceinline__ void issue_stage(St &dst, int kt) const
+    // Piece g (0 <= g < G) of the HBM -> LDS copy of stage kt (A rows [m0, m0+BM) x k
+    // [k0, k0+BK), B k-rows x columns [n0, n0+BN)) into dst.  A stage past the end of K
+    // copies zeros (every offset falls out of range), which keeps the issue pattern, and
+    // so the counter arithmetic below, the same in every iteration.
+    __device__ __forceinline__ void issue_piece(St &dst, int kt, int g) const
     {
         const int k0 = kt * T::BK;
-#pragma unroll
-        for (int g = 0; g < T::GA; ++g) {
+        if (g < T::GA) {
             const uint32_t off = masked_offset(a_off[g] + (uint32_t)k0 * 2u, k0 + a_kc[g] < K);
             lds_dma16(a_rs, dst.a + (g * T::NW + wave) * 512, off);
-        }
-        const int rows_k = min(T::BK, K - k0);
-        const __amdgpu_buffer_rsrc_t b_rs = make_rsrc(
-            B + (int64_t)min(k0, K) * N + n0, rows_k > 0 ? (uint32_t)(rows_k * N - n0) * 2u : 0u);
-#pragma unroll
-        for (int g = 0; g < T::GB; ++g) {
-            lds_dma16(b_rs, dst.b + (g * T::NW + wave) * 512, b_off[g]);
+        } else {
+            const int gb = g - T::GA;
+            const int rows_k = min(T::BK, K - k0);
+            const __amdgpu_buffer_rsrc_t b_rs =
+                make_rsrc(B + (int64_t)min(k0, K) * N + n0,
+                          rows_k > 0 ? (uint32_t)(rows_k * N - n0) * 2u : 0u);
+            lds_dma16(b_rs, dst.b + (gb * T::NW + wave) * 512, b_off[gb]);
         }
     }
 
-    __device__ __forceinline__ void read_frags(const St &src, int kk, int buf)
+    __device__ __forceinline__ void issue_stage(St &dst, int kt) const
+    {
+#pragma unroll
+        for (int g = 0; g < T::G; ++g) issue_piece(dst, kt, g);
+    }
+
+    // Read r (0 <= r < NREAD) of the fragments for this wave's k-step q of stage src, into
+    // fragment buffer buf.  Order: A block 0, then both halves of every B block, then the
+    // other A blocks -- the order the MFMAs (i outer, j inner) first need them.
+    __device__ __forceinline__ void read_one(const St &src, int q, int buf, int r)
     {
         const char *abase = reinterpret_cast<const char *>(src.a);
         const char *bbase = reinterpret_cast<const char *>(src.b);
-#pragma unroll
-        for (int i = 0; i < T::FM; ++i)
-            af[buf][i] = *reinterpret_cast<const f16x8 *>(abase + a_row_byte[i] + a_chunk_byte[kk]);
-#pragma unroll
-        for (int j = 0; j < T::FN; ++j) {
-            const char *q = bbase + b_row_byte + (16 * kk) * T::BN * 2 + b_col_byte[j];
-            const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                (s16x4 __attribute__((address_space(3))) *)lds_ptr(q));
-            const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                (s16x4 __attribute__((address_space(3))) *)lds_ptr(q + 4 * T::BN * 2));
-            bf[buf][j] = __builtin_bit_cast(f16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+        if (r == 0 || r >= 1 + 2 * T::FN) {
+            const int i = (r == 0) ? 0 : r - 2 * T::FN;
+            af[buf][i] = *reinterpret_cast<const f16x8 *>(abase + a_row_byte[i] + a_chunk_byte[q]);
+        } else {
+            const int j = (r - 1) >> 1;
+            const char *p = bbase + b_row_byte + b_k_byte[q] + b_col_byte[j];
+            if (((r - 1) & 1) == 0)
+                bl[buf][j] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                    (s16x4 __attribute__((address_space(3))) *)lds_ptr(p));
+            else
+                bh[buf][j] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                    (s16x4 __attribute__((address_space(3))) *)lds_ptr(p + 4 * T::BN * 2));
         }
     }
 
-    __device__ __forceinline__ void mfmas(int buf)
+    __device__ __forceinline__ void read_all(const St &src, int q, int buf)
     {
 #pragma unroll
-        for (int i = 0; i < T::FM; ++i)
-#pragma unroll
-            for (int j = 0; j < T::FN; ++j)
-                acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(bf[buf][j], af[buf][i], acc[i][j], 0, 0, 0);
+        for (int r = 0; r < T::NREAD; ++r) read_one(src, q, buf, r);
+    }
+
+    __device__ __forceinline__ void mfma_one(int buf, int m)
+    {
+        const int i = m / T::FN, j = m % T::FN;
+        const f16x8 b = __builtin_bit_cast(
+            f16x8, __builtin_shufflevector(bl[buf][j], bh[buf][j], 0, 1, 2, 3, 4, 5, 6, 7));
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(b, af[buf][i], acc[i][j], 0, 0, 0);
     }
 };
+
+template <int... Is, class F>
+__device__ __forceinline__ void static_for(std::integer_sequence<int, Is...>, F &&f)
+{
+    (f(std::integral_constant<int, Is>{}), ...);
+}
+
+template <int N, class F>
+__device__ __forceinline__ void static_for(F &&f)
+{
+    static_for(std::make_integer_sequence<int, N>{}, f);
+}
 
 template <class T, int EPI>
 __global__ void __launch_bounds__(T::NT) gemm_direct(GemmArgs p)
 {
     using St = Stage<T>;
-    __shared__ St st0;
-    __shared__ St st1;
-    __shared__ typename std::conditional<(T::STAGES > 2), St, char[16]>::type st2;
-    __shared__ typename std::conditional<(T::STAGES > 3), St, char[16]>::type st3;
+    __shared__ __attribute__((aligned(16))) char lds_raw[T::LDS_BYTES];
 
     int tm, tn;
     tile_coords(blockIdx.x, p.tiles_m, p.tiles_n, p.group_m, tm, tn);
@@ -258,58 +309,124 @@ __global__ void __launch_bounds__(T::NT) gemm_direct(GemmArgs p)
     DirectWave<T> w;
     w.init(p, m0, n0, rows_valid, p.N - n0);
 
-    St *const ring[4] = {&st0, &st1, reinterpret_cast<St *>(&st2), reinterpret_cast<St *>(&st3)};
+    St *const ring = reinterpret_cast<St *>(lds_raw);
 
-    // One K step on ring slot J (stage kt): start the copy of stage kt+STAGES-1 into the
-    // slot freed by stage kt-1, run the KK MFMA k-steps with the next step's fragments
-    // read ahead, and cross into stage kt+1 (wait for its copy, barrier, first fragment
-    // reads) before the last k-step's MFMAs so they cover the barrier.  The body has no
-    // branches, which keeps the compiler's LDS-DMA wait tracking exact; past the end of K
-    // it copies zeros, multiplies zeros and reads fragments it never uses.
-    auto step = [&](auto J, int kt) {
-        constexpr int j = decltype(J)::value;
-        St &cur = *ring[j];
-        w.issue_stage(*ring[(j + T::STAGES - 1) % T::STAGES], kt + T::STAGES - 1);
-#pragma unroll
-        for (int kk = 0; kk < T::KK; ++kk) {
-            const int buf = kk & 1;
-            if (kk + 1 < T::KK) {
-                w.read_frags(cur, kk + 1, buf ^ 1);
-            } else {
-                // stage kt+1 has landed once at most the STAGES-2 later copies are in
-                // flight; this wave's reads of stage kt are done before the barrier
-                wait_counts<T::G * (T::STAGES - 2), 0>();
-                workgroup_barrier();
-                w.read_frags(*ring[(j + 1) % T::STAGES], 0, buf ^ 1);
+    // One stage J of a ring turn (stage kt).  The wave runs its Q k-steps; each k-step
+    // issues its MFMAs one by one, and after each MFMA a share of the LDS reads for the
+    // wave's next k-step and, in the first k-step, a share of the HBM -> LDS copy of stage
+    // kt+STAGES-1 into the slot freed by stage kt-1.  The last k-step first waits for
+    // stage kt+1's copy and crosses the barrier, then reads the next stage's fragments
+    // while its MFMAs run.  The body has no branches on data; past the end of K it copies
+    // zeros, multiplies zeros and reads fragments it never uses.
+    auto stage = [&](auto Jc, int kt) {
+        constexpr int J = decltype(Jc)::value;
+        St &cur = ring[J];
+        St &nxt = ring[(J + 1) % T::STAGES];
+        St &dst = ring[(J + T::STAGES - 1) % T::STAGES];
+        static_for<T::Q>([&](auto qc) {
+            constexpr int q = decltype(qc)::value;
+            constexpr int buf = (J * T::Q + q) & 1;
+            constexpr bool last = (q == T::Q - 1);
+            if constexpr (T::Q == 1) {
+                w.issue_stage(dst, kt + T::STAGES - 1);
             }
-            w.mfmas(buf);
-        }
+            if constexpr (last) {
+                // stage kt+1 has landed once at most the STAGES-2 later copies are in
+                // flight; this wave's reads of stage kt were issued before the barrier
+                wait_counts<T::G * (T::STAGES - 2), 15>();
+                workgroup_barrier();
+            }
+            static_for<T::NMFMA>([&](auto mc) {
+                constexpr int m = decltype(mc)::value;
+                w.mfma_one(buf, m);
+                constexpr int r0 = m * T::NREAD / T::NMFMA;
+                constexpr int r1 = (m + 1) * T::NREAD / T::NMFMA;
+#pragma unroll
+                for (int r = r0; r < r1; ++r) {
+                    if constexpr (last)
+                        w.read_one(nxt, 0, buf ^ 1, r);
+                    else
+                        w.read_one(cur, q + 1, buf ^ 1, r);
+                }
+                if constexpr (q == 0 && T::Q > 1) {
+                    constexpr int g0 = m * T::G / T::NMFMA;
+                    constexpr int g1 = (m + 1) * T::G / T::NMFMA;
+#pragma unroll
+                    for (int g = g0; g < g1; ++g) w.issue_piece(dst, kt + T::STAGES - 1, g);
+                }
+                __builtin_amdgcn_sched_barrier(0);
+            });
+        });
     };
 
     if (nk > 0) {
         // ---- prologue: stages 0 .. STAGES-2 in flight, wait for stage 0 ----
 #pragma unroll
-        for (int s = 0; s < T::STAGES - 1; ++s) w.issue_stage(*ring[s], s);
+        for (int s = 0; s < T::STAGES - 1; ++s) w.issue_stage(ring[s], s);
         wait_counts<T::G * (T::STAGES - 2), 15>();
         workgroup_barrier();
-        w.read_frags(*ring[0], 0, 0);
+        w.read_all(ring[0], 0, 0);
 
-        // ---- main loop, unrolled over the ring so every stage is a distinct object.
+        // ---- main loop, unrolled over the ring so every slot address is a constant.
         // The step count is rounded up to a whole number of ring turns: the extra
         // stages lie past the end of K, hold zeros, and add nothing to the sums.
         const int nk_ring = (nk + T::STAGES - 1) / T::STAGES * T::STAGES;
         for (int kt = 0; kt < nk_ring; kt += T::STAGES) {
-            step(std::integral_constant<int, 0>{}, kt);
-            step(std::integral_constant<int, 1>{}, kt + 1);
-            if constexpr (T::STAGES > 2) step(std::integral_constant<int, 2>{}, kt + 2);
-            if constexpr (T::STAGES > 3) step(std::integral_constant<int, 3>{}, kt + 3);
+            static_for<T::STAGES>([&](auto jc) { stage(jc, kt + decltype(jc)::value); });
         }
         // the copies past the end of K are still landing; none may outlive the kernel
-        wait_counts<0, 15>();
+        // (and with k-groups the ring is reused below)
+        wait_counts<0, 0>();
     }
 
-    store_tile<T::FM, T::FN, true, EPI>(w.acc, p, m0, n0, rows_valid, w.wm * T::WTM,
-                                        w.wn * T::WTN, w.lane);
+    if constexpr (T::KGROUPS == 1) {
+        store_tile<T::FM, T::FN, 0, T::FM, true, EPI>(w.acc, p, m0, n0, rows_valid,
+                                                     w.wm * T::WTM, w.wn * T::WTN, w.lane);
+    } else {
+        // Sum the two k-groups' partial tiles.  Group 0 keeps blocks i < FM/2 and hands
+        // blocks i >= FM/2 to group 1; group 1 does the opposite; each then stores the half
+        // it kept.  Each 32x32 fp32 block moves as four 1 KiB ds_write_b128 / ds_read_b128
+        // (lane-contiguous, conflict-free).
+        constexpr int H = T::FM / 2;
+        workgroup_barrier();   // every wave is done reading the ring
+        float *red = reinterpret_cast<float *>(lds_raw);
+        const int wc = w.wave % T::NWC;
+        // slot of (group, wave-in-group, block) in the exchange area; the receiving wave of
+        // the other group reads the slot its partner wrote
+        auto slot_ptr = [&](int grp, int ii, int j, int c) {
+            return red + ((((grp * T::NWC + wc) * H + ii) * T::FN + j) * 4 + c) * 256 + w.lane * 4;
+        };
+        auto exchange = [&](auto give_c, auto keep_c) {
+            constexpr int GIVE = decltype(give_c)::value, KEEP = decltype(keep_c)::value;
+#pragma unroll
+            for (int ii = 0; ii < H; ++ii)
+#pragma unroll
+                for (int j = 0; j < T::FN; ++j)
+#pragma unroll
+                    for (int c = 0; c < 4; ++c) {
+                        const f32x16 &v = w.acc[GIVE + ii][j];
+                        *reinterpret_cast<f32x4 *>(slot_ptr(w.kg, ii, j, c)) =
+                            f32x4{v[4 * c], v[4 * c + 1], v[4 * c + 2], v[4 * c + 3]};
+                    }
+            __syncthreads();
+#pragma unroll
+            for (int ii = 0; ii < H; ++ii)
+#pragma unroll
+                for (int j = 0; j < T::FN; ++j)
+#pragma unroll
+                    for (int c = 0; c < 4; ++c) {
+                        const f32x4 o = *reinterpret_cast<const f32x4 *>(slot_ptr(1 - w.kg, ii, j, c));
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) w.acc[KEEP + ii][j][4 * c + e] += o[e];
+                    }
+            store_tile<T::FM, T::FN, KEEP, KEEP + H, true, EPI>(w.acc, p, m0, n0, rows_valid,
+                                                               w.wm * T::WTM, w.wn * T::WTN, w.lane);
+        };
+        if (w.kg == 0)
+            exchange(std::integral_constant<int, H>{}, std::integral_constant<int, 0>{});
+        else
+            exchange(std::integral_constant<int, 0>{}, std::integral_constant<int, H>{});
+    }
 }
 
 }  // namespace mi355

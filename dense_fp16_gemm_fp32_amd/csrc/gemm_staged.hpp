@@ -228,7 +228,7 @@ __global__ void __launch_bounds__(T::NT) gemm_staged(GemmArgs p)
         __syncthreads();
     }
 
-    store_tile<T::FM, T::FN, BV, EPI>(acc, p, m0, n0, rows_valid, wm * T::WTM, wn * T::WTN, lane);
+    store_tile<T::FM, T::FN, 0, T::FM, BV, EPI>(acc, p, m0, n0, rows_valid, wm * T::WTM, wn * T::WTN, lane);
 }
 
 }  // namespace mi355

@@ -12,13 +12,13 @@
 #include "gemm_direct.hpp"
 #include "gemm_staged.hpp"
 
-// direct-to-LDS tiles: BM, BN, BK, waves (M x N), LDS stages
 namespace mi355 {
-using D256 = DTile<256, 256, 64, 2, 2, 2>;       // 4 waves of 128x128, 128 KiB LDS
-using D256x128 = DTile<256, 128, 64, 2, 2, 3>;   // 4 waves of 128x64, 144 KiB
-using D128x256 = DTile<128, 256, 64, 2, 2, 3>;   // 4 waves of 64x128, 144 KiB
-using D128 = DTile<128, 128, 64, 2, 2, 4>;       // 4 waves of 64x64, 128 KiB
-using D128k32 = DTile<128, 128, 32, 2, 2, 4>;    // 4 waves of 64x64, 64 KiB
+// direct-to-LDS tiles: BM, BN, BK, waves (M x N), k-groups, LDS stages
+using D256 = DTile<256, 256, 32, 2, 4, 1, 4>;       // 8 waves of 128x64, 128 KiB LDS
+using D256k64 = DTile<256, 256, 64, 2, 4, 1, 2>;    // 8 waves of 128x64, 128 KiB
+using D256x128 = DTile<256, 128, 64, 2, 2, 2, 3>;   // 2 x 4 waves of 128x64, 144 KiB
+using D128 = DTile<128, 128, 64, 2, 2, 2, 4>;       // 2 x 4 waves of 64x64, 128 KiB
+using D128w4 = DTile<128, 128, 64, 2, 2, 1, 4>;     // 4 waves of 64x64, 128 KiB
 // register-staged tiles (any alignment)
 using T64 = Tile<64, 64, 64, 2, 1>;              // 2 waves of 32x64
 using T128 = Tile<128, 128, 64, 2, 2>;           // 4 waves of 64x64
@@ -31,10 +31,10 @@ using T256 = Tile<256, 256, 64, 2, 2>;           // 4 waves of 128x128
     template __global__ void gemm_direct<T, 1>(GemmArgs); \
     template __global__ void gemm_direct<T, 2>(GemmArgs);
 MI355_DIRECT(D256)
+MI355_DIRECT(D256k64)
 MI355_DIRECT(D256x128)
-MI355_DIRECT(D128x256)
 MI355_DIRECT(D128)
-MI355_DIRECT(D128k32)
+MI355_DIRECT(D128w4)
 #undef MI355_DIRECT
 }  // namespace mi355
 
@@ -58,7 +58,7 @@ typedef void (*KernelFn)(GemmArgs);
 struct Config {
     const char *name;
     bool direct;      // direct-to-LDS kernel (16-byte operands) or register-staged kernel
-    int bm, bn, bk, stages, waves_m, waves_n, threads, lds_bytes;
+    int bm, bn, bk, stages, waves_m, waves_n, k_groups, threads, lds_bytes;
     bool a_vec, bc_vec;
     int group_m;
     KernelFn fn[3];   // per epilogue
@@ -67,7 +67,7 @@ struct Config {
 template <class T, bool AV, bool BV>
 Config staged_config(const char *name, int group_m)
 {
-    return Config{name, false, T::BM, T::BN, T::BK, T::STAGES, T::WAVES_M, T::WAVES_N, T::NT,
+    return Config{name, false, T::BM, T::BN, T::BK, T::STAGES, T::WAVES_M, T::WAVES_N, 1, T::NT,
                   T::LDS_BYTES, AV, BV, group_m,
                   {gemm_staged<T, AV, BV, 0>, gemm_staged<T, AV, BV, 1>, gemm_staged<T, AV, BV, 2>}};
 }
@@ -75,17 +75,18 @@ Config staged_config(const char *name, int group_m)
 template <class T>
 Config direct_config(const char *name, int group_m)
 {
-    return Config{name, true, T::BM, T::BN, T::BK, T::STAGES, T::WAVES_M, T::WAVES_N, T::NT,
+    return Config{name, true, T::BM, T::BN, T::BK, T::STAGES, T::WAVES_M, T::WAVES_N, T::KGROUPS,
+                  T::NT,
                   T::LDS_BYTES, true, true, group_m,
                   {gemm_direct<T, 0>, gemm_direct<T, 1>, gemm_direct<T, 2>}};
 }
 
 const Config kConfigs[] = {
-    direct_config<D256>("d256x256x64_w2x2_s2", 8),
-    direct_config<D256x128>("d256x128x64_w2x2_s3", 8),
-    direct_config<D128x256>("d128x256x64_w2x2_s3", 8),
-    direct_config<D128>("d128x128x64_w2x2_s4", 8),
-    direct_config<D128k32>("d128x128x32_w2x2_s4", 8),
+    direct_config<D256>("d256x256x32_w2x4_s4", 8),
+    direct_config<D256k64>("d256x256x64_w2x4_s2", 8),
+    direct_config<D256x128>("d256x128x64_w2x2k2_s3", 8),
+    direct_config<D128>("d128x128x64_w2x2k2_s4", 8),
+    direct_config<D128w4>("d128x128x64_w2x2_s4", 8),
     staged_config<T256, true, true>("s256x256x64_w2x2_av_bv", 8),
     staged_config<T128, true, true>("s128x128x64_w2x2_av_bv", 8),
     staged_config<T128, true, false>("s128x128x64_w2x2_av_bn", 8),
@@ -169,9 +170,9 @@ int choose(const Request &r)
     const bool av = a_vector_ok(r), bv = bc_vector_ok(r);
     constexpr int64_t kCUs = 256;
     if (av && bv) {
-        if (tiles(r, 256, 256) >= 2 * kCUs) return find_config(true, 256, 256, true, true);
-        if (tiles(r, 256, 128) >= 2 * kCUs) return find_config(true, 256, 128, true, true);
-        if (tiles(r, 128, 128) >= kCUs / 2) return find_config(true, 128, 128, true, true);
+        if (tiles(r, 256, 256) >= 2 * kCUs) return 0;
+        if (tiles(r, 256, 128) >= 2 * kCUs) return 2;
+        if (tiles(r, 128, 128) >= kCUs / 2) return 3;
     }
     if (tiles(r, 128, 128) >= kCUs / 2) return find_config(false, 128, 128, av, bv);
     return find_config(false, 64, 64, av, bv);
@@ -285,6 +286,7 @@ mi355gemm_status mi355gemm_config_info(int config_id, mi355gemm_config_desc *out
     out->stages = c.stages;
     out->waves_m = c.waves_m;
     out->waves_n = c.waves_n;
+    out->k_groups = c.k_groups;
     out->threads = c.threads;
     out->lds_bytes = c.lds_bytes;
     out->a_vector = c.a_vec;

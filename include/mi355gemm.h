@@ -99,8 +99,9 @@ int mi355gemm_select(int64_t M, int64_t N, int64_t K, int epi,
 typedef struct {
     int block_m, block_n, block_k;  /* macro-tile of C per workgroup and K step */
     int stages;                     /* LDS buffers in the K pipeline */
-    int waves_m, waves_n;           /* wavefront grid inside a workgroup */
-    int threads;                    /* threads per workgroup (64 per wavefront) */
+    int waves_m, waves_n;           /* wavefront grid over the macro-tile */
+    int k_groups;                   /* wave grids splitting each K step (summed at the end) */
+    int threads;                    /* threads per workgroup: 64 * waves_m * waves_n * k_groups */
     int lds_bytes;                  /* LDS the configuration occupies per workgroup */
     int a_vector;                   /* 1: A loaded in 16-byte vectors (needs K % 8 == 0) */
     int bc_vector;                  /* 1: B loaded and C stored in vectors (N % 8 == 0) */

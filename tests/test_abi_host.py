@@ -61,7 +61,8 @@ def test_config_table_is_consistent():
             # two LDS stages of BM and BN rows of BK halves plus a 16-byte pad per row
             assert c["lds_bytes"] == c["stages"] * (c["block_m"] + c["block_n"]) * (c["block_k"] + 8) * 2
         assert c["lds_bytes"] <= g.mi355gemm_lds_budget()
-        assert c["threads"] == 64 * c["waves_m"] * c["waves_n"]
+        assert c["threads"] == 64 * c["waves_m"] * c["waves_n"] * c["k_groups"]
+        assert c["k_groups"] in (1, 2) and (c["direct"] or c["k_groups"] == 1)
         assert c["block_m"] % (32 * c["waves_m"]) == 0 and c["block_n"] % (32 * c["waves_n"]) == 0
         assert c["block_k"] % 16 == 0
     assert g.mi355gemm_config_name(-1) is None
