@@ -74,12 +74,27 @@ __device__ __forceinline__ void tile_coords(int bid, int tiles_m, int tiles_n, i
 }
 
 // ---------------------------------------------------------------- epilogue ----------
-// GELU(x) = x * Phi(x), Phi(x) = 1 - erfc(x/sqrt2)/2 for x >= 0 and erfc(|x|/sqrt2)/2
-// for x < 0; one erfc evaluation, no cancellation on the negative side.
+// GELU(x) = x * Phi(x) with Phi the standard normal CDF:
+//   Phi(x) = 1 - erfc(z)/2 for x >= 0 and erfc(z)/2 for x < 0, z = |x| / sqrt 2,
+// one erfc evaluation and no cancellation on the negative side.  erfc(z) for z >= 0 uses
+// the rational approximation of Abramowitz and Stegun, Handbook of Mathematical Functions,
+// formula 7.1.26 (after Hastings): erfc(z) = t (a1 + t (a2 + t (a3 + t (a4 + t a5))))
+// exp(-z^2) with t = 1 / (1 + p z), absolute error at most 1.5e-7.  The polynomial
+// approximates erfc(z) exp(z^2), so the relative error stays of that order in the
+// tail as well, far below the 2^-11 relative step of the fp16 result.  exp and the
+// reciprocal are the hardware v_exp_f32 / v_rcp_f32.
 __device__ __forceinline__ float gelu_erf(float x)
 {
-    const float q = erfcf(fabsf(x) * 0.70710678118654752f);
-    const float phi = (x >= 0.0f) ? 1.0f - 0.5f * q : 0.5f * q;
+    constexpr float p = 0.3275911f;
+    constexpr float a1 = 0.254829592f, a2 = -0.284496736f, a3 = 1.421413741f,
+                    a4 = -1.453152027f, a5 = 1.061405429f;
+    constexpr float kRsqrt2 = 0.70710678118654752f;
+    constexpr float kHalfLog2e = 0.72134752044448170f;   // log2(e) / 2: exp(-z^2) = 2^(-x^2 log2(e) / 2)
+    const float z = fabsf(x) * kRsqrt2;
+    const float t = __builtin_amdgcn_rcpf(fmaf(p, z, 1.0f));
+    const float poly = t * fmaf(t, fmaf(t, fmaf(t, fmaf(t, a5, a4), a3), a2), a1);
+    const float q = poly * __builtin_amdgcn_exp2f(-(x * x) * kHalfLog2e);   // erfc(z)
+    const float phi = (x >= 0.0f) ? fmaf(-0.5f, q, 1.0f) : 0.5f * q;
     return x * phi;
 }
 

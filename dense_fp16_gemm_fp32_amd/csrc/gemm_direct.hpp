@@ -19,7 +19,8 @@
 //                     extra LDS traffic.  The instruction order inside a k-step is fixed in
 //                     the source: after each MFMA come the LDS reads for the next k-step and
 //                     a share of the HBM -> LDS copies, fenced with sched_barrier;
-//   4. epilogue    -- store_tile(): bias, erf-GELU, fp16 rounding, masked stores.
+//   4. epilogue    -- bias, erf-GELU and fp16 rounding in registers, the tile staged in
+//                     LDS, then whole-row 16-byte stores (tile_to_lds, lds_to_c).
 //
 // Out-of-range rows, columns and the K tail read as zero through the buffer descriptors'
 // range checks (rows past M / K) or an offset pushed out of range (columns past N, K
@@ -69,6 +70,7 @@ struct DTile {
     static_assert(STAGES >= 2 && STAGES <= 5 && G * (STAGES - 2) <= 63, "ring size / vmcnt range");
     static_assert(LDS_BYTES <= 160 * 1024, "over the gfx950 LDS budget");
     static_assert(RED_BYTES <= LDS_BYTES, "k-group exchange must fit in the ring");
+    static_assert(BM * BN * 2 <= LDS_BYTES, "the C tile is staged in the ring");
 };
 
 template <class T>
@@ -282,6 +284,82 @@ struct DirectWave {
     }
 };
 
+
+// ---------------------------------------------------------------- epilogue ----------
+// The C tile is staged in LDS (the ring is free once the K loop is done) so that the
+// stores to HBM are whole rows: 16 bytes per lane, consecutive lanes on consecutive
+// columns, every 128-byte line written by one instruction.  LDS layout: row-major
+// BM x BN fp16, 16-byte chunk c of row r stored at chunk c ^ (r % CW) (CW = chunks per
+// row), so the column-wise writes from the accumulator layout spread over the banks.
+template <class T>
+__device__ __forceinline__ int c_chunk_swz(int r)
+{
+    return r % (T::BN / 8);
+}
+
+// Bias, GELU and fp16 rounding of accumulator block rows I0 <= i < I1 of this wave,
+// written into the LDS copy of the tile.  Accumulator layout of v_mfma_f32_32x32x16_f16
+// with the B fragment as the first operand: register r of lane l holds
+// C[32 i + l % 32][32 j + 8 (r / 4) + 4 (l / 32) + r % 4] of the wave's sub-tile.
+template <class T, int I0, int I1, int EPI>
+__device__ __forceinline__ void tile_to_lds(const f32x16 (&acc)[T::FM][T::FN], const GemmArgs &p,
+                                            int n0, int row0, int col0, int lane, char *ctile)
+{
+    const __amdgpu_buffer_rsrc_t b_rs =
+        make_rsrc(EPI != 0 ? p.bias + n0 : p.C, EPI != 0 ? (uint32_t)(p.N - n0) * 2u : 0u);
+    const int half = lane >> 5;
+#pragma unroll
+    for (int j = 0; j < T::FN; ++j) {
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+            const int n = col0 + j * 32 + 8 * g + 4 * half;   // first of 4 columns, tile-relative
+            float bv[4] = {0.f, 0.f, 0.f, 0.f};
+            if constexpr (EPI != 0) {
+                const u32x2 raw = __builtin_amdgcn_raw_buffer_load_b64(b_rs, (uint32_t)n * 2u, 0, 0);
+                const f16x4 h = __builtin_bit_cast(f16x4, raw);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) bv[e] = (float)h[e];
+            }
+            const int c = n >> 3;
+#pragma unroll
+            for (int i = I0; i < I1; ++i) {
+                const int r = row0 + i * 32 + (lane & 31);
+                uint32_t hb[4];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const f16 h = (f16)epilogue_op<EPI>(acc[i][j][4 * g + e], bv[e]);
+                    hb[e] = __builtin_bit_cast(uint16_t, h);
+                }
+                char *dst = ctile + (r * T::BN + 8 * (c ^ c_chunk_swz<T>(r)) + 4 * half) * 2;
+                *reinterpret_cast<u32x2 *>(dst) = u32x2{hb[0] | (hb[1] << 16), hb[2] | (hb[3] << 16)};
+            }
+        }
+    }
+}
+
+// All threads: copy the LDS tile to C, 16 bytes per lane.  Rows past M fall outside the
+// C descriptor's range, 8-column chunks past N are pushed out of range (N % 8 == 0 here,
+// so a chunk is either wholly inside or wholly outside).
+template <class T>
+__device__ __forceinline__ void lds_to_c(const GemmArgs &p, int m0, int n0, int rows_valid,
+                                         const char *ctile)
+{
+    constexpr int CW = T::BN / 8;
+    constexpr int PER = T::BM * CW / T::NT;
+    static_assert(T::BM * CW % T::NT == 0, "tile must split evenly over the threads");
+    const int cols_valid = p.N - n0;
+    const __amdgpu_buffer_rsrc_t c_rs =
+        make_rsrc(p.C + (int64_t)m0 * p.N + n0, (uint32_t)(rows_valid * p.N - n0) * 2u);
+#pragma unroll
+    for (int k = 0; k < PER; ++k) {
+        const int q = threadIdx.x + k * T::NT;
+        const int r = q / CW, c = q % CW;
+        const u32x4 v = *reinterpret_cast<const u32x4 *>(ctile + (r * T::BN + 8 * (c ^ c_chunk_swz<T>(r))) * 2);
+        const uint32_t off = masked_offset((uint32_t)(r * p.N + 8 * c) * 2u, 8 * c < cols_valid);
+        __builtin_amdgcn_raw_buffer_store_b128(v, c_rs, off, 0, 0);
+    }
+}
+
 template <int... Is, class F>
 __device__ __forceinline__ void static_for(std::integer_sequence<int, Is...>, F &&f)
 {
@@ -379,16 +457,17 @@ __global__ void __launch_bounds__(T::NT) gemm_direct(GemmArgs p)
         wait_counts<0, 0>();
     }
 
+    // every wave is done reading the ring (and, above, its copies have all landed)
+    workgroup_barrier();
+    char *ctile = lds_raw;
     if constexpr (T::KGROUPS == 1) {
-        store_tile<T::FM, T::FN, 0, T::FM, true, EPI>(w.acc, p, m0, n0, rows_valid,
-                                                     w.wm * T::WTM, w.wn * T::WTN, w.lane);
+        tile_to_lds<T, 0, T::FM, EPI>(w.acc, p, n0, w.wm * T::WTM, w.wn * T::WTN, w.lane, ctile);
     } else {
         // Sum the two k-groups' partial tiles.  Group 0 keeps blocks i < FM/2 and hands
-        // blocks i >= FM/2 to group 1; group 1 does the opposite; each then stores the half
-        // it kept.  Each 32x32 fp32 block moves as four 1 KiB ds_write_b128 / ds_read_b128
-        // (lane-contiguous, conflict-free).
+        // blocks i >= FM/2 to group 1; group 1 does the opposite; each then finishes the
+        // half it kept.  Each 32x32 fp32 block moves as four 1 KiB ds_write_b128 /
+        // ds_read_b128 (lane-contiguous, conflict-free).
         constexpr int H = T::FM / 2;
-        workgroup_barrier();   // every wave is done reading the ring
         float *red = reinterpret_cast<float *>(lds_raw);
         const int wc = w.wave % T::NWC;
         // slot of (group, wave-in-group, block) in the exchange area; the receiving wave of
@@ -419,14 +498,17 @@ __global__ void __launch_bounds__(T::NT) gemm_direct(GemmArgs p)
 #pragma unroll
                         for (int e = 0; e < 4; ++e) w.acc[KEEP + ii][j][4 * c + e] += o[e];
                     }
-            store_tile<T::FM, T::FN, KEEP, KEEP + H, true, EPI>(w.acc, p, m0, n0, rows_valid,
-                                                               w.wm * T::WTM, w.wn * T::WTN, w.lane);
+            __syncthreads();   // the exchange area is overwritten by the C tile below
+            tile_to_lds<T, KEEP, KEEP + H, EPI>(w.acc, p, n0, w.wm * T::WTM, w.wn * T::WTN,
+                                                w.lane, ctile);
         };
         if (w.kg == 0)
             exchange(std::integral_constant<int, H>{}, std::integral_constant<int, 0>{});
         else
             exchange(std::integral_constant<int, 0>{}, std::integral_constant<int, H>{});
     }
+    __syncthreads();
+    lds_to_c<T>(p, m0, n0, rows_valid, ctile);
 }
 
 }  // namespace mi355

@@ -151,31 +151,41 @@ int64_t tiles(const Request &r, int bm, int bn)
     return ((r.M + bm - 1) / bm) * ((r.N + bn - 1) / bn);
 }
 
-int find_config(bool direct, int bm, int bn, bool av, bool bv)
+int find_staged(int bm, int bn, bool av, bool bv)
 {
     for (int i = 0; i < kNumConfigs; ++i) {
         const Config &c = kConfigs[i];
-        if (c.direct == direct && c.bm == bm && c.bn == bn && c.a_vec == av && c.bc_vec == bv)
+        if (!c.direct && c.bm == bm && c.bn == bn && c.a_vec == av && c.bc_vec == bv) return i;
+    }
+    return -1;
+}
+
+int find_direct(int bm, int bn, int bk, int waves, int k_groups)
+{
+    for (int i = 0; i < kNumConfigs; ++i) {
+        const Config &c = kConfigs[i];
+        if (c.direct && c.bm == bm && c.bn == bn && c.bk == bk &&
+            c.waves_m * c.waves_n * c.k_groups == waves && c.k_groups == k_groups)
             return i;
     }
     return -1;
 }
 
-// Shape-keyed choice (host only).  Larger tiles need fewer bytes per flop from L2/LDS,
-// but a launch must still cover the 256 compute units: take the largest tile that keeps
-// at least one full wave of workgroups, and fall back to 128x128 / 64x64 for small or
-// unaligned problems (the wide tiles only exist with 16-byte loads).
+// Shape-keyed choice (host only), from timings on MI355X.  A launch should cover the 256
+// compute units; among the tiles that do, the largest wins (fewer bytes per flop from L2
+// into LDS).  256x256 tiles need a full wave of workgroups (M and N >= 4096 or so);
+// 128x128 direct tiles serve mid-size problems; the register-staged kernels take
+// unaligned or small problems (the direct kernels need 16-byte rows and operands).
 int choose(const Request &r)
 {
     const bool av = a_vector_ok(r), bv = bc_vector_ok(r);
     constexpr int64_t kCUs = 256;
     if (av && bv) {
-        if (tiles(r, 256, 256) >= 2 * kCUs) return 0;
-        if (tiles(r, 256, 128) >= 2 * kCUs) return 2;
-        if (tiles(r, 128, 128) >= kCUs / 2) return 3;
+        if (tiles(r, 256, 256) >= kCUs) return find_direct(256, 256, 64, 8, 1);
+        if (tiles(r, 128, 128) >= kCUs / 2) return find_direct(128, 128, 64, 4, 1);
     }
-    if (tiles(r, 128, 128) >= kCUs / 2) return find_config(false, 128, 128, av, bv);
-    return find_config(false, 64, 64, av, bv);
+    if (tiles(r, 128, 128) >= kCUs / 2) return find_staged(128, 128, av, bv);
+    return find_staged(64, 64, av, bv);
 }
 
 // Can configuration c serve request r?

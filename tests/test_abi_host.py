@@ -144,6 +144,8 @@ def test_select_for_the_workload_shapes():
     # large square problems take the widest tile; 2048^3 must still fill 256 CUs
     big = _cfg(_select(8192, 8192, 8192))
     assert (big["block_m"], big["block_n"]) == (256, 256)
+    four = _cfg(_select(4096, 4096, 4096))          # 256 tiles of 256x256: one per CU
+    assert (four["block_m"], four["block_n"]) == (256, 256)
     mid = _cfg(_select(2048, 2048, 2048))
     tiles = (2048 // mid["block_m"]) * (2048 // mid["block_n"])
     assert tiles >= 256

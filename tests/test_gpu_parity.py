@@ -254,3 +254,37 @@ def test_rejects_bad_tensors():
         g.gemm(A, torch.zeros((15, 8), dtype=torch.float16, device=DEV))
     with pytest.raises(g.GemmError):
         g.gemm(A, B, None, "bias_gelu")
+
+
+# ---- the fused GELU over every finite fp16 input -------------------------------------
+
+def _ordered(bits: np.ndarray) -> np.ndarray:
+    """fp16 bit patterns -> integers in the same order as the values (+0 and -0 equal)."""
+    b = bits.astype(np.int32)
+    return np.where(b & 0x8000, -(b & 0x7FFF), b)
+
+
+def test_gelu_epilogue_every_finite_fp16_input():
+    """With A = 0 the kernel's output is C[i, j] = fp16(GELU(bias[j])), so putting every
+    finite fp16 value in the bias runs the register epilogue's erf-GELU once on each.  The
+    result must be within one fp16 step of the oracle's correctly rounded value
+    everywhere and equal to it for almost all inputs (the kernel evaluates GELU in fp32)."""
+    all_bits = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    finite = all_bits[(all_bits & 0x7C00) != 0x7C00]
+    N = finite.size                      # 63488, a multiple of 8
+    M, K = 8, 16
+    bias = torch.from_numpy(finite.view(np.float16).copy())
+    A = torch.zeros((M, K), dtype=torch.float16)
+    _, B, _ = workloads.make_inputs(M, N, K, "normal", seed=5)
+    ref = oracle.gemm(A, B, bias, "bias_gelu")
+    assert np.array_equal(ref[0], ref[M - 1])
+    for cfg in all_configs():
+        if not _compatible(cfg, M, N, K):
+            continue
+        print("gelu sweep", cfg["name"], flush=True)
+        C = _run(A, B, bias, "bias_gelu", config=cfg["id"])
+        got = C.cpu().contiguous().view(torch.int16).numpy().view(np.uint16)
+        d = np.abs(_ordered(got) - _ordered(ref))
+        assert d.max() <= 1, "%s: GELU off by %d fp16 steps at bias %r" % (
+            cfg["name"], d.max(), float(bias[int(np.argmax(d.max(axis=0)))]))
+        assert (d == 0).mean() >= 0.99, "%s: only %.4f exact" % (cfg["name"], (d == 0).mean())
