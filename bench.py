@@ -9,7 +9,10 @@ the epilogue, 256^3), the roofline of the kernel and the CPU oracle timed on thi
 TFLOP/s counts 2*M*N*K per GEMM, as the tutorial does (thecryptopost.io page, section 2:
 flops = 2 * M * N * K); the epilogue's arithmetic is not counted.  Latency is measured
 with device events on the stream the kernels run on, as the tutorial's bench() measures
-with CUDA events (aitrending.vip page, "Benchmarking & Verification").
+with CUDA events (aitrending.vip page, "Benchmarking & Verification").  The step time
+(`value`, `ms_per_step`) is wall clock between synchronisations around back-to-back calls,
+launch gaps included; the roofline uses the kernel's own mean duration from an event pair
+around each launch.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
                        [--no-cpu-baseline] [--no-extra] [--config NAME]
@@ -32,10 +35,29 @@ METRIC = ("TFLOP/s and % of MI355X fp16 MFMA peak, fp16 GEMM 2048³ & 8192³ "
           "(+bias+GELU)")
 HEADLINE = "gemm_2048"
 
-# rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE per dispatch of the headline kernel, KiB, and
-# the copy-kernel calibration factor; filled from the committed profiles (None until the
-# counters are taken on the current kernel).
-TRAFFIC_BYTES = None
+# HBM bytes per dispatch of the headline kernel: rocprofv3 --pmc FETCH_SIZE + WRITE_SIZE,
+# each scaled by what the same counter reads for a plain copy of known size (the
+# --calibrate-copy run).  Reported only while the kernel sources hash to the version the
+# counters were taken on (profiles/ holds the summary); otherwise null.
+TRAFFIC = {"kernel_config": "d128x128x64_w2x2_s4", "sources_sha256_16": "243302a746d617d8",
+           "bytes": 58873258}
+
+
+def kernel_sources_hash() -> str:
+    import glob
+    import hashlib
+    h = hashlib.sha256()
+    for f in sorted(glob.glob(os.path.join(ROOT, "dense_fp16_gemm_fp32_amd", "csrc", "*"))):
+        with open(f, "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def traffic_for(kernel_config: str):
+    if (TRAFFIC and TRAFFIC["kernel_config"] == kernel_config
+            and TRAFFIC["sources_sha256_16"] == kernel_sources_hash()):
+        return TRAFFIC["bytes"]
+    return None
 
 
 def parse():
@@ -49,17 +71,24 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extra", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="also run a 256 MiB device copy (counter calibration for rocprofv3)")
     return ap.parse_args()
 
 
 def time_gemm(lib, A, B, bias, epi, out, steps, warmup, config=None):
-    """Average device time per call (ms) over `steps` back-to-back calls, bracketed by
-    synchronisations, measured with events on the launch stream."""
+    """Two timed passes of `steps` calls each, after `warmup` untimed calls.
+
+    Pass 1 (the step time): wall clock between synchronisations around the back-to-back
+    calls, and device events at both ends of the same region on the launch stream.
+    Pass 2 (the kernel time): an event pair around every single launch on the launch
+    stream; the mean pair time is the kernel's average duration, which the roofline uses.
+    Returns (ms per step by wall clock, ms per step by events, mean ms per launch)."""
     import torch
+    stream = torch.cuda.current_stream()
     for _ in range(warmup):
         lib.gemm(A, B, bias, epi, out=out, config=config)
     torch.cuda.synchronize()
-    stream = torch.cuda.current_stream()
     start = torch.cuda.Event(enable_timing=True)
     stop = torch.cuda.Event(enable_timing=True)
     t0 = time.perf_counter()
@@ -68,8 +97,19 @@ def time_gemm(lib, A, B, bias, epi, out, steps, warmup, config=None):
         lib.gemm(A, B, bias, epi, out=out, config=config)
     stop.record(stream)
     torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    return start.elapsed_time(stop) / steps, wall
+    wall_ms = (time.perf_counter() - t0) * 1e3 / steps
+    event_ms = start.elapsed_time(stop) / steps
+
+    pairs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+             for _ in range(steps)]
+    torch.cuda.synchronize()
+    for a, b in pairs:
+        a.record(stream)
+        lib.gemm(A, B, bias, epi, out=out, config=config)
+        b.record(stream)
+    torch.cuda.synchronize()
+    kernel_ms = sum(a.elapsed_time(b) for a, b in pairs) / steps
+    return wall_ms, event_ms, kernel_ms
 
 
 def run_workload(lib, w, epi, steps, warmup, config=None):
@@ -81,16 +121,32 @@ def run_workload(lib, w, epi, steps, warmup, config=None):
     bias = bias.to(dev) if bias is not None else None
     out = torch.empty((w.M, w.N), dtype=torch.float16, device=dev)
     cid = lib.select(A, B, bias, epi, out=out) if config is None else lib.config_id(config)
-    ms, wall = time_gemm(lib, A, B, bias, epi, out, steps, warmup, config)
-    tflops = w.flops / (ms * 1e-3) / 1e12
-    gbs = w.algorithmic_bytes(epi) / (ms * 1e-3) / 1e9
+    wall_ms, event_ms, kernel_ms = time_gemm(lib, A, B, bias, epi, out, steps, warmup, config)
+    tflops = w.flops / (wall_ms * 1e-3) / 1e12
     return {
         "workload": w.name, "M": w.M, "N": w.N, "K": w.K, "epilogue": epi,
         "kernel_config": lib.mi355gemm_config_name(cid),
-        "ms": ms, "us": ms * 1e3, "tflops": tflops,
+        "ms": wall_ms, "us": wall_ms * 1e3, "tflops": tflops,
         "pct_of_peak": 100.0 * tflops / PEAK_FP16_TFLOPS,
-        "algorithmic_GBps": gbs, "steps": steps, "wall_s": wall,
+        "event_us": event_ms * 1e3,
+        "kernel_us": kernel_ms * 1e3,
+        "kernel_tflops": w.flops / (kernel_ms * 1e-3) / 1e12,
+        "algorithmic_GBps": w.algorithmic_bytes(epi) / (kernel_ms * 1e-3) / 1e9,
+        "steps": steps,
     }
+
+
+def calibrate_copy(reps=5, mib=256):
+    """A plain device-to-device copy of known size (mib MiB read, mib MiB written), for
+    scaling rocprofv3's FETCH_SIZE / WRITE_SIZE counters."""
+    import torch
+    n = mib * (1 << 20) // 2
+    src = torch.ones(n, dtype=torch.float16, device="cuda:0")
+    dst = torch.empty_like(src)
+    for _ in range(reps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print("bench: calibration copy of %d MiB x %d done" % (mib, reps), file=sys.stderr, flush=True)
 
 
 def cpu_baseline(w, epi, seconds):
@@ -130,8 +186,11 @@ def main():
     print("bench: %s epilogue=%s steps=%d warmup=%d" % (w.name, epi, args.steps, args.warmup),
           file=sys.stderr, flush=True)
     head = run_workload(lib, w, epi, args.steps, args.warmup, args.config)
-    print("bench: headline %.2f us  %.1f TFLOP/s" % (head["us"], head["tflops"]),
+    print("bench: headline %.2f us/step (events %.2f us), kernel %.2f us, %.1f TFLOP/s"
+          % (head["us"], head["event_us"], head["kernel_us"], head["tflops"]),
           file=sys.stderr, flush=True)
+    if args.calibrate_copy:
+        calibrate_copy()
 
     extra = []
     if not args.no_extra:
@@ -141,7 +200,8 @@ def main():
                     continue
                 steps = 50 if ew.M >= 8192 else 300
                 r = run_workload(lib, ew, e, steps, 10)
-                print("bench: %s %s %.2f us %.1f TFLOP/s" % (ew.name, e, r["us"], r["tflops"]),
+                print("bench: %s %s %.2f us/step, kernel %.2f us, %.1f TFLOP/s"
+                      % (ew.name, e, r["us"], r["kernel_us"], r["tflops"]),
                       file=sys.stderr, flush=True)
                 extra.append(r)
 
@@ -167,9 +227,14 @@ def main():
                    "inputs": "%s seed %d" % (w.dist, w.seed),
                    "kernel_config": head["kernel_config"]},
         "pct_of_peak": head["pct_of_peak"],
-        "roofline": {"bound": "mfma", "achieved": head["tflops"], "peak": PEAK_FP16_TFLOPS,
-                     "unit": "TFLOP/s", "frac": head["tflops"] / PEAK_FP16_TFLOPS,
-                     "traffic": TRAFFIC_BYTES},
+        "event_ms_per_step": head["event_us"] * 1e-3,
+        "kernel_us": head["kernel_us"],
+        # the dominant (only) kernel: 2*M*N*K flops per launch over its mean duration from
+        # per-launch event pairs on the launch stream
+        "roofline": {"bound": "mfma", "achieved": head["kernel_tflops"],
+                     "peak": PEAK_FP16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": head["kernel_tflops"] / PEAK_FP16_TFLOPS,
+                     "traffic": traffic_for(head["kernel_config"])},
         "cpu_baseline": cpu,
         "device": {"name": props.name, "arch": getattr(props, "gcnArchName", None),
                    "cus": props.multi_processor_count},
