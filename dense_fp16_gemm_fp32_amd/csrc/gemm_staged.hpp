@@ -3,9 +3,11 @@
 //
 // One workgroup computes one BM x BN macro-tile of C:
 //   1. tile order  -- tile_coords();
-//   2. loader      -- buffer loads HBM -> VGPR (16-byte vectors where the layout allows,
-//                     2-byte loads otherwise; out-of-range lanes read 0 through the buffer
-//                     descriptor's range check), then VGPR -> LDS into a 2-stage padded
+//   2. loader      -- buffer loads HBM -> VGPR (16-byte vectors; for A also at 2-byte
+//                     alignment, with 2-byte loads only in the stage holding the K tail; for
+//                     B 2-byte loads when its rows are not 16-byte aligned; out-of-range
+//                     lanes read 0 through the buffer descriptor's range check), then
+//                     VGPR -> LDS into a 2-stage padded
 //                     ring; B is transposed 4x8 in registers on the way so both LDS tiles
 //                     are k-contiguous, as the MFMA operands want;
 //   3. MFMA loop   -- each wavefront owns a WTM x WTN sub-tile of 32x32 blocks and chains
@@ -43,8 +45,25 @@ struct ALoader {
     u32x4 r[PER];
 
     // rs covers rows [m0, m0 + rows_valid) of A from column 0; rows past it read 0.
+    // VEC: K % 8 == 0 and A 16-byte aligned, every 8-half chunk is one aligned 16-byte
+    // load.  Otherwise rows are only 2-byte aligned: a chunk that lies wholly inside its
+    // row is still one 16-byte load (gfx9 buffer loads need no alignment beyond the
+    // element size here; the compiler emits the same for unaligned vector loads), and only
+    // the stage holding the K tail, whose last chunk of a row may reach past the row (and
+    // past the end of A), falls back to one 2-byte load per element.
     __device__ __forceinline__ void load(__amdgpu_buffer_rsrc_t rs, int k0, int K, int tid)
     {
+        if constexpr (!VEC) {
+            if (k0 + T::BK <= K) {
+#pragma unroll
+                for (int i = 0; i < PER; ++i) {
+                    const int v = tid + i * T::NT;
+                    const int row = v / VPR, k = k0 + 8 * (v % VPR);
+                    r[i] = __builtin_amdgcn_raw_buffer_load_b128(rs, (uint32_t)(row * K + k) * 2u, 0, 0);
+                }
+                return;
+            }
+        }
 #pragma unroll
         for (int i = 0; i < PER; ++i) {
             const int v = tid + i * T::NT;
