@@ -137,11 +137,14 @@ def configs() -> list[dict]:
     return out
 
 
+_config_ids: dict | None = None
+
+
 def config_id(name: str) -> int:
-    for i in range(mi355gemm_num_configs()):
-        if mi355gemm_config_name(i) == name:
-            return i
-    raise KeyError(name)
+    global _config_ids
+    if _config_ids is None:
+        _config_ids = {mi355gemm_config_name(i): i for i in range(mi355gemm_num_configs())}
+    return _config_ids[name]
 
 
 def _check_tensor(t, name, ndim):
@@ -163,39 +166,54 @@ def _epi(epilogue) -> int:
     return int(epilogue)
 
 
+try:   # the raw handle of the current stream without building a Stream object
+    _raw_stream = torch._C._cuda_getCurrentRawStream
+except AttributeError:  # pragma: no cover - older torch
+    def _raw_stream(index):
+        return torch.cuda.current_stream(index).cuda_stream
+
+
 def gemm(a: torch.Tensor, b: torch.Tensor, bias: torch.Tensor | None = None,
          epilogue="none", out: torch.Tensor | None = None, config: int | str | None = None,
          stream: torch.cuda.Stream | None = None) -> torch.Tensor:
-    """``out = epilogue(a @ b [+ bias])`` on the GPU; a (M,K), b (K,N), bias (N,), fp16."""
+    """``out = epilogue(a @ b [+ bias])`` on the GPU; a (M,K), b (K,N), bias (N,), fp16.
+
+    Runs on `stream` (default: the current stream of a's device) and returns without
+    synchronising, like any other torch GPU op."""
     _check_tensor(a, "a", 2)
     _check_tensor(b, "b", 2)
     M, K = a.shape
     if b.shape[0] != K:
         raise ValueError("inner dimensions differ: a %s, b %s" % (tuple(a.shape), tuple(b.shape)))
     N = b.shape[1]
-    if b.device != a.device:
+    dev = a.device
+    if b.device != dev:
         raise ValueError("a and b are on different devices")
     epi = _epi(epilogue)
+    bptr = None
     if bias is not None:
         _check_tensor(bias, "bias", 1)
-        if bias.shape[0] != N or bias.device != a.device:
-            raise ValueError("bias must have N=%d elements on %s" % (N, a.device))
+        if bias.shape[0] != N or bias.device != dev:
+            raise ValueError("bias must have N=%d elements on %s" % (N, dev))
+        bptr = bias.data_ptr()
     if out is None:
-        out = torch.empty((M, N), dtype=torch.float16, device=a.device)
+        out = torch.empty((M, N), dtype=torch.float16, device=dev)
     else:
         _check_tensor(out, "out", 2)
-        if tuple(out.shape) != (M, N) or out.device != a.device:
-            raise ValueError("out must be (%d, %d) on %s" % (M, N, a.device))
-    s = stream if stream is not None else torch.cuda.current_stream(a.device)
-    bptr = bias.data_ptr() if bias is not None else None
-    with torch.cuda.device(a.device):
-        if config is None:
-            st = mi355gemm_gemm(M, N, K, a.data_ptr(), b.data_ptr(), out.data_ptr(), bptr, epi,
-                                s.cuda_stream)
-        else:
-            cid = config_id(config) if isinstance(config, str) else int(config)
-            st = mi355gemm_gemm_config(M, N, K, a.data_ptr(), b.data_ptr(), out.data_ptr(), bptr,
-                                       epi, s.cuda_stream, cid)
+        if tuple(out.shape) != (M, N) or out.device != dev:
+            raise ValueError("out must be (%d, %d) on %s" % (M, N, dev))
+    lib = _lib if _lib is not None else library()
+    idx = dev.index if dev.index is not None else torch.cuda.current_device()
+    sptr = stream.cuda_stream if stream is not None else _raw_stream(idx)
+    args = (M, N, K, a.data_ptr(), b.data_ptr(), out.data_ptr(), bptr, epi, sptr)
+    # the library launches on the calling thread's current HIP device
+    if idx == torch.cuda.current_device():
+        st = (lib.mi355gemm_gemm(*args) if config is None else
+              lib.mi355gemm_gemm_config(*args, config_id(config) if isinstance(config, str) else int(config)))
+    else:
+        with torch.cuda.device(idx):
+            st = (lib.mi355gemm_gemm(*args) if config is None else
+                  lib.mi355gemm_gemm_config(*args, config_id(config) if isinstance(config, str) else int(config)))
     if st != OK:
         raise GemmError(st, mi355gemm_last_error())
     return out

@@ -1,5 +1,7 @@
-// Direct-to-LDS GEMM kernel for gfx950: the fast path for 16-byte-friendly operands
-// (K % 8 == 0 and N % 8 == 0, 16-byte aligned A, B, C).
+// Direct-to-LDS GEMM kernel for gfx950: the fast path whenever B and C rows are 16-byte
+// friendly (N % 8 == 0, 16-byte aligned B and C, 8-byte aligned bias).  A may have any
+// 2-byte alignment and any K: the LDS-DMA copy takes unaligned source offsets, and the
+// one chunk per row that straddles K (K % 8 != 0) is patched in LDS (see load_tail).
 //
 // One workgroup computes one BM x BN macro-tile of C with WAVES_M x WAVES_N x KGROUPS
 // wavefronts (two per SIMD in the shipped configurations, so one wave's LDS reads and
@@ -151,6 +153,10 @@ struct DirectWave {
     int b_k_byte[T::Q];
     int b_col_byte[T::FN];
     int b_row_byte;
+    uint32_t tailh[T::GA][8]; // the K-tail chunks of this lane's A pieces (K % 8 != 0),
+                              // one half per register: packed only when patched, so the
+                              // loads stay in flight until then
+    uint32_t tail_mask;       // bit g: piece g of the last stage straddles K
     f32x16 acc[T::FM][T::FN];
     f16x8 af[2][T::FM];
     s16x4 bl[2][T::FN], bh[2][T::FN];
@@ -219,6 +225,51 @@ struct DirectWave {
 #pragma unroll
             for (int j = 0; j < T::FN; ++j)
                 acc[i][j] = f32x16{};
+    }
+
+    // K % 8 != 0: in the last stage, the A chunk of a row that contains K holds some
+    // elements below K and some past it.  The copy would read the next row's elements (or
+    // past the end of A) there, so the lane that copies such a chunk loads its elements
+    // below K one by one (zeros past K) at the start of the kernel, and patch_tail()
+    // writes them over the copied chunk once the last stage's copy has landed.
+    __device__ __forceinline__ void load_tail(int nk)
+    {
+        tail_mask = 0;
+        const int k0 = (nk - 1) * T::BK;
+#pragma unroll
+        for (int g = 0; g < T::GA; ++g) {
+            const int k = k0 + a_kc[g];
+            if (k < K && k + 8 > K) tail_mask |= 1u << g;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const uint32_t off = masked_offset(a_off[g] + (uint32_t)(k0 + e) * 2u, k + e < K);
+                tailh[g][e] = __builtin_amdgcn_raw_buffer_load_b16(a_rs, off, 0, 0);
+            }
+        }
+    }
+
+    // Overwrites the straddling chunks of the last stage, held in slot dst, with the
+    // values load_tail() read; call after that stage's copy has landed and before the
+    // barrier that lets the waves read it.
+    __device__ __forceinline__ void patch_tail(St &dst) const
+    {
+#pragma unroll
+        for (int g = 0; g < T::GA; ++g) {
+            if (tail_mask & (1u << g)) {
+                char *q = reinterpret_cast<char *>(dst.a) + ((g * T::NW + wave) * 64 + lane) * 16;
+                uint32_t t[8];
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    t[e] = tailh[g][e];
+                    // opaque here, so the packing (and the wait for these loads) is not
+                    // hoisted out of the K loop to the start of the kernel
+                    asm volatile("" : "+v"(t[e]));
+                }
+                *reinterpret_cast<u32x4 *>(q) =
+                    u32x4{t[0] | (t[1] << 16), t[2] | (t[3] << 16), t[4] | (t[5] << 16), t[6] | (t[7] << 16)};
+            }
+        }
+        wait_counts<63, 0>();   // the patch is in LDS before the barrier
     }
 
     // Piece g (0 <= g < G) of the HBM -> LDS copy of stage kt (A rows [m0, m0+BM) x k
@@ -386,6 +437,8 @@ __global__ void __launch_bounds__(T::NT) gemm_direct(GemmArgs p)
 
     DirectWave<T> w;
     w.init(p, m0, n0, rows_valid, p.N - n0);
+    const bool k_tail = (p.K & 7) != 0;
+    if (k_tail && nk > 0) w.load_tail(nk);
 
     St *const ring = reinterpret_cast<St *>(lds_raw);
 
@@ -412,6 +465,7 @@ __global__ void __launch_bounds__(T::NT) gemm_direct(GemmArgs p)
                 // stage kt+1 has landed once at most the STAGES-2 later copies are in
                 // flight; this wave's reads of stage kt were issued before the barrier
                 wait_counts<T::G * (T::STAGES - 2), 15>();
+                if (k_tail && kt + 1 == nk - 1) w.patch_tail(nxt);
                 workgroup_barrier();
             }
             static_for<T::NMFMA>([&](auto mc) {
@@ -442,6 +496,7 @@ __global__ void __launch_bounds__(T::NT) gemm_direct(GemmArgs p)
 #pragma unroll
         for (int s = 0; s < T::STAGES - 1; ++s) w.issue_stage(ring[s], s);
         wait_counts<T::G * (T::STAGES - 2), 15>();
+        if (k_tail && nk == 1) w.patch_tail(ring[0]);
         workgroup_barrier();
         w.read_all(ring[0], 0, 0);
 

@@ -77,13 +77,13 @@ Config direct_config(const char *name, int group_m)
 {
     return Config{name, true, T::BM, T::BN, T::BK, T::STAGES, T::WAVES_M, T::WAVES_N, T::KGROUPS,
                   T::NT,
-                  T::LDS_BYTES, true, true, group_m,
+                  T::LDS_BYTES, false, true, group_m,
                   {gemm_direct<T, 0>, gemm_direct<T, 1>, gemm_direct<T, 2>}};
 }
 
 const Config kConfigs[] = {
-    direct_config<D256>("d256x256x32_w2x4_s4", 8),
-    direct_config<D256k64>("d256x256x64_w2x4_s2", 8),
+    direct_config<D256>("d256x256x32_w2x4_s4", 4),
+    direct_config<D256k64>("d256x256x64_w2x4_s2", 4),
     direct_config<D256x128>("d256x128x64_w2x2k2_s3", 8),
     direct_config<D128>("d128x128x64_w2x2k2_s4", 8),
     direct_config<D128w4>("d128x128x64_w2x2_s4", 8),
@@ -171,18 +171,21 @@ int find_direct(int bm, int bn, int bk, int waves, int k_groups)
     return -1;
 }
 
-// Shape-keyed choice (host only), from timings on MI355X.  A launch should cover the 256
-// compute units; among the tiles that do, the largest wins (fewer bytes per flop from L2
-// into LDS).  256x256 tiles need a full wave of workgroups (M and N >= 4096 or so);
-// 128x128 direct tiles serve mid-size problems; the register-staged kernels take
-// unaligned or small problems (the direct kernels need 16-byte rows and operands).
+// Shape-keyed choice (host only), from interleaved timings on MI355X.  A launch should
+// cover the 256 compute units; among the tiles that do, the largest wins (fewer bytes per
+// flop from L2 into LDS).  256x256 tiles need a full wave of workgroups: from two waves
+// on, the 32-deep 4-stage ring (3 stages in flight) is ahead, for one wave the 64-deep
+// 2-stage ring; mid-size problems take 128x128 tiles with two k-groups of 4 waves (two
+// waves per SIMD); the register-staged kernels take unaligned or small problems (the
+// direct kernels need 16-byte-friendly B and C rows; A may have any alignment).
 int choose(const Request &r)
 {
     const bool av = a_vector_ok(r), bv = bc_vector_ok(r);
     constexpr int64_t kCUs = 256;
-    if (av && bv) {
+    if (bv) {
+        if (tiles(r, 256, 256) >= 2 * kCUs) return find_direct(256, 256, 32, 8, 1);
         if (tiles(r, 256, 256) >= kCUs) return find_direct(256, 256, 64, 8, 1);
-        if (tiles(r, 128, 128) >= kCUs / 2) return find_direct(128, 128, 64, 4, 1);
+        if (tiles(r, 128, 128) >= kCUs / 2) return find_direct(128, 128, 64, 8, 2);
     }
     if (tiles(r, 128, 128) >= kCUs / 2) return find_staged(128, 128, av, bv);
     return find_staged(64, 64, av, bv);

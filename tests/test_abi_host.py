@@ -54,9 +54,10 @@ def test_config_table_is_consistent():
     assert any(c["direct"] for c in cfgs) and any(not c["direct"] for c in cfgs)
     for c in cfgs:
         if c["direct"]:
-            # ring of STAGES buffers of the A (BM x BK) and B (BK x BN) tiles, XOR-swizzled
+            # ring of STAGES buffers of the A (BM x BK) and B (BK x BN) tiles, XOR-swizzled;
+            # A may have any alignment (unaligned LDS-DMA, K tail patched), B and C not
             assert c["lds_bytes"] == c["stages"] * (c["block_m"] + c["block_n"]) * c["block_k"] * 2
-            assert c["a_vector"] == 1 and c["bc_vector"] == 1
+            assert c["a_vector"] == 0 and c["bc_vector"] == 1
         else:
             # two LDS stages of BM and BN rows of BK halves plus a 16-byte pad per row
             assert c["lds_bytes"] == c["stages"] * (c["block_m"] + c["block_n"]) * (c["block_k"] + 8) * 2
@@ -136,11 +137,11 @@ def test_select_for_the_workload_shapes():
             i = _select(w.M, w.N, w.K, epi)
             assert i >= 0, w.name
             c = _cfg(i)
-            if w.K % 8 == 0:
-                assert c["a_vector"] == 1, w.name
-            else:
-                assert c["a_vector"] == 0, w.name     # ragged K: 2-byte loads for A
+            if w.K % 8 != 0:
+                assert c["a_vector"] == 0, w.name     # ragged K: A may not need 16-byte rows
             assert c["bc_vector"] == (1 if w.N % 8 == 0 else 0), w.name
+            # every workload but the tiny one fills the chip with the direct kernel
+            assert c["direct"] == (0 if w.M * w.N < 128 * 128 * 128 else 1), w.name
     # large square problems take the widest tile; 2048^3 must still fill 256 CUs
     big = _cfg(_select(8192, 8192, 8192))
     assert (big["block_m"], big["block_n"]) == (256, 256)
@@ -154,6 +155,10 @@ def test_select_for_the_workload_shapes():
 def test_select_routes_misaligned_pointers_to_narrow_loads():
     c = _cfg(_select(512, 512, 512, A=P2))
     assert c["a_vector"] == 0 and c["bc_vector"] == 1
+    c = _cfg(_select(2048, 2048, 2048, A=P2))        # A misaligned: still the direct kernel
+    assert c["direct"] == 1
+    c = _cfg(_select(1000, 3000, 777))                # the ragged workload: direct, K tail patched
+    assert c["direct"] == 1
     c = _cfg(_select(512, 512, 512, B=P2))
     assert c["bc_vector"] == 0
     c = _cfg(_select(512, 512, 512, C=P2))

@@ -288,3 +288,33 @@ def test_gelu_epilogue_every_finite_fp16_input():
         assert d.max() <= 1, "%s: GELU off by %d fp16 steps at bias %r" % (
             cfg["name"], d.max(), float(bias[int(np.argmax(d.max(axis=0)))]))
         assert (d == 0).mean() >= 0.99, "%s: only %.4f exact" % (cfg["name"], (d == 0).mean())
+
+
+# ---- the direct kernel on A with any alignment and any K --------------------------------
+
+@pytest.mark.parametrize("shape", [(300, 264, 777), (1000, 3000, 777), (130, 136, 9), (64, 128, 5),
+                                   (257, 384, 1027), (128, 128, 65)],
+                         ids=lambda s: "%dx%dx%d" % s)
+def test_direct_kernel_k_tail_and_misaligned_a(shape):
+    """K % 8 != 0 (the chunk of each A row that holds K is patched in LDS) and an A that is
+    only 2-byte aligned, on every direct configuration, against the oracle; C sits between
+    NaN guard bands."""
+    M, N, K = shape
+    A, B, bias = workloads.make_inputs(M, N, K, "uniform", with_bias=True, seed=K)
+    refs = {e: oracle.gemm(A, B, bias, e) for e in ("none", "bias_gelu")}
+    Ab = torch.zeros(M * K + 1, dtype=torch.float16, device=DEV)
+    Ab[1:] = A.reshape(-1).to(DEV)
+    for cfg in all_configs():
+        if not cfg["direct"]:
+            continue
+        for a_dev, how in ((A.to(DEV), "aligned"), (Ab[1:].view(M, K), "A+2 bytes")):
+            for e in ("none", "bias_gelu"):
+                pad = 4096
+                buf = torch.full((M * N + 2 * pad,), float("nan"), dtype=torch.float16, device=DEV)
+                out = buf[pad:pad + M * N].view(M, N)
+                print("direct", cfg["name"], shape, how, e, flush=True)
+                g.gemm(a_dev, B.to(DEV), bias.to(DEV) if e != "none" else None, e, out=out,
+                       config=cfg["id"])
+                torch.cuda.synchronize()
+                assert torch.isnan(buf[:pad]).all().item() and torch.isnan(buf[pad + M * N:]).all().item()
+                assert_parity(out, refs[e], "%s %s %s %s" % (cfg["name"], shape, how, e))
