@@ -157,6 +157,7 @@ struct DirectWave {
                               // one half per register: packed only when patched, so the
                               // loads stay in flight until then
     uint32_t tail_mask;       // bit g: piece g of the last stage straddles K
+    u32x2 bias_raw[T::FN][4]; // bias of this lane's accumulator columns (bias epilogues)
     f32x16 acc[T::FM][T::FN];
     f16x8 af[2][T::FM];
     s16x4 bl[2][T::FN], bh[2][T::FN];
@@ -225,6 +226,21 @@ struct DirectWave {
 #pragma unroll
             for (int j = 0; j < T::FN; ++j)
                 acc[i][j] = f32x16{};
+    }
+
+    // The bias values this lane's accumulator columns need, loaded at the start so the
+    // epilogue does not wait a memory round trip for them.  Columns past N read 0.
+    __device__ __forceinline__ void load_bias(const GemmArgs &p)
+    {
+        const __amdgpu_buffer_rsrc_t b_rs = make_rsrc(p.bias + n0, (uint32_t)(N - n0) * 2u);
+        const int half = lane >> 5;
+#pragma unroll
+        for (int j = 0; j < T::FN; ++j)
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                const int n = wn * T::WTN + j * 32 + 8 * g + 4 * half;
+                bias_raw[j][g] = __builtin_amdgcn_raw_buffer_load_b64(b_rs, (uint32_t)n * 2u, 0, 0);
+            }
     }
 
     // K % 8 != 0: in the last stage, the A chunk of a row that contains K holds some
@@ -352,12 +368,13 @@ __device__ __forceinline__ int c_chunk_swz(int r)
 // written into the LDS copy of the tile.  Accumulator layout of v_mfma_f32_32x32x16_f16
 // with the B fragment as the first operand: register r of lane l holds
 // C[32 i + l % 32][32 j + 8 (r / 4) + 4 (l / 32) + r % 4] of the wave's sub-tile.
+// bias_raw[j][g] holds the four bias values of this lane's columns in register quad g of
+// block column j (loaded by DirectWave::load_bias at the start of the kernel).
 template <class T, int I0, int I1, int EPI>
-__device__ __forceinline__ void tile_to_lds(const f32x16 (&acc)[T::FM][T::FN], const GemmArgs &p,
-                                            int n0, int row0, int col0, int lane, char *ctile)
+__device__ __forceinline__ void tile_to_lds(const f32x16 (&acc)[T::FM][T::FN],
+                                            const u32x2 (&bias_raw)[T::FN][4], int row0,
+                                            int col0, int lane, char *ctile)
 {
-    const __amdgpu_buffer_rsrc_t b_rs =
-        make_rsrc(EPI != 0 ? p.bias + n0 : p.C, EPI != 0 ? (uint32_t)(p.N - n0) * 2u : 0u);
     const int half = lane >> 5;
 #pragma unroll
     for (int j = 0; j < T::FN; ++j) {
@@ -366,8 +383,7 @@ __device__ __forceinline__ void tile_to_lds(const f32x16 (&acc)[T::FM][T::FN], c
             const int n = col0 + j * 32 + 8 * g + 4 * half;   // first of 4 columns, tile-relative
             float bv[4] = {0.f, 0.f, 0.f, 0.f};
             if constexpr (EPI != 0) {
-                const u32x2 raw = __builtin_amdgcn_raw_buffer_load_b64(b_rs, (uint32_t)n * 2u, 0, 0);
-                const f16x4 h = __builtin_bit_cast(f16x4, raw);
+                const f16x4 h = __builtin_bit_cast(f16x4, bias_raw[j][g]);
 #pragma unroll
                 for (int e = 0; e < 4; ++e) bv[e] = (float)h[e];
             }
@@ -437,6 +453,7 @@ __global__ void __launch_bounds__(T::NT) gemm_direct(GemmArgs p)
 
     DirectWave<T> w;
     w.init(p, m0, n0, rows_valid, p.N - n0);
+    if constexpr (EPI != 0) w.load_bias(p);
     const bool k_tail = (p.K & 7) != 0;
     if (k_tail && nk > 0) w.load_tail(nk);
 
@@ -516,7 +533,7 @@ __global__ void __launch_bounds__(T::NT) gemm_direct(GemmArgs p)
     workgroup_barrier();
     char *ctile = lds_raw;
     if constexpr (T::KGROUPS == 1) {
-        tile_to_lds<T, 0, T::FM, EPI>(w.acc, p, n0, w.wm * T::WTM, w.wn * T::WTN, w.lane, ctile);
+        tile_to_lds<T, 0, T::FM, EPI>(w.acc, w.bias_raw, w.wm * T::WTM, w.wn * T::WTN, w.lane, ctile);
     } else {
         // Sum the two k-groups' partial tiles.  Group 0 keeps blocks i < FM/2 and hands
         // blocks i >= FM/2 to group 1; group 1 does the opposite; each then finishes the
@@ -554,7 +571,7 @@ __global__ void __launch_bounds__(T::NT) gemm_direct(GemmArgs p)
                         for (int e = 0; e < 4; ++e) w.acc[KEEP + ii][j][4 * c + e] += o[e];
                     }
             __syncthreads();   // the exchange area is overwritten by the C tile below
-            tile_to_lds<T, KEEP, KEEP + H, EPI>(w.acc, p, n0, w.wm * T::WTM, w.wn * T::WTN,
+            tile_to_lds<T, KEEP, KEEP + H, EPI>(w.acc, w.bias_raw, w.wm * T::WTM, w.wn * T::WTN,
                                                 w.lane, ctile);
         };
         if (w.kg == 0)
