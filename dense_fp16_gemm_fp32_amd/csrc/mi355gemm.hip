@@ -171,20 +171,22 @@ int find_direct(int bm, int bn, int bk, int waves, int k_groups)
     return -1;
 }
 
-// Shape-keyed choice (host only), from interleaved timings on MI355X.  A launch should
-// cover the 256 compute units; among the tiles that do, the largest wins (fewer bytes per
-// flop from L2 into LDS).  256x256 tiles need a full wave of workgroups: from two waves
-// on, the 32-deep 4-stage ring (3 stages in flight) is ahead, for one wave the 64-deep
-// 2-stage ring; mid-size problems take 128x128 tiles with two k-groups of 4 waves (two
-// waves per SIMD); the register-staged kernels take unaligned or small problems (the
-// direct kernels need 16-byte-friendly B and C rows; A may have any alignment).
+// Shape-keyed choice (host only), from interleaved timings of the candidates on several
+// MI355X boxes.  A launch should cover the 256 compute units; among the tiles that do,
+// the largest wins (fewer bytes per flop from L2 into LDS).  With every CU busy the part
+// runs at its power limit, where the lighter configurations are the steadier ones:
+// 256x256x64 tiles (8 waves, 2 stages) from one full wave of them, 128x128 tiles with 4
+// waves when they fill the chip; with part of the chip idle (fewer than 256 128x128
+// tiles) the two k-groups' extra latency hiding wins.  The register-staged kernels take
+// small problems and those whose B or C rows are not 16-byte friendly (the direct kernels
+// need N % 8 == 0 and 16-byte aligned B and C; A may have any alignment).
 int choose(const Request &r)
 {
     const bool av = a_vector_ok(r), bv = bc_vector_ok(r);
     constexpr int64_t kCUs = 256;
     if (bv) {
-        if (tiles(r, 256, 256) >= 2 * kCUs) return find_direct(256, 256, 32, 8, 1);
         if (tiles(r, 256, 256) >= kCUs) return find_direct(256, 256, 64, 8, 1);
+        if (tiles(r, 128, 128) >= kCUs) return find_direct(128, 128, 64, 4, 1);
         if (tiles(r, 128, 128) >= kCUs / 2) return find_direct(128, 128, 64, 8, 2);
     }
     if (tiles(r, 128, 128) >= kCUs / 2) return find_staged(128, 128, av, bv);
