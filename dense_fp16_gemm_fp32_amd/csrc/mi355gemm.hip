@@ -8,6 +8,7 @@
 #include <stdarg.h>
 #include <stdint.h>
 #include <stdio.h>
+#include <string.h>
 
 #include "gemm_direct.hpp"
 #include "gemm_staged.hpp"
@@ -171,6 +172,38 @@ int find_direct(int bm, int bn, int bk, int waves, int k_groups)
     return -1;
 }
 
+// Can configuration c serve request r?  (Silent version of check_config.)
+bool config_fits(const Config &c, const Request &r)
+{
+    return c.lds_bytes <= kLdsBudget && (!c.a_vec || a_vector_ok(r)) && (!c.bc_vec || bc_vector_ok(r));
+}
+
+// Measured winners for exact shapes, written by the package's tune.py (an interleaved
+// sweep over the forced configurations); an entry exists only where the winner beat the
+// rules below by the tuner's margin.
+struct TunedEntry {
+    int64_t M, N, K;
+    int epi, a_vec, bc_vec;
+    const char *config;
+};
+const TunedEntry kTuned[] = {
+#include "tuned_table.inc"
+    {0, 0, 0, -1, 0, 0, nullptr},   // end marker (keeps the array non-empty)
+};
+
+int tuned_choice(const Request &r, bool av, bool bv)
+{
+    for (const TunedEntry &t : kTuned) {
+        if (t.config == nullptr) break;
+        if (t.M != r.M || t.N != r.N || t.K != r.K || t.epi != r.epi || t.a_vec != (int)av ||
+            t.bc_vec != (int)bv)
+            continue;
+        for (int i = 0; i < kNumConfigs; ++i)
+            if (strcmp(kConfigs[i].name, t.config) == 0 && config_fits(kConfigs[i], r)) return i;
+    }
+    return -1;
+}
+
 // Shape-keyed choice (host only), from interleaved timings of the candidates on several
 // MI355X boxes.  A launch should cover the 256 compute units; among the tiles that do,
 // the largest wins (fewer bytes per flop from L2 into LDS).  With every CU busy the part
@@ -183,6 +216,8 @@ int find_direct(int bm, int bn, int bk, int waves, int k_groups)
 int choose(const Request &r)
 {
     const bool av = a_vector_ok(r), bv = bc_vector_ok(r);
+    const int tuned = tuned_choice(r, av, bv);
+    if (tuned >= 0) return tuned;
     constexpr int64_t kCUs = 256;
     if (bv) {
         if (tiles(r, 256, 256) >= kCUs) return find_direct(256, 256, 64, 8, 1);

@@ -1,0 +1,183 @@
+"""Shape-keyed autotuning: time every configuration that can serve a shape and write the
+selector's table of measured winners.
+
+The tutorial's schedule sweep (thecryptopost.io page, section 3, "Knobs - sweeping the
+schedule by hand") builds each candidate schedule, checks it numerically, times it and
+keeps the fastest, noting that the best schedule depends on the architecture and the
+shape; its autotuning section searches the same space per target.  Here the candidates
+are the library's compiled configurations, forced one at a time through
+``mi355gemm_gemm_config`` (a configuration that cannot serve the shape is skipped, as the
+sweep skips schedules over the shared-memory budget), and each one is first checked
+against the rule-chosen configuration's output (relative Frobenius distance below 5e-3,
+as a wrong kernel would fail the sweep's numerical check).
+
+MI355X runs these GEMMs at its power limit, so single timings move by several percent
+from run to run: candidates are timed in interleaved rounds and compared by their median.
+A shape gets a table entry only when its winner beats the configuration the selector's
+rules would pick by at least ``--margin`` (default 3%); otherwise the rules stand.
+
+The table is C source, ``csrc/tuned_table.inc``, compiled into the library (rebuild after
+writing it); ``mi355gemm_select`` consults it for an exact (M, N, K, epilogue, alignment)
+match before the rules.
+
+Usage (on the GPU):
+  python -m dense_fp16_gemm_fp32_amd.tune [--shapes MxNxK[:epilogue[:dist]] ...]
+         [--rounds 7] [--margin 0.03] [--write]
+With no --shapes, the benchmark's workloads are tuned.
+"""
+from __future__ import annotations
+
+import argparse
+import datetime
+import os
+import statistics
+import sys
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(PKG)
+TABLE = os.path.join(PKG, "csrc", "tuned_table.inc")
+
+
+def parse_shape(text: str):
+    parts = text.split(":")
+    M, N, K = (int(x) for x in parts[0].split("x"))
+    epi = parts[1] if len(parts) > 1 and parts[1] else "none"
+    dist = parts[2] if len(parts) > 2 and parts[2] else "normal"
+    return M, N, K, epi, dist
+
+
+def default_shapes():
+    if ROOT not in sys.path:
+        sys.path.insert(0, ROOT)
+    import workloads
+    out = []
+    for w in workloads.WORKLOADS:
+        for e in w.epilogues:
+            out.append((w.M, w.N, w.K, e, w.dist))
+    return out
+
+
+def _aligned(t, n):
+    return t is None or t.data_ptr() % n == 0
+
+
+def alignment_class(A, B, out, bias, K, N):
+    """(A rows 16-byte friendly, B and C rows 16-byte friendly), as the library defines
+    them (K % 8 == 0 and A 16-byte aligned; N % 8 == 0, B and C 16-byte aligned and the
+    bias 8-byte aligned)."""
+    av = K % 8 == 0 and _aligned(A, 16)
+    bv = N % 8 == 0 and _aligned(B, 16) and _aligned(out, 16) and _aligned(bias, 8)
+    return int(av), int(bv)
+
+
+def _time(fn, steps):
+    import torch
+    s = torch.cuda.current_stream()
+    a = torch.cuda.Event(enable_timing=True)
+    b = torch.cuda.Event(enable_timing=True)
+    a.record(s)
+    for _ in range(steps):
+        fn()
+    b.record(s)
+    torch.cuda.synchronize()
+    return a.elapsed_time(b) / steps * 1e3   # us per call
+
+
+def tune(shapes, rounds=7, margin=0.03, log=print):
+    """Returns a list of dicts, one per shape: the rule choice, every candidate's median
+    time, the winner and whether it earns a table entry."""
+    import torch
+    if ROOT not in sys.path:
+        sys.path.insert(0, ROOT)
+    import dense_fp16_gemm_fp32_amd as g
+    import workloads
+
+    results = []
+    for (M, N, K, epi, dist) in shapes:
+        A, B, bias = workloads.make_inputs(M, N, K, dist, with_bias=True, seed=0)
+        A, B, bias = A.cuda(), B.cuda(), bias.cuda()
+        b_arg = bias if epi != "none" else None
+        out = torch.empty((M, N), dtype=torch.float16, device="cuda")
+        rule = g.select(A, B, b_arg, epi, out=out)
+        ref = g.gemm(A, B, b_arg, epi).float()
+        ref_norm = float(ref.norm())
+        flops = 2.0 * M * N * K
+        steps = max(3, min(300, int(3e-3 / max(flops / 1e15, 1e-9))))   # about 3 ms per timing
+        cands = []
+        for cfg in g.configs():
+            st = g.mi355gemm_gemm_config(M, N, K, A.data_ptr(), B.data_ptr(), out.data_ptr(),
+                                         b_arg.data_ptr() if b_arg is not None else None,
+                                         g.EPILOGUES[epi], torch.cuda.current_stream().cuda_stream,
+                                         cfg["id"])
+            if st != g.OK:
+                continue                                   # cannot serve this shape
+            torch.cuda.synchronize()
+            d = float((out.float() - ref).norm()) / max(ref_norm, 1e-30)
+            if not d <= 5e-3:
+                log("  %s: output differs from the rule choice (rel. Frobenius %.2e), skipped"
+                    % (cfg["name"], d))
+                continue
+            cands.append(cfg)
+        times = {c["name"]: [] for c in cands}
+        for _ in range(rounds):
+            for c in cands:
+                cid = c["id"]
+                for _ in range(2):
+                    g.gemm(A, B, b_arg, epi, out=out, config=cid)
+                torch.cuda.synchronize()
+                times[c["name"]].append(_time(lambda: g.gemm(A, B, b_arg, epi, out=out, config=cid), steps))
+        med = {k: statistics.median(v) for k, v in times.items()}
+        rule_name = g.mi355gemm_config_name(rule)
+        best = min(med, key=med.get)
+        entry = best != rule_name and med[best] <= (1.0 - margin) * med[rule_name]
+        log("%dx%dx%d %s (%s): rule %s %.2f us, best %s %.2f us%s"
+            % (M, N, K, epi, dist, rule_name, med[rule_name], best, med[best],
+               "  -> table entry" if entry else ""))
+        av, bv = alignment_class(A, B, out, b_arg, K, N)
+        results.append({"M": M, "N": N, "K": K, "epilogue": epi, "dist": dist,
+                        "a_vector": av, "bc_vector": bv,
+                        "rule": rule_name, "best": best, "entry": entry, "median_us": med})
+    return results
+
+
+def table_source(results, device: str) -> str:
+    lines = [
+        "// Measured selector table: written by dense_fp16_gemm_fp32_amd/tune.py, do not edit.",
+        "// Device: %s; %s." % (device, datetime.date.today().isoformat()),
+        "// Fields: M, N, K, epilogue, A 16-byte rows, B/C 16-byte rows, configuration name.",
+        "// Shapes whose best configuration beat the rule choice by less than the margin have",
+        "// no entry (the rules stand); their timings are listed for the record.",
+    ]
+    epi_code = {"none": 0, "bias": 1, "bias_gelu": 2}
+    for r in results:
+        lines.append("// %dx%dx%d %s: %s" % (r["M"], r["N"], r["K"], r["epilogue"], ", ".join(
+            "%s %.2f us" % (k, v) for k, v in sorted(r["median_us"].items(), key=lambda kv: kv[1]))))
+        if r["entry"]:
+            lines.append('{%d, %d, %d, %d, %d, %d, "%s"},' % (
+                r["M"], r["N"], r["K"], epi_code[r["epilogue"]], r["a_vector"], r["bc_vector"],
+                r["best"]))
+    return "\n".join(lines) + "\n"
+
+
+def main(argv=None):
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--shapes", nargs="*", default=None)
+    ap.add_argument("--rounds", type=int, default=7)
+    ap.add_argument("--margin", type=float, default=0.03)
+    ap.add_argument("--write", action="store_true", help="write csrc/tuned_table.inc")
+    ap.add_argument("--output", default=TABLE)
+    args = ap.parse_args(argv)
+    import torch
+    shapes = [parse_shape(s) for s in args.shapes] if args.shapes else default_shapes()
+    res = tune(shapes, args.rounds, args.margin, log=lambda m: print(m, flush=True))
+    src = table_source(res, torch.cuda.get_device_properties(0).name)
+    if args.write:
+        with open(args.output, "w") as f:
+            f.write(src)
+        print("wrote", args.output, "- rebuild the library to use it")
+    else:
+        sys.stdout.write(src)
+
+
+if __name__ == "__main__":
+    main()

@@ -188,3 +188,39 @@ def test_selected_config_always_passes_its_own_checks():
                 assert K % 8 == 0 and A % 16 == 0
             if c["bc_vector"]:
                 assert N % 8 == 0
+
+
+def _tuned_entries():
+    import re
+    path = os.path.join(ROOT, "dense_fp16_gemm_fp32_amd", "csrc", "tuned_table.inc")
+    text = open(path).read()
+    rows = re.findall(r'^\{(\d+), (\d+), (\d+), (\d), ([01]), ([01]), "([^"]+)"\},\s*$', text, re.M)
+    # every non-comment line must be an entry of that exact form
+    body = [l for l in text.splitlines() if l.strip() and not l.strip().startswith("//")]
+    assert len(body) == len(rows), body
+    return [(int(a), int(b), int(c), int(d), int(e), int(f), name) for a, b, c, d, e, f, name in rows]
+
+
+def test_tuned_table_entries_name_real_configs_and_drive_the_selector():
+    names = {c["name"] for c in g.configs()}
+    for M, N, K, epi, av, bv, name in _tuned_entries():
+        assert name in names, name
+        A = P16 if av else P2          # fake pointers with the entry's alignment class
+        B = C = P16 if bv else P2
+        i = _select(M, N, K, epi, A=A, B=B, C=C, bias=P16 if bv else P2)
+        assert g.mi355gemm_config_name(i) == name, (M, N, K, epi, av, bv)
+
+
+def test_tuner_writes_entries_only_for_wins_above_the_margin():
+    from dense_fp16_gemm_fp32_amd import tune
+    res = [
+        {"M": 64, "N": 64, "K": 64, "epilogue": "none", "a_vector": 1, "bc_vector": 1,
+         "rule": "a", "best": "b", "entry": True, "median_us": {"a": 10.0, "b": 9.0}},
+        {"M": 32, "N": 64, "K": 8, "epilogue": "bias_gelu", "a_vector": 0, "bc_vector": 1,
+         "rule": "a", "best": "a", "entry": False, "median_us": {"a": 5.0}},
+    ]
+    src = tune.table_source(res, "test device")
+    body = [l for l in src.splitlines() if not l.startswith("//")]
+    assert body == ['{64, 64, 64, 0, 1, 1, "b"},']
+    assert tune.parse_shape("1000x3000x777:bias_gelu:uniform") == (1000, 3000, 777, "bias_gelu", "uniform")
+    assert tune.parse_shape("8x16x24") == (8, 16, 24, "none", "normal")
