@@ -136,6 +136,39 @@ def run_workload(lib, w, epi, steps, warmup, config=None):
     }
 
 
+def run_vector_add(lib, n, steps, warmup):
+    """The tutorial's first kernel at n elements: c = a + b (fp16), 6 bytes per element.
+    Its GB/s is the measured HBM roofline the GEMM's traffic figures are read against;
+    torch's own a + b on the same tensors is timed beside it as context."""
+    import torch
+    gen = torch.Generator(device="cpu")
+    gen.manual_seed(0)
+    a = torch.randn(n, generator=gen, dtype=torch.float32).to(torch.float16).to("cuda:0")
+    b = torch.randn(n, generator=gen, dtype=torch.float32).to(torch.float16).to("cuda:0")
+    c = torch.empty_like(a)
+    stream = torch.cuda.current_stream()
+    out = {"workload": "vector_add", "n": n, "bytes": 6 * n}
+    for name, fn in (("mi355gemm", lambda: lib.vector_add(a, b, out=c)),
+                     ("torch", lambda: torch.add(a, b, out=c))):
+        for _ in range(warmup):
+            fn()
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(steps):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / steps
+        gbs = 6.0 * n / (ms * 1e-3) / 1e9
+        if name == "mi355gemm":
+            out.update({"us": ms * 1e3, "GBps": gbs, "frac_of_hbm_peak": gbs / PEAK_HBM_GBS})
+        else:
+            out["torch_GBps"] = gbs
+    return out
+
+
 def calibrate_copy(reps=5, mib=256):
     """A plain device-to-device copy of known size (mib MiB read, mib MiB written), for
     scaling rocprofv3's FETCH_SIZE / WRITE_SIZE counters."""
@@ -205,6 +238,12 @@ def main():
                       file=sys.stderr, flush=True)
                 extra.append(r)
 
+    vadd = None
+    if not args.no_extra:
+        vadd = run_vector_add(lib, 1 << 28, 50, 5)
+        print("bench: vector_add n=2^28 %.2f us %.1f GB/s (torch %.1f GB/s)"
+              % (vadd["us"], vadd["GBps"], vadd["torch_GBps"]), file=sys.stderr, flush=True)
+
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(w, epi, args.cpu_seconds)
@@ -236,6 +275,7 @@ def main():
                      "frac": head["kernel_tflops"] / PEAK_FP16_TFLOPS,
                      "traffic": traffic_for(head["kernel_config"])},
         "cpu_baseline": cpu,
+        "memory_roofline": vadd,
         "device": {"name": props.name, "arch": getattr(props, "gcnArchName", None),
                    "cus": props.multi_processor_count},
         "workloads": extra,

@@ -28,7 +28,7 @@ STATUS_NAMES = {OK: "OK", EINVAL: "EINVAL", EUNSUPPORTED: "EUNSUPPORTED", EHIP: 
 EXPORTS = (
     "mi355gemm_gemm", "mi355gemm_gemm_config", "mi355gemm_select", "mi355gemm_num_configs",
     "mi355gemm_config_name", "mi355gemm_config_info", "mi355gemm_lds_budget",
-    "mi355gemm_last_error", "mi355gemm_version",
+    "mi355gemm_last_error", "mi355gemm_version", "mi355gemm_vector_add",
 )
 
 
@@ -76,6 +76,8 @@ def library() -> ctypes.CDLL:
         lib.mi355gemm_lds_budget.restype = ci
         lib.mi355gemm_last_error.argtypes = []
         lib.mi355gemm_last_error.restype = ctypes.c_char_p
+        lib.mi355gemm_vector_add.argtypes = [i64, p, p, p, p]
+        lib.mi355gemm_vector_add.restype = ci
         lib.mi355gemm_version.argtypes = []
         lib.mi355gemm_version.restype = ctypes.c_char_p
         _lib = lib
@@ -90,6 +92,10 @@ def mi355gemm_gemm(M, N, K, A, B, C, bias, epi, stream) -> int:
 
 def mi355gemm_gemm_config(M, N, K, A, B, C, bias, epi, stream, config_id) -> int:
     return library().mi355gemm_gemm_config(M, N, K, A, B, C, bias, epi, stream, config_id)
+
+
+def mi355gemm_vector_add(n, a, b, c, stream) -> int:
+    return library().mi355gemm_vector_add(n, a, b, c, stream)
 
 
 def mi355gemm_select(M, N, K, epi, A, B, C, bias) -> int:
@@ -214,6 +220,35 @@ def gemm(a: torch.Tensor, b: torch.Tensor, bias: torch.Tensor | None = None,
         with torch.cuda.device(idx):
             st = (lib.mi355gemm_gemm(*args) if config is None else
                   lib.mi355gemm_gemm_config(*args, config_id(config) if isinstance(config, str) else int(config)))
+    if st != OK:
+        raise GemmError(st, mi355gemm_last_error())
+    return out
+
+
+def vector_add(a: torch.Tensor, b: torch.Tensor, out: torch.Tensor | None = None,
+               stream: torch.cuda.Stream | None = None) -> torch.Tensor:
+    """``out = a + b`` element-wise on the GPU (fp16, one rounding), any shape, contiguous."""
+    for t, name in ((a, "a"), (b, "b")):
+        if not isinstance(t, torch.Tensor) or t.dtype != torch.float16:
+            raise TypeError("%s must be a float16 torch.Tensor" % name)
+        if t.device.type != "cuda" or not t.is_contiguous():
+            raise ValueError("%s must be a contiguous tensor on a GPU device" % name)
+    if a.shape != b.shape or a.device != b.device:
+        raise ValueError("a and b must have the same shape and device")
+    if out is None:
+        out = torch.empty_like(a)
+    elif (out.shape != a.shape or out.dtype != torch.float16 or out.device != a.device
+          or not out.is_contiguous()):
+        raise ValueError("out must be a contiguous float16 tensor shaped like a")
+    lib = _lib if _lib is not None else library()
+    idx = a.device.index if a.device.index is not None else torch.cuda.current_device()
+    sptr = stream.cuda_stream if stream is not None else _raw_stream(idx)
+    args = (a.numel(), a.data_ptr(), b.data_ptr(), out.data_ptr(), sptr)
+    if idx == torch.cuda.current_device():
+        st = lib.mi355gemm_vector_add(*args)
+    else:
+        with torch.cuda.device(idx):
+            st = lib.mi355gemm_vector_add(*args)
     if st != OK:
         raise GemmError(st, mi355gemm_last_error())
     return out

@@ -5,6 +5,8 @@
 
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
+
 #include <stdarg.h>
 #include <stdint.h>
 #include <stdio.h>
@@ -12,6 +14,7 @@
 
 #include "gemm_direct.hpp"
 #include "gemm_staged.hpp"
+#include "vector_add.hpp"
 
 namespace mi355 {
 // direct-to-LDS tiles: BM, BN, BK, waves (M x N), k-groups, LDS stages
@@ -315,6 +318,30 @@ int mi355gemm_select(int64_t M, int64_t N, int64_t K, int epi, const void *A, co
         return -1;
     }
     return choose(r);
+}
+
+mi355gemm_status mi355gemm_vector_add(int64_t n, const void *a, const void *b, void *c,
+                                      void *stream)
+{
+    g_last_error[0] = 0;
+    if (n < 0) return fail(MI355GEMM_EINVAL, "negative length %lld", (long long)n);
+    if (n == 0) return MI355GEMM_OK;
+    if (a == nullptr || b == nullptr || c == nullptr)
+        return fail(MI355GEMM_EINVAL, "a, b and c must not be NULL");
+    if (!aligned(a, 2) || !aligned(b, 2) || !aligned(c, 2))
+        return fail(MI355GEMM_EINVAL, "fp16 pointers must be 2-byte aligned");
+    // elements added one by one until c is 16-byte aligned, then 8 per lane per access
+    const int64_t head = std::min<int64_t>(n, (int64_t)(((16 - ((uintptr_t)c & 15)) & 15) / 2));
+    const int64_t nv = (n - head) / 8;
+    const int64_t blocks = std::max<int64_t>(
+        1, std::min<int64_t>((nv + kVecThreads - 1) / kVecThreads, ((int64_t)1 << 31) - 1));
+    hipLaunchKernelGGL(vector_add_kernel, dim3((unsigned)blocks), dim3(kVecThreads), 0,
+                       static_cast<hipStream_t>(stream), static_cast<const vf16 *>(a),
+                       static_cast<const vf16 *>(b), static_cast<vf16 *>(c), n, head);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess)
+        return fail(MI355GEMM_EHIP, "launch of vector_add failed: %s", hipGetErrorString(e));
+    return MI355GEMM_OK;
 }
 
 int mi355gemm_num_configs(void) { return kNumConfigs; }

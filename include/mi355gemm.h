@@ -95,6 +95,26 @@ mi355gemm_status mi355gemm_gemm_config(int64_t M, int64_t N, int64_t K,
 int mi355gemm_select(int64_t M, int64_t N, int64_t K, int epi,
                      const void *A, const void *B, const void *C, const void *bias);
 
+/*
+ * c[i] = a[i] + b[i] for 0 <= i < n, all fp16, one round-to-nearest-even per element (the
+ * correctly rounded sum), enqueued on `stream`.  The tutorial's first kernel: "Designing
+ * High-Performance GPU Kernels with TileLang: ...", ainovat.com page, first paragraph (a
+ * vector-add kernel whose bandwidth is compared with PyTorch's).  HBM-bound: 6 bytes move
+ * per element; the benchmark reports its GB/s as the measured memory roofline.
+ *
+ * n        number of elements (>= 0; 0 does nothing and returns OK).
+ * a, b     device pointers to n fp16 values each (read).
+ * c        device pointer to n fp16 values (written; may be a or b, element-wise).
+ * stream   hipStream_t to enqueue on; NULL is the default stream.
+ *
+ * Every pointer must be at least 2-byte aligned; any such alignment is served.  The
+ * caller owns the buffers; the call allocates nothing and returns after the enqueue.
+ * Errors: EINVAL for n < 0, a NULL pointer with n > 0 or a misaligned pointer; EHIP if
+ * the launch fails.
+ */
+mi355gemm_status mi355gemm_vector_add(int64_t n, const void *a, const void *b, void *c,
+                                      void *stream);
+
 /* Description of one compiled kernel configuration. */
 typedef struct {
     int block_m, block_n, block_k;  /* macro-tile of C per workgroup and K step */

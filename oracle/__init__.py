@@ -11,7 +11,8 @@ High-Performance GPU Kernels with TileLang: Tensor-Core GEMM, Fused Softmax,
 FlashAttention, and Autotuning": the thecryptopost.io page, section 2 ("Memory
 hierarchy - tiled tensor-core GEMM", ``make_matmul``: A (M, K), B (K, N), C (M, N)
 float16 row-major) for the product, and the ainovat.com page's fused-epilogue
-paragraph for ``GELU(acc + bias)`` before the single fp16 write.
+paragraph for ``GELU(acc + bias)`` before the single fp16 write; ``vector_add`` is the
+same tutorial's first kernel (the ainovat.com page's first paragraph).
 
 Every function here is pinned by ``tests/test_oracle.py`` (closed forms, exhaustive
 codec checks against numpy, exact rational brute force); none is "parity unpinned".
@@ -70,6 +71,8 @@ def _declare(lib: ctypes.CDLL) -> None:
     lib.oracle_gemm.restype = ctypes.c_int
     lib.oracle_gemm_sampled.argtypes = [i64, i64, i64, p, p, p, ctypes.c_int, i64, p, p, p]
     lib.oracle_gemm_sampled.restype = ctypes.c_int
+    lib.oracle_vector_add.argtypes = [i64, p, p, p]
+    lib.oracle_vector_add.restype = ctypes.c_int
     lib.oracle_num_threads.argtypes = []
     lib.oracle_num_threads.restype = ctypes.c_int
     for name in ("oracle_f16_to_f64_array", "oracle_f64_to_f16_array", "oracle_gelu_array"):
@@ -153,6 +156,19 @@ def gemm(A, B, bias=None, epilogue="none", lib=None) -> np.ndarray:
     rc = lib.oracle_gemm(M, N, K, _ptr(a), _ptr(b), _ptr(bb), epi, _ptr(out))
     if rc != 0:
         raise ValueError("oracle_gemm rejected its arguments (rc=%d)" % rc)
+    return out
+
+
+def vector_add(a, b, lib=None) -> np.ndarray:
+    """c = fp16(a + b) element-wise (one rounding); returns uint16 bits of a's shape."""
+    lib = lib or load()
+    x, y = _bits(a), _bits(b)
+    if x.shape != y.shape:
+        raise ValueError("shape mismatch %s vs %s" % (x.shape, y.shape))
+    out = np.empty(x.shape, dtype=np.uint16)
+    rc = lib.oracle_vector_add(x.size, _ptr(x), _ptr(y), _ptr(out))
+    if rc != 0:
+        raise ValueError("oracle_vector_add rejected its arguments (rc=%d)" % rc)
     return out
 
 

@@ -1,5 +1,6 @@
 /*
- * CPU oracle for the half-precision GEMM with optional bias + erf-GELU epilogue.
+ * CPU oracle for the half-precision GEMM with optional bias + erf-GELU epilogue (and the
+ * tutorial's element-wise vector add, oracle_vector_add).
  *
  * TEST INFRASTRUCTURE ONLY.  Nothing on the product path may include, link or call
  * this file; only the test suite, the smoke check and the benchmark's CPU-baseline
@@ -173,6 +174,19 @@ int oracle_gemm_sampled(int64_t M, int64_t N, int64_t K, const uint16_t *A,
     #pragma omp parallel for schedule(dynamic, 16)
     for (int64_t s = 0; s < count; ++s)
         out[s] = element(N, K, A, B, bias, epi, rows[s], cols[s]);
+    return 0;
+}
+
+/* Element-wise sum of two half-precision vectors, the tutorial's first kernel (the
+ * ainovat.com page's first paragraph: a vector-add kernel whose bandwidth is compared with
+ * PyTorch's).  c[i] = fp16_rne(a[i] + b[i]): the sum of two binary16 values is exact in
+ * binary64 (their exponents differ by at most 39, so it needs at most 51 significant bits),
+ * so this is the correctly rounded sum, one rounding. */
+int oracle_vector_add(int64_t n, const uint16_t *a, const uint16_t *b, uint16_t *c)
+{
+    if (n < 0) return 1;
+    for (int64_t i = 0; i < n; ++i)
+        c[i] = oracle_f64_to_f16(oracle_f16_to_f64(a[i]) + oracle_f16_to_f64(b[i]));
     return 0;
 }
 

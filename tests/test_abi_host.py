@@ -30,7 +30,7 @@ def header_functions():
 
 def test_library_exports_every_declared_symbol():
     declared = header_functions()
-    assert len(declared) == 9
+    assert len(declared) == 10
     assert sorted(g.EXPORTS) == declared
     lib = g.library()
     for name in declared:
@@ -224,3 +224,17 @@ def test_tuner_writes_entries_only_for_wins_above_the_margin():
     assert body == ['{64, 64, 64, 0, 1, 1, "b"},']
     assert tune.parse_shape("1000x3000x777:bias_gelu:uniform") == (1000, 3000, 777, "bias_gelu", "uniform")
     assert tune.parse_shape("8x16x24") == (8, 16, 24, "none", "normal")
+
+
+@pytest.mark.parametrize("args,want", [
+    (dict(n=-1), g.EINVAL),
+    (dict(n=0), g.OK),
+    (dict(n=0, a=None, b=None, c=None), g.OK),
+    (dict(n=8, a=None), g.EINVAL),
+    (dict(n=8, c=None), g.EINVAL),
+    (dict(n=8, b=P16 + 1), g.EINVAL),
+])
+def test_vector_add_argument_checks(args, want):
+    a = dict(n=0, a=P16, b=P16, c=P16)
+    a.update(args)
+    assert g.mi355gemm_vector_add(a["n"], a["a"], a["b"], a["c"], None) == want

@@ -384,3 +384,48 @@ def test_rejects_bad_arguments(oracle_lib):
         oracle.gemm(A, np.zeros((2, 4), np.float16), lib=oracle_lib)
     with pytest.raises(ValueError):
         oracle.gemm_sampled(A, B, [2], [0], lib=oracle_lib)
+
+
+# ---------------------------------------------------------------- vector add --------
+
+def _finite(bits):
+    return (bits & 0x7C00) != 0x7C00
+
+
+def test_vector_add_matches_numpy_float16_sums(oracle_lib):
+    """numpy adds two float16 arrays in float32 and rounds once to float16, which is the
+    correctly rounded sum (the float32 sum of two float16 values rounds to the same
+    float16 as the exact sum); random bit patterns cover subnormals, zeros and the
+    overflow boundary."""
+    rng = np.random.default_rng(7)
+    a = rng.integers(0, 1 << 16, 400_000, dtype=np.uint32).astype(np.uint16)
+    b = rng.integers(0, 1 << 16, 400_000, dtype=np.uint32).astype(np.uint16)
+    keep = _finite(a) & _finite(b)
+    a, b = a[keep], b[keep]
+    got = oracle.vector_add(a, b, lib=oracle_lib)
+    with np.errstate(over="ignore"):
+        ref = (a.view(np.float16) + b.view(np.float16)).view(np.uint16)
+    assert np.array_equal(got, ref)
+
+
+def test_vector_add_closed_forms(oracle_lib):
+    f = ALL_BITS[_finite(ALL_BITS)]
+    zero = np.zeros_like(f)
+    # x + 0 = x (and -0 + +0 = +0)
+    got = oracle.vector_add(f, zero, lib=oracle_lib)
+    want = np.where(f == 0x8000, 0, f).astype(np.uint16)
+    assert np.array_equal(got, want)
+    # x + (-x) = +0
+    assert np.all(oracle.vector_add(f, f ^ 0x8000, lib=oracle_lib) == 0)
+    # x + x = 2x exactly while 2x is finite (exponent + 1, or a doubled subnormal)
+    xv = f.view(np.float16).astype(np.float64)
+    ok = np.abs(2 * xv) < 65504
+    got = oracle.vector_add(f[ok], f[ok], lib=oracle_lib).view(np.float16).astype(np.float64)
+    assert np.array_equal(got, 2 * xv[ok])
+    # specials: inf + finite = inf, inf + -inf = nan, nan propagates
+    inf, ninf, nan = np.uint16(0x7C00), np.uint16(0xFC00), np.uint16(0x7E00)
+    r = oracle.vector_add(np.array([inf, inf, nan, 0x3C00], np.uint16),
+                          np.array([0x3C00, ninf, 0x3C00, 0x7BFF], np.uint16), lib=oracle_lib)
+    assert r[0] == 0x7C00 and (r[1] & 0x7C00) == 0x7C00 and (r[1] & 0x3FF) != 0
+    assert (r[2] & 0x7C00) == 0x7C00 and (r[2] & 0x3FF) != 0
+    assert r[3] == 0x7BFF     # 65504 + 1 rounds back to 65504

@@ -42,6 +42,12 @@ MUTANTS = [
     ("fp32_accumulation", [("double s = 0.0;", "float s = 0.0f;"),
                            ("for (int64_t j = 0; j < N; ++j) acc[j] += a * Bd[k * N + j];",
                             "for (int64_t j = 0; j < N; ++j) acc[j] = (float)(acc[j] + a * Bd[k * N + j]);")]),
+    ("vector_add_subtracts", [("oracle_f16_to_f64(a[i]) + oracle_f16_to_f64(b[i])",
+                               "oracle_f16_to_f64(a[i]) - oracle_f16_to_f64(b[i])")]),
+    ("vector_add_drops_b", [("oracle_f16_to_f64(a[i]) + oracle_f16_to_f64(b[i])",
+                             "oracle_f16_to_f64(a[i]) + 0.0 * oracle_f16_to_f64(b[i])")]),
+    ("vector_add_float_sum", [("oracle_f16_to_f64(a[i]) + oracle_f16_to_f64(b[i])",
+                               "(double)(float)(oracle_f16_to_f64(a[i]) + oracle_f16_to_f64(b[i]) * 1.0000001)")]),
 ]
 
 
