@@ -169,6 +169,38 @@ def run_vector_add(lib, n, steps, warmup):
     return out
 
 
+def run_softmax(lib, M, N, steps, warmup):
+    """The tutorial's row-wise softmax on an M x N fp16 matrix (N(0, 3^2) entries, seed 0):
+    4 bytes move per element (one read, one write), so its GB/s reads against HBM peak;
+    torch.softmax on the same tensor is timed beside it as context."""
+    import torch
+    gen = torch.Generator(device="cpu")
+    gen.manual_seed(0)
+    x = (torch.randn(M, N, generator=gen, dtype=torch.float32) * 3).to(torch.float16).to("cuda:0")
+    y = torch.empty_like(x)
+    stream = torch.cuda.current_stream()
+    out = {"workload": "softmax", "M": M, "N": N, "bytes": 4 * M * N}
+    for name, fn in (("mi355gemm", lambda: lib.softmax(x, out=y)),
+                     ("torch", lambda: torch.softmax(x, dim=1, out=y))):
+        for _ in range(warmup):
+            fn()
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(steps):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / steps
+        gbs = 4.0 * M * N / (ms * 1e-3) / 1e9
+        if name == "mi355gemm":
+            out.update({"us": ms * 1e3, "GBps": gbs, "frac_of_hbm_peak": gbs / PEAK_HBM_GBS})
+        else:
+            out.update({"torch_us": ms * 1e3, "torch_GBps": gbs})
+    return out
+
+
 def calibrate_copy(reps=5, mib=256):
     """A plain device-to-device copy of known size (mib MiB read, mib MiB written), for
     scaling rocprofv3's FETCH_SIZE / WRITE_SIZE counters."""
@@ -244,6 +276,14 @@ def main():
         print("bench: vector_add n=2^28 %.2f us %.1f GB/s (torch %.1f GB/s)"
               % (vadd["us"], vadd["GBps"], vadd["torch_GBps"]), file=sys.stderr, flush=True)
 
+    softmax = []
+    if not args.no_extra:
+        for (M, N) in ((8192, 8192), (4096, 4096), (64, 65536)):
+            r = run_softmax(lib, M, N, 100, 5)
+            print("bench: softmax %dx%d %.2f us %.1f GB/s (torch %.1f GB/s)"
+                  % (M, N, r["us"], r["GBps"], r["torch_GBps"]), file=sys.stderr, flush=True)
+            softmax.append(r)
+
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(w, epi, args.cpu_seconds)
@@ -276,6 +316,7 @@ def main():
                      "traffic": traffic_for(head["kernel_config"])},
         "cpu_baseline": cpu,
         "memory_roofline": vadd,
+        "softmax": softmax,
         "device": {"name": props.name, "arch": getattr(props, "gcnArchName", None),
                    "cus": props.multi_processor_count},
         "workloads": extra,

@@ -28,7 +28,7 @@ STATUS_NAMES = {OK: "OK", EINVAL: "EINVAL", EUNSUPPORTED: "EUNSUPPORTED", EHIP: 
 EXPORTS = (
     "mi355gemm_gemm", "mi355gemm_gemm_config", "mi355gemm_select", "mi355gemm_num_configs",
     "mi355gemm_config_name", "mi355gemm_config_info", "mi355gemm_lds_budget",
-    "mi355gemm_last_error", "mi355gemm_version", "mi355gemm_vector_add",
+    "mi355gemm_last_error", "mi355gemm_version", "mi355gemm_vector_add", "mi355gemm_softmax",
 )
 
 
@@ -78,6 +78,8 @@ def library() -> ctypes.CDLL:
         lib.mi355gemm_last_error.restype = ctypes.c_char_p
         lib.mi355gemm_vector_add.argtypes = [i64, p, p, p, p]
         lib.mi355gemm_vector_add.restype = ci
+        lib.mi355gemm_softmax.argtypes = [i64, i64, p, p, p]
+        lib.mi355gemm_softmax.restype = ci
         lib.mi355gemm_version.argtypes = []
         lib.mi355gemm_version.restype = ctypes.c_char_p
         _lib = lib
@@ -96,6 +98,10 @@ def mi355gemm_gemm_config(M, N, K, A, B, C, bias, epi, stream, config_id) -> int
 
 def mi355gemm_vector_add(n, a, b, c, stream) -> int:
     return library().mi355gemm_vector_add(n, a, b, c, stream)
+
+
+def mi355gemm_softmax(M, N, x, y, stream) -> int:
+    return library().mi355gemm_softmax(M, N, x, y, stream)
 
 
 def mi355gemm_select(M, N, K, epi, A, B, C, bias) -> int:
@@ -249,6 +255,30 @@ def vector_add(a: torch.Tensor, b: torch.Tensor, out: torch.Tensor | None = None
     else:
         with torch.cuda.device(idx):
             st = lib.mi355gemm_vector_add(*args)
+    if st != OK:
+        raise GemmError(st, mi355gemm_last_error())
+    return out
+
+
+def softmax(x: torch.Tensor, out: torch.Tensor | None = None,
+            stream: torch.cuda.Stream | None = None) -> torch.Tensor:
+    """Row-wise softmax of a contiguous 2-D fp16 tensor on the GPU (over the last dim)."""
+    _check_tensor(x, "x", 2)
+    if out is None:
+        out = torch.empty_like(x)
+    else:
+        _check_tensor(out, "out", 2)
+        if out.shape != x.shape or out.device != x.device:
+            raise ValueError("out must be shaped like x on its device")
+    lib = _lib if _lib is not None else library()
+    idx = x.device.index if x.device.index is not None else torch.cuda.current_device()
+    sptr = stream.cuda_stream if stream is not None else _raw_stream(idx)
+    M, N = x.shape
+    if idx == torch.cuda.current_device():
+        st = lib.mi355gemm_softmax(M, N, x.data_ptr(), out.data_ptr(), sptr)
+    else:
+        with torch.cuda.device(idx):
+            st = lib.mi355gemm_softmax(M, N, x.data_ptr(), out.data_ptr(), sptr)
     if st != OK:
         raise GemmError(st, mi355gemm_last_error())
     return out

@@ -14,6 +14,7 @@
 
 #include "gemm_direct.hpp"
 #include "gemm_staged.hpp"
+#include "softmax.hpp"
 #include "vector_add.hpp"
 
 namespace mi355 {
@@ -341,6 +342,35 @@ mi355gemm_status mi355gemm_vector_add(int64_t n, const void *a, const void *b, v
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess)
         return fail(MI355GEMM_EHIP, "launch of vector_add failed: %s", hipGetErrorString(e));
+    return MI355GEMM_OK;
+}
+
+mi355gemm_status mi355gemm_softmax(int64_t M, int64_t N, const void *x, void *y, void *stream)
+{
+    g_last_error[0] = 0;
+    if (M < 0 || N < 0)
+        return fail(MI355GEMM_EINVAL, "negative size (M=%lld N=%lld)", (long long)M, (long long)N);
+    if (M == 0 || N == 0) return MI355GEMM_OK;
+    if (x == nullptr || y == nullptr) return fail(MI355GEMM_EINVAL, "x and y must not be NULL");
+    if (!aligned(x, 2) || !aligned(y, 2))
+        return fail(MI355GEMM_EINVAL, "fp16 pointers must be 2-byte aligned");
+    if (N >= ((int64_t)1 << 31) || M >= ((int64_t)1 << 31))
+        return fail(MI355GEMM_EUNSUPPORTED, "M and N must be below 2^31");
+    const sf16 *xs = static_cast<const sf16 *>(x);
+    sf16 *ys = static_cast<sf16 *>(y);
+    const hipStream_t st = static_cast<hipStream_t>(stream);
+    const int n = (int)N;
+    const dim3 rows_grid((unsigned)((M + 3) / 4));
+    if (N <= 512) hipLaunchKernelGGL(softmax_rows<1>, rows_grid, dim3(kSoftmaxThreads), 0, st, xs, ys, M, n);
+    else if (N <= 1024) hipLaunchKernelGGL(softmax_rows<2>, rows_grid, dim3(kSoftmaxThreads), 0, st, xs, ys, M, n);
+    else if (N <= 2048) hipLaunchKernelGGL(softmax_rows<4>, rows_grid, dim3(kSoftmaxThreads), 0, st, xs, ys, M, n);
+    else if (N <= 4096) hipLaunchKernelGGL(softmax_rows<8>, rows_grid, dim3(kSoftmaxThreads), 0, st, xs, ys, M, n);
+    else if (N <= 8192) hipLaunchKernelGGL(softmax_rows<16>, rows_grid, dim3(kSoftmaxThreads), 0, st, xs, ys, M, n);
+    else if (N <= 16384) hipLaunchKernelGGL(softmax_rows<32>, rows_grid, dim3(kSoftmaxThreads), 0, st, xs, ys, M, n);
+    else hipLaunchKernelGGL(softmax_long, dim3((unsigned)M), dim3(kSoftmaxLongThreads), 0, st, xs, ys, n);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess)
+        return fail(MI355GEMM_EHIP, "launch of softmax failed: %s", hipGetErrorString(e));
     return MI355GEMM_OK;
 }
 

@@ -115,6 +115,28 @@ int mi355gemm_select(int64_t M, int64_t N, int64_t K, int epi,
 mi355gemm_status mi355gemm_vector_add(int64_t n, const void *a, const void *b, void *c,
                                       void *stream);
 
+/*
+ * Row-wise softmax: y[i][j] = exp(x[i][j] - m_i) / sum_j exp(x[i][j] - m_i) with
+ * m_i = max_j x[i][j], for an M x N fp16 row-major x; fp32 arithmetic, one rounding to
+ * fp16 per output.  The tutorial's fused softmax: "Designing High-Performance GPU Kernels
+ * with TileLang: ...", ainovat.com page, third paragraph (maximum and sum reductions over
+ * each row, the normalisation kept in registers).  HBM-bound: 4 bytes per element.
+ *
+ * M, N     rows and row length (>= 0; M == 0 or N == 0 does nothing and returns OK).
+ * x        device pointer to M x N fp16 (read), leading dimension N.
+ * y        device pointer to M x N fp16 (written), leading dimension N; may equal x.
+ * stream   hipStream_t to enqueue on; NULL is the default stream.
+ *
+ * Rows of up to 16384 elements are held in registers by one wavefront; longer rows take
+ * two passes over the row by one workgroup.  IEEE rules give the edge cases: a row with
+ * a NaN or +inf entry, or with every entry -inf, comes out NaN.  Pointers must be 2-byte
+ * aligned (any such alignment and any N are served).  The caller owns the buffers; the
+ * call allocates nothing and returns after the enqueue.  Errors: EINVAL for negative
+ * sizes, NULL pointers with work to do or misaligned pointers; EUNSUPPORTED for M or N
+ * of 2^31 or more; EHIP if the launch fails.
+ */
+mi355gemm_status mi355gemm_softmax(int64_t M, int64_t N, const void *x, void *y, void *stream);
+
 /* Description of one compiled kernel configuration. */
 typedef struct {
     int block_m, block_n, block_k;  /* macro-tile of C per workgroup and K step */

@@ -12,7 +12,8 @@ FlashAttention, and Autotuning": the thecryptopost.io page, section 2 ("Memory
 hierarchy - tiled tensor-core GEMM", ``make_matmul``: A (M, K), B (K, N), C (M, N)
 float16 row-major) for the product, and the ainovat.com page's fused-epilogue
 paragraph for ``GELU(acc + bias)`` before the single fp16 write; ``vector_add`` is the
-same tutorial's first kernel (the ainovat.com page's first paragraph).
+same tutorial's first kernel (the ainovat.com page's first paragraph) and ``softmax`` its
+row-wise softmax (the same page's third paragraph).
 
 Every function here is pinned by ``tests/test_oracle.py`` (closed forms, exhaustive
 codec checks against numpy, exact rational brute force); none is "parity unpinned".
@@ -73,6 +74,8 @@ def _declare(lib: ctypes.CDLL) -> None:
     lib.oracle_gemm_sampled.restype = ctypes.c_int
     lib.oracle_vector_add.argtypes = [i64, p, p, p]
     lib.oracle_vector_add.restype = ctypes.c_int
+    lib.oracle_softmax.argtypes = [i64, i64, p, p]
+    lib.oracle_softmax.restype = ctypes.c_int
     lib.oracle_num_threads.argtypes = []
     lib.oracle_num_threads.restype = ctypes.c_int
     for name in ("oracle_f16_to_f64_array", "oracle_f64_to_f16_array", "oracle_gelu_array"):
@@ -169,6 +172,19 @@ def vector_add(a, b, lib=None) -> np.ndarray:
     rc = lib.oracle_vector_add(x.size, _ptr(x), _ptr(y), _ptr(out))
     if rc != 0:
         raise ValueError("oracle_vector_add rejected its arguments (rc=%d)" % rc)
+    return out
+
+
+def softmax(x, lib=None) -> np.ndarray:
+    """Row-wise softmax of a 2-D fp16 array (fp64 inside, one rounding); uint16 bits."""
+    lib = lib or load()
+    a = _bits(x)
+    if a.ndim != 2:
+        raise ValueError("softmax expects a 2-D array, got %s" % (a.shape,))
+    out = np.empty(a.shape, dtype=np.uint16)
+    rc = lib.oracle_softmax(a.shape[0], a.shape[1], _ptr(a), _ptr(out))
+    if rc != 0:
+        raise ValueError("oracle_softmax rejected its arguments (rc=%d)" % rc)
     return out
 
 

@@ -1,6 +1,7 @@
 /*
  * CPU oracle for the half-precision GEMM with optional bias + erf-GELU epilogue (and the
- * tutorial's element-wise vector add, oracle_vector_add).
+ * tutorial's element-wise vector add, oracle_vector_add, and row-wise softmax,
+ * oracle_softmax).
  *
  * TEST INFRASTRUCTURE ONLY.  Nothing on the product path may include, link or call
  * this file; only the test suite, the smoke check and the benchmark's CPU-baseline
@@ -187,6 +188,33 @@ int oracle_vector_add(int64_t n, const uint16_t *a, const uint16_t *b, uint16_t 
     if (n < 0) return 1;
     for (int64_t i = 0; i < n; ++i)
         c[i] = oracle_f64_to_f16(oracle_f16_to_f64(a[i]) + oracle_f16_to_f64(b[i]));
+    return 0;
+}
+
+/* Row-wise softmax, the tutorial's fused softmax (the ainovat.com page's third paragraph:
+ * a row-wise softmax with maximum and sum reductions over each row).  For each row i of
+ * the M x N half-precision input, in fp64:
+ *   m = max_j x[i][j]                 (NaN entries skipped, as fmax does)
+ *   e_j = exp(x[i][j] - m),  s = sum_j e_j  (j in increasing order)
+ *   y[i][j] = fp16_rne(e_j / s)
+ * Subtracting the row maximum changes nothing mathematically (exp(x - m) / sum exp(x - m)
+ * = exp(x) / sum exp(x)) and keeps every exponent <= 0.  IEEE rules give the edge cases:
+ * a row of -inf has m = -inf and -inf - -inf = NaN, so every output is NaN; a +inf entry
+ * gives NaN the same way; a NaN entry makes the sum, and every output, NaN. */
+int oracle_softmax(int64_t M, int64_t N, const uint16_t *x, uint16_t *y)
+{
+    if (M < 0 || N < 0) return 1;
+    #pragma omp parallel for schedule(dynamic, 16)
+    for (int64_t i = 0; i < M; ++i) {
+        const uint16_t *xr = x + i * N;
+        uint16_t *yr = y + i * N;
+        double m = -INFINITY;
+        for (int64_t j = 0; j < N; ++j) m = fmax(m, oracle_f16_to_f64(xr[j]));
+        double s = 0.0;
+        for (int64_t j = 0; j < N; ++j) s += exp(oracle_f16_to_f64(xr[j]) - m);
+        for (int64_t j = 0; j < N; ++j)
+            yr[j] = oracle_f64_to_f16(exp(oracle_f16_to_f64(xr[j]) - m) / s);
+    }
     return 0;
 }
 

@@ -30,7 +30,7 @@ def header_functions():
 
 def test_library_exports_every_declared_symbol():
     declared = header_functions()
-    assert len(declared) == 10
+    assert len(declared) == 11
     assert sorted(g.EXPORTS) == declared
     lib = g.library()
     for name in declared:
@@ -238,3 +238,19 @@ def test_vector_add_argument_checks(args, want):
     a = dict(n=0, a=P16, b=P16, c=P16)
     a.update(args)
     assert g.mi355gemm_vector_add(a["n"], a["a"], a["b"], a["c"], None) == want
+
+
+@pytest.mark.parametrize("args,want", [
+    (dict(M=-1), g.EINVAL),
+    (dict(N=-1), g.EINVAL),
+    (dict(M=0, x=None, y=None), g.OK),
+    (dict(N=0, x=None, y=None), g.OK),
+    (dict(x=None), g.EINVAL),
+    (dict(y=P16 + 1), g.EINVAL),
+    (dict(N=1 << 31), g.EUNSUPPORTED),
+])
+def test_softmax_argument_checks(args, want):
+    a = dict(M=4, N=8, x=P16, y=P16)
+    a.update(args)
+    # every case here fails validation or has nothing to do, so nothing is launched
+    assert g.mi355gemm_softmax(a["M"], a["N"], a["x"], a["y"], None) == want

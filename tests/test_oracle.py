@@ -429,3 +429,60 @@ def test_vector_add_closed_forms(oracle_lib):
     assert r[0] == 0x7C00 and (r[1] & 0x7C00) == 0x7C00 and (r[1] & 0x3FF) != 0
     assert (r[2] & 0x7C00) == 0x7C00 and (r[2] & 0x3FF) != 0
     assert r[3] == 0x7BFF     # 65504 + 1 rounds back to 65504
+
+
+# ---------------------------------------------------------------- softmax -----------
+
+def _sm(x, lib):
+    return oracle.softmax(np.asarray(x, dtype=np.float16), lib=lib).view(np.float16).astype(np.float64)
+
+
+def test_softmax_matches_scipy(oracle_lib):
+    """scipy's fp64 softmax, rounded once to fp16 by numpy, must equal the oracle except
+    at the rare near-ties of the final rounding (none expected at this size)."""
+    from scipy.special import softmax as sp_softmax
+    rng = np.random.default_rng(3)
+    for (M, N, scale) in [(37, 1, 1.0), (23, 5, 3.0), (64, 333, 4.0), (8, 4096, 8.0)]:
+        x = (rng.standard_normal((M, N)) * scale).astype(np.float16)
+        got = oracle.softmax(x, lib=oracle_lib)
+        ref = sp_softmax(x.astype(np.float64), axis=1).astype(np.float16).view(np.uint16)
+        diff = (got != ref).sum()
+        assert diff <= max(1, x.size // 100000), (M, N, diff)
+
+
+def test_softmax_closed_forms(oracle_lib):
+    # equal entries: 1/N everywhere
+    for N in (1, 2, 3, 7, 64, 1000):
+        y = _sm(np.full((3, N), 1.25), oracle_lib)
+        assert np.all(y == np.float64(np.float16(1.0 / N)))
+    # two entries: (sigmoid(a - b), sigmoid(b - a))
+    from scipy.special import expit
+    rng = np.random.default_rng(5)
+    a = rng.standard_normal(200).astype(np.float16)
+    b = rng.standard_normal(200).astype(np.float16)
+    y = _sm(np.stack([a, b], axis=1), oracle_lib)
+    d = a.astype(np.float64) - b.astype(np.float64)
+    assert np.array_equal(y[:, 0], expit(d).astype(np.float16).astype(np.float64))
+    assert np.array_equal(y[:, 1], expit(-d).astype(np.float16).astype(np.float64))
+    # shift invariance by a power of two that keeps every value exact in fp16
+    x = np.round(rng.standard_normal((16, 50)) * 4).astype(np.float16)
+    assert np.array_equal(_sm(x, oracle_lib), _sm(x + np.float16(32), oracle_lib))
+    # a dominant entry: one-hot (the rest underflow below fp16's smallest subnormal)
+    x = np.zeros((4, 300), np.float16)
+    x[np.arange(4), [0, 17, 150, 299]] = 60.0
+    y = _sm(x, oracle_lib)
+    assert np.all(y[np.arange(4), [0, 17, 150, 299]] == 1.0) and y.sum() == 4.0
+    # rows sum to 1 within the fp16 rounding of each entry
+    x = (rng.standard_normal((32, 777)) * 2).astype(np.float16)
+    y = _sm(x, oracle_lib)
+    assert np.all(np.abs(y.sum(axis=1) - 1.0) <= 777 * 2.0 ** -12)
+
+
+def test_softmax_ieee_edge_cases(oracle_lib):
+    ninf, pinf, nan = -np.inf, np.inf, np.nan
+    x = np.array([[ninf, 0.0, 1.0], [ninf, ninf, ninf], [pinf, 0.0, 1.0], [nan, 0.0, 1.0]], np.float16)
+    y = _sm(x, oracle_lib)
+    assert y[0, 0] == 0.0 and np.isclose(y[0, 1] + y[0, 2], 1.0, atol=1e-3)
+    assert np.all(np.isnan(y[1])) and np.all(np.isnan(y[2])) and np.all(np.isnan(y[3]))
+    assert oracle.softmax(np.zeros((0, 5), np.float16), lib=oracle_lib).shape == (0, 5)
+    assert oracle.softmax(np.zeros((5, 0), np.float16), lib=oracle_lib).shape == (5, 0)

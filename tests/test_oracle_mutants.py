@@ -42,6 +42,9 @@ MUTANTS = [
     ("fp32_accumulation", [("double s = 0.0;", "float s = 0.0f;"),
                            ("for (int64_t j = 0; j < N; ++j) acc[j] += a * Bd[k * N + j];",
                             "for (int64_t j = 0; j < N; ++j) acc[j] = (float)(acc[j] + a * Bd[k * N + j]);")]),
+    ("softmax_no_max_shift", [("s += exp(oracle_f16_to_f64(xr[j]) - m);", "s += exp(oracle_f16_to_f64(xr[j]) - 0.0 * m);")]),
+    ("softmax_skips_first", [("for (int64_t j = 0; j < N; ++j) s += exp(", "for (int64_t j = 1; j < N; ++j) s += exp(")]),
+    ("softmax_wrong_axis", [("const uint16_t *xr = x + i * N;", "const uint16_t *xr = x + (i * N) % (N > 1 ? N : 1);")]),
     ("vector_add_subtracts", [("oracle_f16_to_f64(a[i]) + oracle_f16_to_f64(b[i])",
                                "oracle_f16_to_f64(a[i]) - oracle_f16_to_f64(b[i])")]),
     ("vector_add_drops_b", [("oracle_f16_to_f64(a[i]) + oracle_f16_to_f64(b[i])",
