@@ -12,8 +12,9 @@ FlashAttention, and Autotuning": the thecryptopost.io page, section 2 ("Memory
 hierarchy - tiled tensor-core GEMM", ``make_matmul``: A (M, K), B (K, N), C (M, N)
 float16 row-major) for the product, and the ainovat.com page's fused-epilogue
 paragraph for ``GELU(acc + bias)`` before the single fp16 write; ``vector_add`` is the
-same tutorial's first kernel (the ainovat.com page's first paragraph) and ``softmax`` its
-row-wise softmax (the same page's third paragraph).
+same tutorial's first kernel (the ainovat.com page's first paragraph), ``softmax`` its
+row-wise softmax (the same page's third paragraph) and ``attention`` the plain definition
+its FlashAttention forward kernel computes (the same page's FlashAttention paragraph).
 
 Every function here is pinned by ``tests/test_oracle.py`` (closed forms, exhaustive
 codec checks against numpy, exact rational brute force); none is "parity unpinned".
@@ -76,6 +77,12 @@ def _declare(lib: ctypes.CDLL) -> None:
     lib.oracle_vector_add.restype = ctypes.c_int
     lib.oracle_softmax.argtypes = [i64, i64, p, p]
     lib.oracle_softmax.restype = ctypes.c_int
+    d = ctypes.c_double
+    lib.oracle_attention.argtypes = [i64, i64, i64, i64, p, p, p, d, ctypes.c_int, p, p, p]
+    lib.oracle_attention.restype = ctypes.c_int
+    lib.oracle_attention_rows.argtypes = [i64, i64, i64, i64, p, p, p, d, ctypes.c_int, i64,
+                                          p, p, p, p, p]
+    lib.oracle_attention_rows.restype = ctypes.c_int
     lib.oracle_num_threads.argtypes = []
     lib.oracle_num_threads.restype = ctypes.c_int
     for name in ("oracle_f16_to_f64_array", "oracle_f64_to_f16_array", "oracle_gelu_array"):
@@ -186,6 +193,63 @@ def softmax(x, lib=None) -> np.ndarray:
     if rc != 0:
         raise ValueError("oracle_softmax rejected its arguments (rc=%d)" % rc)
     return out
+
+
+def _attn_operands(q, k, v):
+    qb, kb, vb = _bits(q), _bits(k), _bits(v)
+    if qb.ndim < 2 or kb.shape != vb.shape or qb.shape[:-2] != kb.shape[:-2] \
+            or qb.shape[-1] != kb.shape[-1]:
+        raise ValueError("attention expects q (..., Sq, D), k and v (..., Sk, D); got %s %s %s"
+                         % (qb.shape, kb.shape, vb.shape))
+    return qb, kb, vb
+
+
+def attention(q, k, v, scale=None, causal=False, lib=None):
+    """Attention forward over the leading (batch, head) dimensions, fp64 inside, one
+    rounding: returns (o bits uint16 shaped like q, lse fp64 (..., Sq), err fp64 like q),
+    err being sum_j p_j |v_j| / l per output element (the tolerance scale)."""
+    lib = lib or load()
+    qb, kb, vb = _attn_operands(q, k, v)
+    Sq, D = qb.shape[-2:]
+    Sk = kb.shape[-2]
+    BH = int(np.prod(qb.shape[:-2], dtype=np.int64))
+    if scale is None:
+        scale = 1.0 / np.sqrt(D)
+    o = np.empty(qb.shape, dtype=np.uint16)
+    lse = np.empty(qb.shape[:-1], dtype=np.float64)
+    err = np.empty(qb.shape, dtype=np.float64)
+    rc = lib.oracle_attention(BH, Sq, Sk, D, _ptr(qb), _ptr(kb), _ptr(vb), float(scale),
+                              int(bool(causal)), _ptr(o), _ptr(lse), _ptr(err))
+    if rc != 0:
+        raise ValueError("oracle_attention rejected its arguments (rc=%d)" % rc)
+    return o, lse, err
+
+
+def attention_rows(q, k, v, pairs, rows, scale=None, causal=False, lib=None):
+    """Selected output rows o[pair[t], row[t], :] (pairs index the flattened leading
+    dimensions), each computed exactly as ``attention`` computes it: (o bits (n, D),
+    lse (n,), err (n, D))."""
+    lib = lib or load()
+    qb, kb, vb = _attn_operands(q, k, v)
+    Sq, D = qb.shape[-2:]
+    Sk = kb.shape[-2]
+    BH = int(np.prod(qb.shape[:-2], dtype=np.int64))
+    if scale is None:
+        scale = 1.0 / np.sqrt(D)
+    pr = np.ascontiguousarray(pairs, dtype=np.int64)
+    rw = np.ascontiguousarray(rows, dtype=np.int64)
+    if pr.shape != rw.shape or pr.ndim != 1:
+        raise ValueError("pairs and rows must be 1-D and of one length")
+    n = pr.size
+    o = np.empty((n, D), dtype=np.uint16)
+    lse = np.empty(n, dtype=np.float64)
+    err = np.empty((n, D), dtype=np.float64)
+    rc = lib.oracle_attention_rows(BH, Sq, Sk, D, _ptr(qb), _ptr(kb), _ptr(vb), float(scale),
+                                   int(bool(causal)), n, _ptr(pr), _ptr(rw), _ptr(o), _ptr(lse),
+                                   _ptr(err))
+    if rc != 0:
+        raise ValueError("oracle_attention_rows rejected its arguments (rc=%d)" % rc)
+    return o, lse, err
 
 
 def gemm_sampled(A, B, rows, cols, bias=None, epilogue="none", lib=None) -> np.ndarray:

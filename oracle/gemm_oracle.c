@@ -1,7 +1,7 @@
 /*
  * CPU oracle for the half-precision GEMM with optional bias + erf-GELU epilogue (and the
- * tutorial's element-wise vector add, oracle_vector_add, and row-wise softmax,
- * oracle_softmax).
+ * tutorial's element-wise vector add, oracle_vector_add, row-wise softmax, oracle_softmax,
+ * and attention forward, oracle_attention).
  *
  * TEST INFRASTRUCTURE ONLY.  Nothing on the product path may include, link or call
  * this file; only the test suite, the smoke check and the benchmark's CPU-baseline
@@ -214,6 +214,106 @@ int oracle_softmax(int64_t M, int64_t N, const uint16_t *x, uint16_t *y)
         for (int64_t j = 0; j < N; ++j) s += exp(oracle_f16_to_f64(xr[j]) - m);
         for (int64_t j = 0; j < N; ++j)
             yr[j] = oracle_f64_to_f16(exp(oracle_f16_to_f64(xr[j]) - m) / s);
+    }
+    return 0;
+}
+
+/* Attention forward, the tutorial's FlashAttention (the ainovat.com page, the paragraph
+ * on the fused FlashAttention forward kernel: scores of query and key tiles, a softmax
+ * over the keys, weights applied to the value tiles, causal and non-causal, checked
+ * against PyTorch's scaled dot-product attention).  This is the plain definition the
+ * tiled kernel must reach; none of its tiling or online rescaling appears here.
+ *
+ * q: (BH, Sq, D), k and v: (BH, Sk, D), o: (BH, Sq, D), half precision, row-major, one
+ * (batch, head) pair after another.  For row i of pair b, in fp64:
+ *   keys j allowed: 0 <= j < Sk, and j <= i when causal (the upper-left aligned mask of
+ *     PyTorch's is_causal: query i sees keys 0..i);
+ *   s_j = scale * sum_{d=0}^{D-1} q[i][d] * k[j][d]      (d in increasing order)
+ *   m = max_j s_j,  p_j = exp(s_j - m),  l = sum_j p_j   (j in increasing order)
+ *   o[i][d] = fp16_rne( sum_j p_j v[j][d] / l )
+ *   lse[i]  = m + log(l)              (log of sum_j exp(s_j); may be NULL)
+ *   err[i][d] = sum_j p_j |v[j][d]| / l   (may be NULL): the scale against which an fp16
+ *     rounding of every weight shows in o, used by the tests to set their tolerance.
+ * Subtracting m changes nothing mathematically and keeps every exponent <= 0.  Sk == 0
+ * leaves the softmax undefined and is rejected (return 1). */
+static void attention_row(int64_t Sk, int64_t D, const uint16_t *qi, const uint16_t *kb,
+                          const uint16_t *vb, double scale, int64_t nkeys, double *sbuf,
+                          uint16_t *oi, double *lse_i, double *err_i)
+{
+    double m = -INFINITY;
+    for (int64_t j = 0; j < nkeys; ++j) {
+        double dot = 0.0;
+        for (int64_t d = 0; d < D; ++d)
+            dot += oracle_f16_to_f64(qi[d]) * oracle_f16_to_f64(kb[j * D + d]);
+        sbuf[j] = scale * dot;
+        m = fmax(m, sbuf[j]);
+    }
+    double l = 0.0;
+    for (int64_t j = 0; j < nkeys; ++j) {
+        sbuf[j] = exp(sbuf[j] - m);
+        l += sbuf[j];
+    }
+    for (int64_t d = 0; d < D; ++d) {
+        double acc = 0.0, mag = 0.0;
+        for (int64_t j = 0; j < nkeys; ++j) {
+            const double vj = oracle_f16_to_f64(vb[j * D + d]);
+            acc += sbuf[j] * vj;
+            mag += sbuf[j] * fabs(vj);
+        }
+        oi[d] = oracle_f64_to_f16(acc / l);
+        if (err_i) err_i[d] = mag / l;
+    }
+    if (lse_i) *lse_i = m + log(l);
+    (void)Sk;
+}
+
+static int64_t allowed_keys(int64_t i, int64_t Sk, int causal)
+{
+    return (causal && i + 1 < Sk) ? i + 1 : Sk;
+}
+
+int oracle_attention(int64_t BH, int64_t Sq, int64_t Sk, int64_t D, const uint16_t *q,
+                     const uint16_t *k, const uint16_t *v, double scale, int causal,
+                     uint16_t *o, double *lse, double *err)
+{
+    if (BH < 0 || Sq < 0 || Sk < 0 || D < 0) return 1;
+    if (BH == 0 || Sq == 0) return 0;
+    if (Sk == 0) return 1;
+    #pragma omp parallel
+    {
+        double *sbuf = (double *)malloc((size_t)Sk * sizeof(double));
+        #pragma omp for schedule(dynamic, 4) collapse(2)
+        for (int64_t b = 0; b < BH; ++b)
+            for (int64_t i = 0; i < Sq; ++i)
+                attention_row(Sk, D, q + (b * Sq + i) * D, k + b * Sk * D, v + b * Sk * D, scale,
+                              allowed_keys(i, Sk, causal), sbuf, o + (b * Sq + i) * D,
+                              lse ? lse + b * Sq + i : NULL, err ? err + (b * Sq + i) * D : NULL);
+        free(sbuf);
+    }
+    return 0;
+}
+
+/* The same rows one by one: n selected (pair, row) indices, outputs packed n x D (and n
+ * for lse), each computed exactly as oracle_attention computes it. */
+int oracle_attention_rows(int64_t BH, int64_t Sq, int64_t Sk, int64_t D, const uint16_t *q,
+                          const uint16_t *k, const uint16_t *v, double scale, int causal,
+                          int64_t n, const int64_t *pair, const int64_t *row, uint16_t *o,
+                          double *lse, double *err)
+{
+    if (BH < 0 || Sq < 0 || Sk <= 0 || D < 0 || n < 0) return 1;
+    for (int64_t t = 0; t < n; ++t)
+        if (pair[t] < 0 || pair[t] >= BH || row[t] < 0 || row[t] >= Sq) return 1;
+    #pragma omp parallel
+    {
+        double *sbuf = (double *)malloc((size_t)Sk * sizeof(double));
+        #pragma omp for schedule(dynamic, 1)
+        for (int64_t t = 0; t < n; ++t) {
+            const int64_t b = pair[t], i = row[t];
+            attention_row(Sk, D, q + (b * Sq + i) * D, k + b * Sk * D, v + b * Sk * D, scale,
+                          allowed_keys(i, Sk, causal), sbuf, o + t * D, lse ? lse + t : NULL,
+                          err ? err + t * D : NULL);
+        }
+        free(sbuf);
     }
     return 0;
 }

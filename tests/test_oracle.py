@@ -486,3 +486,188 @@ def test_softmax_ieee_edge_cases(oracle_lib):
     assert np.all(np.isnan(y[1])) and np.all(np.isnan(y[2])) and np.all(np.isnan(y[3]))
     assert oracle.softmax(np.zeros((0, 5), np.float16), lib=oracle_lib).shape == (0, 5)
     assert oracle.softmax(np.zeros((5, 0), np.float16), lib=oracle_lib).shape == (5, 0)
+
+
+# ---------------------------------------------------------------- attention ---------
+
+def _f16_of_fraction(fr: Fraction) -> np.float16:
+    """The fp16 value nearest to an exact rational (ties to even), found among the
+    neighbours of numpy's conversion of its nearest double."""
+    h = np.float16(float(fr))
+    cands = [h, np.nextafter(h, np.float16(np.inf)), np.nextafter(h, np.float16(-np.inf))]
+    cands = [c for c in cands if np.isfinite(c)]
+    best = min(cands, key=lambda c: (abs(Fraction(float(c)) - fr), int(c.view(np.uint16)) & 1))
+    return best
+
+
+def _qkv(rng, BH, Sq, Sk, D, scale=1.0):
+    q = (rng.standard_normal((BH, Sq, D)) * scale).astype(np.float16)
+    k = (rng.standard_normal((BH, Sk, D)) * scale).astype(np.float16)
+    v = rng.standard_normal((BH, Sk, D)).astype(np.float16)
+    return q, k, v
+
+
+def _ulps(a_bits, b_bits):
+    def ordered(b):
+        b = b.astype(np.int32)
+        return np.where(b & 0x8000, -(b & 0x7FFF), b)
+    return np.abs(ordered(a_bits) - ordered(b_bits))
+
+
+def test_attention_single_key(oracle_lib):
+    """One key: every weight is 1, so o = v[0] exactly and lse = the single score."""
+    rng = np.random.default_rng(11)
+    q, k, v = _qkv(rng, 3, 5, 1, 16)
+    for causal in (False, True):
+        o, lse, err = oracle.attention(q, k, v, scale=0.37, causal=causal, lib=oracle_lib)
+        assert np.array_equal(o, np.broadcast_to(v.view(np.uint16), o.shape))
+        assert np.array_equal(err, np.abs(np.broadcast_to(v.astype(np.float64), o.shape)))
+        for b in range(3):
+            for i in range(5):
+                dot = sum(Fraction(float(x)) * Fraction(float(y)) for x, y in zip(q[b, i], k[b, 0]))
+                assert lse[b, i] == pytest.approx(0.37 * float(dot), rel=1e-14, abs=1e-14)
+
+
+def test_attention_uniform_weights(oracle_lib):
+    """q = 0 (or scale = 0) makes every allowed weight equal: o is the exact mean of the
+    allowed value rows, rounded once, and lse = log(number of allowed keys)."""
+    rng = np.random.default_rng(12)
+    BH, Sq, Sk, D = 2, 9, 13, 4
+    _, k, v = _qkv(rng, BH, Sq, Sk, D)
+    qz = np.zeros((BH, Sq, D), np.float16)
+    qr = rng.standard_normal((BH, Sq, D)).astype(np.float16)
+    for causal in (False, True):
+        for (q, scale) in ((qz, 0.5), (qr, 0.0)):
+            o, lse, _ = oracle.attention(q, k, v, scale=scale, causal=causal, lib=oracle_lib)
+            of = o.view(np.float16)
+            for b in range(BH):
+                for i in range(Sq):
+                    n = min(i + 1, Sk) if causal else Sk
+                    assert lse[b, i] == pytest.approx(np.log(n), abs=1e-14)
+                    for d in range(D):
+                        mean = sum(Fraction(float(x)) for x in v[b, :n, d]) / n
+                        assert of[b, i, d] == _f16_of_fraction(mean), (causal, b, i, d)
+
+
+def test_attention_selection(oracle_lib):
+    """Keys are scaled one-hot rows along a permutation sigma of the head dimensions and
+    query i points at key pi(i): with a large scale the softmax is one-hot within far less
+    than fp16's resolution, so o[i] = v[pi(i)] exactly (a transposed k or v, a swapped
+    operand or a wrong row picks another value row)."""
+    rng = np.random.default_rng(13)
+    Sk = D = 16
+    sigma = rng.permutation(D)
+    k = np.zeros((1, Sk, D), np.float16)
+    k[0, np.arange(Sk), sigma] = 4.0
+    v = rng.standard_normal((1, Sk, D)).astype(np.float16)
+    pi = rng.permutation(Sk)[:12]
+    q = np.zeros((1, 12, D), np.float16)
+    q[0, np.arange(12), sigma[pi]] = 8.0
+    o, _, _ = oracle.attention(q, k, v, scale=2.0, causal=False, lib=oracle_lib)
+    assert np.array_equal(o[0], v[0, pi].view(np.uint16))
+    # causal: query i selects key i (on the diagonal, always visible)
+    qd = np.zeros((1, Sk, D), np.float16)
+    qd[0, np.arange(Sk), sigma] = 8.0
+    o, _, _ = oracle.attention(qd, k, v, scale=2.0, causal=True, lib=oracle_lib)
+    assert np.array_equal(o[0], v[0].view(np.uint16))
+
+
+def test_attention_two_keys_logistic(oracle_lib):
+    """Two keys: the weights are the logistic function of the score difference, o =
+    v0 expit(s0 - s1) + v1 expit(s1 - s0) and lse = logaddexp(s0, s1)."""
+    from scipy.special import expit
+    rng = np.random.default_rng(14)
+    n = 300
+    x = rng.standard_normal((1, n, 1)).astype(np.float16)
+    k = np.array([[[1.0], [0.0]]], np.float16)
+    v = rng.standard_normal((1, 2, 1)).astype(np.float16)
+    scale = 1.7
+    o, lse, _ = oracle.attention(x, k, v, scale=scale, causal=False, lib=oracle_lib)
+    s0 = scale * x[0, :, 0].astype(np.float64)
+    v0, v1 = float(v[0, 0, 0]), float(v[0, 1, 0])
+    ref = (v0 * expit(s0) + v1 * expit(-s0)).astype(np.float16).view(np.uint16)
+    d = _ulps(o[0, :, 0], ref)
+    assert d.max() <= 1 and (d == 0).mean() >= 0.99
+    assert np.allclose(lse[0], np.logaddexp(s0, 0.0), rtol=0, atol=1e-13)
+
+
+def _scipy_attention(q, k, v, scale, causal):
+    from scipy.special import logsumexp, softmax
+    s = scale * np.matmul(q.astype(np.float64), np.swapaxes(k.astype(np.float64), -1, -2))
+    if causal:
+        Sq, Sk = s.shape[-2:]
+        s = np.where(np.tril(np.ones((Sq, Sk), bool)), s, -np.inf)
+    p = softmax(s, axis=-1)
+    return p @ v.astype(np.float64), logsumexp(s, axis=-1), p @ np.abs(v.astype(np.float64))
+
+
+@pytest.mark.parametrize("BH,Sq,Sk,D,causal", [
+    (2, 17, 17, 16, False), (2, 17, 17, 16, True), (3, 40, 23, 8, True),
+    (1, 23, 40, 32, True), (2, 64, 96, 64, False), (1, 5, 200, 128, True)])
+def test_attention_matches_scipy(oracle_lib, BH, Sq, Sk, D, causal):
+    """scipy's softmax and numpy's fp64 matmul (an independent formulation): o within one
+    fp16 step and almost always equal, lse and err to fp64 accuracy."""
+    rng = np.random.default_rng(BH * 1000 + Sq * 10 + Sk)
+    q, k, v = _qkv(rng, BH, Sq, Sk, D, scale=1.5)
+    scale = 1.0 / np.sqrt(D)
+    o, lse, err = oracle.attention(q, k, v, scale=scale, causal=causal, lib=oracle_lib)
+    ro, rl, re = _scipy_attention(q, k, v, scale, causal)
+    d = _ulps(o, ro.astype(np.float16).view(np.uint16))
+    assert d.max() <= 1 and (d == 0).mean() >= 0.995
+    assert np.allclose(lse, rl, rtol=0, atol=1e-12)
+    assert np.allclose(err, re, rtol=1e-12, atol=1e-15)
+
+
+def test_attention_causal_is_the_prefix(oracle_lib):
+    """Causal row i is the non-causal attention of query i over keys 0..i only."""
+    rng = np.random.default_rng(15)
+    q, k, v = _qkv(rng, 2, 12, 12, 8)
+    o, lse, err = oracle.attention(q, k, v, scale=0.4, causal=True, lib=oracle_lib)
+    for i in range(12):
+        oi, li, ei = oracle.attention(q[:, i:i + 1], k[:, :i + 1], v[:, :i + 1], scale=0.4,
+                                      causal=False, lib=oracle_lib)
+        assert np.array_equal(o[:, i], oi[:, 0]) and np.array_equal(lse[:, i], li[:, 0])
+        assert np.array_equal(err[:, i], ei[:, 0])
+
+
+def test_attention_shift_invariance_without_overflow(oracle_lib):
+    """A score offset common to every key of a row (an extra head dimension where every
+    key holds 1 and the query holds 1000) leaves o unchanged and moves lse by exactly the
+    offset; without the row-maximum shift exp(1000) would overflow."""
+    rng = np.random.default_rng(16)
+    q, k, v = _qkv(rng, 2, 10, 30, 7)
+    o, lse, _ = oracle.attention(q, k, v, scale=1.0, causal=False, lib=oracle_lib)
+    q2 = np.concatenate([q, np.full((2, 10, 1), 1000.0, np.float16)], axis=-1)
+    k2 = np.concatenate([k, np.ones((2, 30, 1), np.float16)], axis=-1)
+    v2 = np.concatenate([v, np.zeros((2, 30, 1), np.float16)], axis=-1)
+    o2, lse2, _ = oracle.attention(q2, k2, v2, scale=1.0, causal=False, lib=oracle_lib)
+    d = _ulps(o2[..., :7], o)
+    assert d.max() <= 1 and (d == 0).mean() >= 0.99
+    assert np.allclose(lse2 - 1000.0, lse, rtol=0, atol=1e-9)
+
+
+def test_attention_convex_hull(oracle_lib):
+    """Every output is a weighted mean of the allowed values: within their min and max."""
+    rng = np.random.default_rng(17)
+    q, k, v = _qkv(rng, 3, 33, 33, 16, scale=2.0)
+    for causal in (False, True):
+        o, _, _ = oracle.attention(q, k, v, scale=0.25, causal=causal, lib=oracle_lib)
+        of = o.view(np.float16)
+        for i in range(33):
+            n = i + 1 if causal else 33
+            assert np.all(of[:, i] >= v[:, :n].min(axis=1)) and np.all(of[:, i] <= v[:, :n].max(axis=1))
+
+
+def test_attention_rows_and_edges(oracle_lib):
+    rng = np.random.default_rng(18)
+    q, k, v = _qkv(rng, 4, 21, 19, 8)
+    o, lse, err = oracle.attention(q, k, v, causal=True, lib=oracle_lib)
+    pairs = np.array([0, 3, 2, 1, 3]); rows = np.array([0, 20, 7, 18, 19])
+    ro, rl, re = oracle.attention_rows(q, k, v, pairs, rows, causal=True, lib=oracle_lib)
+    assert np.array_equal(ro, o[pairs, rows]) and np.array_equal(rl, lse[pairs, rows])
+    assert np.array_equal(re, err[pairs, rows])
+    with pytest.raises(ValueError):
+        oracle.attention(q, k[:, :0], v[:, :0], lib=oracle_lib)   # no keys: undefined
+    assert oracle.attention(q[:, :0], k, v, lib=oracle_lib)[0].shape == (4, 0, 8)
+    with pytest.raises(ValueError):
+        oracle.attention_rows(q, k, v, [4], [0], lib=oracle_lib)

@@ -49,6 +49,17 @@ MUTANTS = [
                                "oracle_f16_to_f64(a[i]) - oracle_f16_to_f64(b[i])")]),
     ("vector_add_drops_b", [("oracle_f16_to_f64(a[i]) + oracle_f16_to_f64(b[i])",
                              "oracle_f16_to_f64(a[i]) + 0.0 * oracle_f16_to_f64(b[i])")]),
+    ("attn_causal_strict", [("return (causal && i + 1 < Sk) ? i + 1 : Sk;",
+                             "return (causal && i < Sk) ? i : Sk;")]),
+    ("attn_causal_ignored", [("return (causal && i + 1 < Sk) ? i + 1 : Sk;", "return Sk;")]),
+    ("attn_no_scale", [("sbuf[j] = scale * dot;", "sbuf[j] = dot;")]),
+    ("attn_transposed_k", [("oracle_f16_to_f64(kb[j * D + d])", "oracle_f16_to_f64(kb[d * nkeys + j])")]),
+    ("attn_transposed_v", [("oracle_f16_to_f64(vb[j * D + d])", "oracle_f16_to_f64(vb[d * nkeys + j])")]),
+    ("attn_not_normalised", [("oi[d] = oracle_f64_to_f16(acc / l);", "oi[d] = oracle_f64_to_f16(acc);")]),
+    ("attn_lse_no_log", [("*lse_i = m + log(l);", "*lse_i = m + l;")]),
+    ("attn_no_max_shift", [("sbuf[j] = exp(sbuf[j] - m);", "sbuf[j] = exp(sbuf[j]);")]),
+    ("attn_kv_of_pair_zero", [("k + b * Sk * D, v + b * Sk * D, scale,\n                              allowed_keys",
+                               "k, v, scale,\n                              allowed_keys")]),
     ("vector_add_float_sum", [("oracle_f16_to_f64(a[i]) + oracle_f16_to_f64(b[i])",
                                "(double)(float)(oracle_f16_to_f64(a[i]) + oracle_f16_to_f64(b[i]) * 1.0000001)")]),
 ]
