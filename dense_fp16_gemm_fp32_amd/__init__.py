@@ -29,6 +29,7 @@ EXPORTS = (
     "mi355gemm_gemm", "mi355gemm_gemm_config", "mi355gemm_select", "mi355gemm_num_configs",
     "mi355gemm_config_name", "mi355gemm_config_info", "mi355gemm_lds_budget",
     "mi355gemm_last_error", "mi355gemm_version", "mi355gemm_vector_add", "mi355gemm_softmax",
+    "mi355gemm_attention",
 )
 
 
@@ -80,6 +81,9 @@ def library() -> ctypes.CDLL:
         lib.mi355gemm_vector_add.restype = ci
         lib.mi355gemm_softmax.argtypes = [i64, i64, p, p, p]
         lib.mi355gemm_softmax.restype = ci
+        lib.mi355gemm_attention.argtypes = [i64, i64, i64, i64, i64, p, p, p, p, p,
+                                            ctypes.c_float, ci, p]
+        lib.mi355gemm_attention.restype = ci
         lib.mi355gemm_version.argtypes = []
         lib.mi355gemm_version.restype = ctypes.c_char_p
         _lib = lib
@@ -279,6 +283,57 @@ def softmax(x: torch.Tensor, out: torch.Tensor | None = None,
     else:
         with torch.cuda.device(idx):
             st = lib.mi355gemm_softmax(M, N, x.data_ptr(), out.data_ptr(), sptr)
+    if st != OK:
+        raise GemmError(st, mi355gemm_last_error())
+    return out
+
+
+def mi355gemm_attention(batch, heads, seq_q, seq_k, head_dim, q, k, v, o, lse, scale, causal,
+                        stream) -> int:
+    return library().mi355gemm_attention(batch, heads, seq_q, seq_k, head_dim, q, k, v, o, lse,
+                                         scale, causal, stream)
+
+
+def attention(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, causal: bool = False,
+              scale: float | None = None, out: torch.Tensor | None = None,
+              lse: torch.Tensor | None = None,
+              stream: torch.cuda.Stream | None = None) -> torch.Tensor:
+    """Attention forward of contiguous fp16 (batch, heads, seq, head_dim) tensors on the
+    GPU; ``scale`` defaults to 1/sqrt(head_dim).  ``lse`` (optional, fp32, (batch, heads,
+    seq_q)) receives the natural-log sum of exp of each query row's scores."""
+    for t, n in ((q, "q"), (k, "k"), (v, "v")):
+        _check_tensor(t, n, 4)
+    B, H, Sq, D = q.shape
+    Sk = k.shape[2]
+    if k.shape != (B, H, Sk, D) or v.shape != k.shape:
+        raise ValueError("k and v must be (batch, heads, seq_k, head_dim) like q; got %s %s %s"
+                         % (tuple(q.shape), tuple(k.shape), tuple(v.shape)))
+    if k.device != q.device or v.device != q.device:
+        raise ValueError("q, k and v must be on one device")
+    if out is None:
+        out = torch.empty_like(q)
+    else:
+        _check_tensor(out, "out", 4)
+        if out.shape != q.shape or out.device != q.device:
+            raise ValueError("out must be shaped like q on its device")
+    lse_ptr = None
+    if lse is not None:
+        if (lse.dtype != torch.float32 or lse.device != q.device or lse.shape != (B, H, Sq)
+                or not lse.is_contiguous()):
+            raise ValueError("lse must be a contiguous float32 (batch, heads, seq_q) tensor on q's device")
+        lse_ptr = lse.data_ptr()
+    if scale is None:
+        scale = 1.0 / float(D) ** 0.5
+    lib = _lib if _lib is not None else library()
+    idx = q.device.index if q.device.index is not None else torch.cuda.current_device()
+    sptr = stream.cuda_stream if stream is not None else _raw_stream(idx)
+    args = (B, H, Sq, Sk, D, q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse_ptr,
+            float(scale), int(bool(causal)), sptr)
+    if idx == torch.cuda.current_device():
+        st = lib.mi355gemm_attention(*args)
+    else:
+        with torch.cuda.device(idx):
+            st = lib.mi355gemm_attention(*args)
     if st != OK:
         raise GemmError(st, mi355gemm_last_error())
     return out

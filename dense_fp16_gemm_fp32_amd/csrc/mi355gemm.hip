@@ -12,6 +12,7 @@
 #include <stdio.h>
 #include <string.h>
 
+#include "attention.hpp"
 #include "gemm_direct.hpp"
 #include "gemm_staged.hpp"
 #include "softmax.hpp"
@@ -24,6 +25,9 @@ using D256k64 = DTile<256, 256, 64, 2, 4, 1, 2>;    // 8 waves of 128x64, 128 Ki
 using D256x128 = DTile<256, 128, 64, 2, 2, 2, 3>;   // 2 x 4 waves of 128x64, 144 KiB
 using D128 = DTile<128, 128, 64, 2, 2, 2, 4>;       // 2 x 4 waves of 64x64, 128 KiB
 using D128w4 = DTile<128, 128, 64, 2, 2, 1, 4>;     // 4 waves of 64x64, 128 KiB
+// attention: head dim, keys per block, waves (32 query rows each), LDS stages
+using A128 = ATile<128, 64, 8, 3>;   // 256 query rows, 96 KiB LDS
+using A64 = ATile<64, 64, 8, 3>;     // 256 query rows, 48 KiB LDS
 // register-staged tiles (any alignment)
 using T64 = Tile<64, 64, 64, 2, 1>;              // 2 waves of 32x64
 using T128 = Tile<128, 128, 64, 2, 2>;           // 4 waves of 64x64
@@ -371,6 +375,60 @@ mi355gemm_status mi355gemm_softmax(int64_t M, int64_t N, const void *x, void *y,
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess)
         return fail(MI355GEMM_EHIP, "launch of softmax failed: %s", hipGetErrorString(e));
+    return MI355GEMM_OK;
+}
+
+mi355gemm_status mi355gemm_attention(int64_t batch, int64_t heads, int64_t seq_q, int64_t seq_k,
+                                     int64_t head_dim, const void *q, const void *k,
+                                     const void *v, void *o, float *lse, float scale,
+                                     int causal, void *stream)
+{
+    g_last_error[0] = 0;
+    if (batch < 0 || heads < 0 || seq_q < 0 || seq_k < 0 || head_dim < 0)
+        return fail(MI355GEMM_EINVAL, "negative size (batch=%lld heads=%lld seq_q=%lld seq_k=%lld head_dim=%lld)",
+                    (long long)batch, (long long)heads, (long long)seq_q, (long long)seq_k,
+                    (long long)head_dim);
+    if (causal != 0 && causal != 1) return fail(MI355GEMM_EINVAL, "causal must be 0 or 1");
+    if (!(scale > 0.0f) || !(scale < __builtin_inff()))
+        return fail(MI355GEMM_EINVAL, "scale must be finite and positive");
+    if (head_dim != 64 && head_dim != 128)
+        return fail(MI355GEMM_EUNSUPPORTED, "head_dim %lld (64 or 128 are served)", (long long)head_dim);
+    if (batch == 0 || heads == 0 || seq_q == 0) return MI355GEMM_OK;
+    if (seq_k == 0) return fail(MI355GEMM_EINVAL, "seq_k == 0: the softmax over no keys is undefined");
+    if (q == nullptr || k == nullptr || v == nullptr || o == nullptr)
+        return fail(MI355GEMM_EINVAL, "q, k, v and o must not be NULL");
+    if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16))
+        return fail(MI355GEMM_EINVAL, "q, k, v and o must be 16-byte aligned");
+    if (lse != nullptr && !aligned(lse, 4)) return fail(MI355GEMM_EINVAL, "lse must be 4-byte aligned");
+    const int64_t lim = (int64_t)1 << 31;
+    if (batch >= lim || heads >= lim || batch * heads >= lim ||
+        (seq_q + 1024) * head_dim * 2 >= lim || (seq_k + 1024) * head_dim * 2 >= lim)
+        return fail(MI355GEMM_EUNSUPPORTED, "sizes past the kernel's 32-bit offsets");
+    constexpr int BM = A128::BM;
+    static_assert(A64::BM == BM && A64::NT == A128::NT, "one launch shape for both head dims");
+    const int64_t q_blocks = (seq_q + BM - 1) / BM;
+    if (batch * heads * q_blocks >= lim) return fail(MI355GEMM_EUNSUPPORTED, "grid too large");
+    AttnArgs a;
+    a.q = static_cast<const f16 *>(q);
+    a.k = static_cast<const f16 *>(k);
+    a.v = static_cast<const f16 *>(v);
+    a.o = static_cast<f16 *>(o);
+    a.lse = lse;
+    a.pairs = (int)(batch * heads);
+    a.Sq = (int)seq_q;
+    a.Sk = (int)seq_k;
+    a.q_blocks = (int)q_blocks;
+    a.c = scale * 1.4426950408889634f;
+    a.causal = causal;
+    const dim3 grid((unsigned)(batch * heads * q_blocks));
+    const hipStream_t st = static_cast<hipStream_t>(stream);
+    if (head_dim == 128)
+        hipLaunchKernelGGL(attention_fwd<A128>, grid, dim3(A128::NT), 0, st, a);
+    else
+        hipLaunchKernelGGL(attention_fwd<A64>, grid, dim3(A64::NT), 0, st, a);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess)
+        return fail(MI355GEMM_EHIP, "launch of attention failed: %s", hipGetErrorString(e));
     return MI355GEMM_OK;
 }
 

@@ -137,6 +137,44 @@ mi355gemm_status mi355gemm_vector_add(int64_t n, const void *a, const void *b, v
  */
 mi355gemm_status mi355gemm_softmax(int64_t M, int64_t N, const void *x, void *y, void *stream);
 
+/*
+ * Attention forward (the tutorial's FlashAttention: "Designing High-Performance GPU
+ * Kernels with TileLang: ...", ainovat.com page, the FlashAttention paragraph -- query,
+ * key and value tiles, an online softmax with running maxima, sums and rescaling, tiled
+ * tensor-core products, the score matrix never written to memory; causal and non-causal).
+ * For every (batch, head) pair and query row i:
+ *   s_j = scale * sum_d q[i][d] k[j][d]   for the allowed keys j: all 0 <= j < seq_k, or,
+ *         when causal, j <= i (the upper-left aligned mask of PyTorch's is_causal);
+ *   o[i][d] = sum_j exp(s_j - m) v[j][d] / sum_j exp(s_j - m),  m = max_j s_j;
+ *   lse[i] = m + log sum_j exp(s_j - m)  (natural log).
+ * fp32 arithmetic; the softmax weights are rounded to fp16 for the product with v, and o
+ * is rounded to fp16 once.
+ *
+ * batch, heads      >= 0; the pairs (b, h) are laid out one after another.
+ * seq_q, seq_k      query and key/value lengths (>= 0; seq_k >= 1 when there is work).
+ * head_dim          64 or 128.
+ * q                 device pointer, batch x heads x seq_q x head_dim fp16 (read).
+ * k, v              device pointers, batch x heads x seq_k x head_dim fp16 (read).
+ * o                 device pointer, batch x heads x seq_q x head_dim fp16 (written); must
+ *                   not overlap q, k or v.
+ * lse               device pointer to batch x heads x seq_q fp32 (written), or NULL.
+ * scale             the score scale (finite, > 0; 1/sqrt(head_dim) is the usual one).
+ * causal            0 or 1.
+ * stream            hipStream_t to enqueue on; NULL is the default stream.
+ *
+ * The caller owns every buffer; the call allocates nothing and returns after the
+ * enqueue.  batch * heads == 0 or seq_q == 0 does nothing and returns OK.  Errors:
+ * EINVAL for negative sizes, seq_k == 0 with work to do (the softmax over no keys is
+ * undefined), a scale that is not finite and positive, NULL or misaligned pointers (q, k,
+ * v, o need 16-byte alignment, lse 4-byte); EUNSUPPORTED for another head_dim or sizes
+ * past the 32-bit offsets the kernel uses ((seq + 1024) * head_dim * 2 bytes must stay
+ * below 2^31 per pair); EHIP if the launch fails.
+ */
+mi355gemm_status mi355gemm_attention(int64_t batch, int64_t heads, int64_t seq_q, int64_t seq_k,
+                                     int64_t head_dim, const void *q, const void *k,
+                                     const void *v, void *o, float *lse, float scale,
+                                     int causal, void *stream);
+
 /* Description of one compiled kernel configuration. */
 typedef struct {
     int block_m, block_n, block_k;  /* macro-tile of C per workgroup and K step */

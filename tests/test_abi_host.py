@@ -30,7 +30,7 @@ def header_functions():
 
 def test_library_exports_every_declared_symbol():
     declared = header_functions()
-    assert len(declared) == 11
+    assert len(declared) == 12
     assert sorted(g.EXPORTS) == declared
     lib = g.library()
     for name in declared:
@@ -254,3 +254,35 @@ def test_softmax_argument_checks(args, want):
     a.update(args)
     # every case here fails validation or has nothing to do, so nothing is launched
     assert g.mi355gemm_softmax(a["M"], a["N"], a["x"], a["y"], None) == want
+
+
+@pytest.mark.parametrize("args,want", [
+    (dict(B=-1), g.EINVAL),
+    (dict(Sk=-1), g.EINVAL),
+    (dict(D=96), g.EUNSUPPORTED),
+    (dict(D=256), g.EUNSUPPORTED),
+    (dict(B=0, q=None, k=None, v=None, o=None), g.OK),
+    (dict(H=0), g.OK),
+    (dict(Sq=0, q=None), g.OK),
+    (dict(Sk=0), g.EINVAL),
+    (dict(scale=0.0), g.EINVAL),
+    (dict(scale=-0.1), g.EINVAL),
+    (dict(scale=float("inf")), g.EINVAL),
+    (dict(scale=float("nan")), g.EINVAL),
+    (dict(causal=2), g.EINVAL),
+    (dict(v=None), g.EINVAL),
+    (dict(o=P2), g.EINVAL),
+    (dict(k=P16 + 8), g.EINVAL),
+    (dict(lse=P16 + 2), g.EINVAL),
+    (dict(Sq=(1 << 23)), g.EUNSUPPORTED),
+    (dict(Sk=(1 << 23)), g.EUNSUPPORTED),
+    (dict(B=1 << 16, H=1 << 15), g.EUNSUPPORTED),
+])
+def test_attention_argument_checks(args, want):
+    a = dict(B=2, H=3, Sq=64, Sk=64, D=128, q=P16, k=P16, v=P16, o=P16, lse=None,
+             scale=0.125, causal=0)
+    a.update(args)
+    # every case here fails validation or has nothing to do, so nothing is launched
+    st = g.mi355gemm_attention(a["B"], a["H"], a["Sq"], a["Sk"], a["D"], a["q"], a["k"], a["v"],
+                               a["o"], a["lse"], a["scale"], a["causal"], None)
+    assert st == want, g.mi355gemm_last_error()
