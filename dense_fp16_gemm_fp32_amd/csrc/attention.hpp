@@ -18,11 +18,15 @@
 //   S^T = K Q^T   with v_mfma_f32_32x32x16_f16, K as the first operand, so lane l holds
 //                 the scores of query row l % 32 for 16 of the 32 keys of each 32-key
 //                 block (its partner lane l ^ 32 holds the other 16);
-//   the online softmax in registers (base 2: exp(x) = 2^(x log2 e), scale folded in):
-//                 m' = max(m, rowmax(S) c), alpha = 2^(m - m'), P = 2^(S c - m'),
-//                 l = l alpha + rowsum(P), O = O alpha  (c = scale * log2 e); the row
-//                 maximum needs one exchange with the partner lane, the sum none (each
-//                 lane keeps its partial sum, added at the end);
+//   the online softmax in registers (base 2: exp(x) = 2^(x log2 e), scale folded in,
+//                 c = scale * log2 e): P = 2^(S c - m), l = l + rowsum(P), O = O + P V
+//                 against a reference m per row.  Any m gives the same o = O / l as long
+//                 as O and l share it; m is raised (O and l scaled by 2^(m - m')) only
+//                 when some row of the wave sees a block maximum more than 8 above it, so
+//                 weights stay at most 2^8 (exact range for fp16 and fp32) and the
+//                 rescale of O is skipped for most blocks.  The row maximum needs one
+//                 exchange with the partner lane, the sum none (each lane keeps its
+//                 partial sum, added at the end);
 //   O^T += V^T P^T  with V as the first operand read by ds_read_b64_tr_b16 (the
 //                 transposing LDS read) and P^T straight from the score registers: the
 //                 keys a lane holds define the order of the contraction, and the V
@@ -95,6 +99,7 @@ __global__ void __launch_bounds__(T::NT) attention_fwd(AttnArgs p)
     __shared__ __attribute__((aligned(16))) char lds[T::LDS_BYTES];
     constexpr int D = T::D, BN = T::BN, CH = T::CH;
     constexpr float kNegInf = -__builtin_inff();
+    constexpr float kRescaleLog2 = 8.0f;   // weights stay below 2^8 between rescales
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -213,14 +218,16 @@ __global__ void __launch_bounds__(T::NT) attention_fwd(AttnArgs p)
                 s[nb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(kf, qf[kk], s[nb], 0, 0, 0);
             }
 
-        // register r of s[nb] is key kv0 + 32 nb + 8 (r / 4) + 4 h + r % 4 of query row qi
+        // register r of s[nb] is key kv0 + 4 h + off(nb, r), off = 32 nb + 8 (r / 4) + r % 4,
+        // of query row qi; keys from kv0 + 4 h + lim on are past Sk or, when causal, past qi
         if (kv0 + BN > p.Sk || (p.causal && kv0 + BN - 1 > qw)) {
+            const int lim = (p.causal ? min(p.Sk, qi + 1) : p.Sk) - kv0 - 4 * h;
 #pragma unroll
             for (int nb = 0; nb < T::NB; ++nb)
 #pragma unroll
                 for (int r = 0; r < 16; ++r) {
-                    const int key = kv0 + 32 * nb + 8 * (r >> 2) + 4 * h + (r & 3);
-                    if (key >= p.Sk || (p.causal && key > qi)) s[nb][r] = kNegInf;
+                    const int off = 32 * nb + 8 * (r >> 2) + (r & 3);
+                    s[nb][r] = (off >= lim) ? kNegInf : s[nb][r];
                 }
         }
 
@@ -231,24 +238,32 @@ __global__ void __launch_bounds__(T::NT) attention_fwd(AttnArgs p)
 #pragma unroll
             for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[nb][r]);
         mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-        const float m_new = fmaxf(m_run, mx * p.c);   // finite: key 0 is in every row's first block
-        const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
-        m_run = m_new;
+        // raise the reference when a row's maximum passes it by more than 2^8 (always in
+        // the first block, where it is -inf; key 0 makes every row's first maximum finite)
+        float alpha = 1.0f;
+        const bool resc = __any(mx * p.c > m_run + kRescaleLog2);
+        if (resc) {
+            const float m_new = fmaxf(m_run, mx * p.c);
+            alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+            m_run = m_new;
+        }
         float rs = 0.0f;
         f16x8 pf[T::U];
 #pragma unroll
         for (int nb = 0; nb < T::NB; ++nb)
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
-                const float e = __builtin_amdgcn_exp2f(fmaf(s[nb][r], p.c, -m_new));
+                const float e = __builtin_amdgcn_exp2f(fmaf(s[nb][r], p.c, -m_run));
                 rs += e;
                 pf[2 * nb + (r >> 3)][r & 7] = (f16)e;
             }
-        l_run = fmaf(l_run, alpha, rs);
+        if (resc) {
+            l_run *= alpha;
 #pragma unroll
-        for (int db = 0; db < T::DB; ++db)
+            for (int db = 0; db < T::DB; ++db)
 #pragma unroll
-            for (int r = 0; r < 16; ++r) o[db][r] *= alpha;
+                for (int r = 0; r < 16; ++r) o[db][r] *= alpha;
+        }
 
         // O^T += V^T P^T
 #pragma unroll
@@ -263,6 +278,7 @@ __global__ void __launch_bounds__(T::NT) attention_fwd(AttnArgs p)
                 const f16x8 vf = __builtin_bit_cast(f16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
                 o[db] = __builtin_amdgcn_mfma_f32_32x32x16_f16(vf, pf[u], o[db], 0, 0, 0);
             }
+        l_run += rs;
     };
 
     for (int jb = 0; jb < n_kv; jb += T::STAGES) {

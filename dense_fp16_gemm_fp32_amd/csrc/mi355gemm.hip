@@ -26,8 +26,8 @@ using D256x128 = DTile<256, 128, 64, 2, 2, 2, 3>;   // 2 x 4 waves of 128x64, 14
 using D128 = DTile<128, 128, 64, 2, 2, 2, 4>;       // 2 x 4 waves of 64x64, 128 KiB
 using D128w4 = DTile<128, 128, 64, 2, 2, 1, 4>;     // 4 waves of 64x64, 128 KiB
 // attention: head dim, keys per block, waves (32 query rows each), LDS stages
-using A128 = ATile<128, 64, 8, 3>;   // 256 query rows, 96 KiB LDS
-using A64 = ATile<64, 64, 8, 3>;     // 256 query rows, 48 KiB LDS
+using A128 = ATile<128, 128, 8, 2>;  // 256 query rows, 128-key blocks, 128 KiB LDS
+using A64 = ATile<64, 64, 8, 3>;     // 256 query rows, 64-key blocks, 48 KiB LDS
 // register-staged tiles (any alignment)
 using T64 = Tile<64, 64, 64, 2, 1>;              // 2 waves of 32x64
 using T128 = Tile<128, 128, 64, 2, 2>;           // 4 waves of 64x64
