@@ -205,6 +205,53 @@ def run_softmax(lib, M, N, steps, warmup):
     return out
 
 
+def attention_flops(B, H, Sq, Sk, D, causal):
+    """4 D flops (two products) per query-key pair the mask allows; causal allows
+    min(i + 1, Sk) keys to query i (upper-left aligned)."""
+    if causal:
+        n = min(Sq, Sk)
+        pairs = n * (n + 1) // 2 + max(0, Sq - Sk) * Sk
+    else:
+        pairs = Sq * Sk
+    return 4.0 * B * H * D * pairs
+
+
+def run_attention(lib, B, H, S, D, causal, steps, warmup):
+    """The tutorial's FlashAttention forward on (B, H, S, D) fp16 tensors, N(0,1) seed 0,
+    scale 1/sqrt(D); torch's scaled_dot_product_attention on the same tensors is timed
+    beside it as context."""
+    import torch
+    import torch.nn.functional as F
+    gen = torch.Generator(device="cpu")
+    gen.manual_seed(0)
+    q, k, v = (torch.randn((B, H, S, D), generator=gen).to(torch.float16).to("cuda:0")
+               for _ in range(3))
+    o = torch.empty_like(q)
+    stream = torch.cuda.current_stream()
+    flops = attention_flops(B, H, S, S, D, causal)
+    out = {"workload": "attention", "batch": B, "heads": H, "seq": S, "head_dim": D,
+           "causal": causal, "flops": flops}
+    for name, fn in (("mi355gemm", lambda: lib.attention(q, k, v, causal=causal, out=o)),
+                     ("torch_sdpa", lambda: F.scaled_dot_product_attention(q, k, v, is_causal=causal))):
+        for _ in range(warmup):
+            fn()
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(steps):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / steps
+        tf = flops / (ms * 1e-3) / 1e12
+        if name == "mi355gemm":
+            out.update({"us": ms * 1e3, "tflops": tf, "frac_of_fp16_peak": tf / PEAK_FP16_TFLOPS})
+        else:
+            out.update({"torch_sdpa_us": ms * 1e3, "torch_sdpa_tflops": tf})
+    return out
+
+
 def calibrate_copy(reps=5, mib=256):
     """A plain device-to-device copy of known size (mib MiB read, mib MiB written), for
     scaling rocprofv3's FETCH_SIZE / WRITE_SIZE counters."""
@@ -288,6 +335,15 @@ def main():
                   % (M, N, r["us"], r["GBps"], r["torch_GBps"]), file=sys.stderr, flush=True)
             softmax.append(r)
 
+    attention = []
+    if not args.no_extra:
+        for (D, causal) in ((128, False), (128, True), (64, False), (64, True)):
+            r = run_attention(lib, 4, 32, 4096, D, causal, 20, 3)
+            print("bench: attention 4x32x4096 d%d %s %.1f us %.1f TFLOP/s (torch sdpa %.1f TFLOP/s)"
+                  % (D, "causal" if causal else "full", r["us"], r["tflops"], r["torch_sdpa_tflops"]),
+                  file=sys.stderr, flush=True)
+            attention.append(r)
+
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(w, epi, args.cpu_seconds)
@@ -321,6 +377,7 @@ def main():
         "cpu_baseline": cpu,
         "memory_roofline": vadd,
         "softmax": softmax,
+        "attention": attention,
         "device": {"name": props.name, "arch": getattr(props, "gcnArchName", None),
                    "cus": props.multi_processor_count},
         "workloads": extra,

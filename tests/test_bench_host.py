@@ -1,0 +1,32 @@
+"""Host checks of the benchmark's bookkeeping (CPU only)."""
+from __future__ import annotations
+
+import os
+import sys
+
+import numpy as np
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+import bench  # noqa: E402
+
+
+@pytest.mark.parametrize("Sq,Sk", [(1, 1), (4, 4), (5, 3), (3, 5), (17, 40), (256, 256)])
+def test_attention_flops_count_the_allowed_pairs(Sq, Sk):
+    """4 D flops per allowed (query, key) pair; the causal mask (key j <= query i) counted
+    by brute force."""
+    B, H, D = 2, 3, 64
+    allowed = np.tril(np.ones((Sq, Sk), dtype=np.int64)).sum()
+    assert bench.attention_flops(B, H, Sq, Sk, D, True) == 4.0 * B * H * D * allowed
+    assert bench.attention_flops(B, H, Sq, Sk, D, False) == 4.0 * B * H * D * Sq * Sk
+
+
+def test_gpus_above_one_exit_with_a_message(capsys, monkeypatch):
+    monkeypatch.setattr(sys, "argv", ["bench.py", "--gpus", "2"])
+    with pytest.raises(SystemExit) as e:
+        bench.main()
+    assert e.value.code != 0
+    assert "one GPU" in capsys.readouterr().err
