@@ -74,6 +74,8 @@ def parse():
     ap.add_argument("--config", default=None, help="force a kernel configuration by name")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extra", action="store_true")
+    ap.add_argument("--gemm-only", action="store_true",
+                    help="extra GEMM workloads only (no vector add, softmax, attention, cold run)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run a 256 MiB device copy (counter calibration for rocprofv3)")
@@ -87,7 +89,8 @@ def time_gemm(lib, A, B, bias, epi, out, steps, warmup, config=None):
     calls, and device events at both ends of the same region on the launch stream.
     Pass 2 (the kernel time): an event pair around every single launch on the launch
     stream; the mean pair time is the kernel's average duration, which the roofline uses.
-    Returns (ms per step by wall clock, ms per step by events, mean ms per launch)."""
+    Returns (ms per step by wall clock, ms per step by events, mean, median and minimum
+    ms per launch)."""
     import torch
     stream = torch.cuda.current_stream()
     for _ in range(warmup):
@@ -112,8 +115,102 @@ def time_gemm(lib, A, B, bias, epi, out, steps, warmup, config=None):
         lib.gemm(A, B, bias, epi, out=out, config=config)
         b.record(stream)
     torch.cuda.synchronize()
-    kernel_ms = sum(a.elapsed_time(b) for a, b in pairs) / steps
-    return wall_ms, event_ms, kernel_ms
+    per = sorted(a.elapsed_time(b) for a, b in pairs)
+    kernel_ms = sum(per) / steps
+    return wall_ms, event_ms, kernel_ms, per[len(per) // 2], per[0]
+
+
+def _sha16(t) -> str:
+    import hashlib
+    return hashlib.sha256(t.contiguous().view(-1).view(dtype=__import__("torch").int16).numpy().tobytes()).hexdigest()[:16]
+
+
+def inputs_sha256(w, epi) -> dict:
+    """sha256 (first 16 hex digits) of the fp16 bytes of every input of the workload."""
+    import workloads
+    A, B, bias = workloads.make_inputs(w.M, w.N, w.K, w.dist, with_bias=(epi != "none"), seed=w.seed)
+    out = {"A": _sha16(A), "B": _sha16(B)}
+    if bias is not None:
+        out["bias"] = _sha16(bias)
+    return out
+
+
+def run_cold(lib, w, steps, min_bytes=256 << 20):
+    """The workload with cold caches: enough copies of A and B (more than min_bytes in
+    all, past the L2s and the Infinity Cache) that each call reads operands the previous
+    calls did not touch; per-launch event pairs, mean and median."""
+    import torch
+    import workloads
+    A, B, _ = workloads.make_inputs(w.M, w.N, w.K, w.dist, with_bias=False, seed=w.seed)
+    per_copy = 2 * (A.numel() + B.numel())
+    n = max(2, -(-min_bytes // per_copy) + 1)
+    As = [A.to("cuda:0") for _ in range(n)]
+    Bs = [B.to("cuda:0") for _ in range(n)]
+    out = torch.empty((w.M, w.N), dtype=torch.float16, device="cuda:0")
+    stream = torch.cuda.current_stream()
+    for i in range(n):
+        lib.gemm(As[i], Bs[i], out=out)
+    torch.cuda.synchronize()
+    pairs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+             for _ in range(steps)]
+    for i, (a, b) in enumerate(pairs):
+        a.record(stream)
+        lib.gemm(As[i % n], Bs[i % n], out=out)
+        b.record(stream)
+    torch.cuda.synchronize()
+    per = sorted(a.elapsed_time(b) for a, b in pairs)
+    mean = sum(per) / len(per)
+    return {"workload": w.name + "_cold", "copies": n, "bytes_rotated": n * per_copy,
+            "kernel_us": mean * 1e3, "kernel_median_us": per[len(per) // 2] * 1e3,
+            "tflops": w.flops / (mean * 1e-3) / 1e12}
+
+
+def derived_peak():
+    """CUs x 4096 flop/clk x the highest engine clock the driver lists (sysfs
+    pp_dpm_sclk), next to the published 2.5 PFLOP/s; None where unreadable."""
+    import glob
+    import re
+    import torch
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    mhz = None
+    for f in glob.glob("/sys/class/drm/card*/device/pp_dpm_sclk"):
+        try:
+            vals = [int(m) for m in re.findall(r"(\d+)\s*Mhz", open(f).read(), flags=re.I)]
+        except OSError:
+            continue
+        if vals:
+            mhz = max(mhz or 0, max(vals))
+    return {"cus": cus, "max_sclk_mhz": mhz,
+            "tflops": cus * 4096 * mhz * 1e6 / 1e12 if mhz else None,
+            "published_tflops": PEAK_FP16_TFLOPS}
+
+
+def cpu_oracle_by_workload(max_gflop=20.0):
+    """The CPU oracle on every workload: the full product where it costs at most
+    max_gflop, else the first rows of A (a row block, the same per-row work) scaled to
+    GFLOP/s; plus one-thread timings of the small and the ragged workload."""
+    import oracle
+    import workloads
+    lib = oracle.load()
+    threads = oracle.num_threads(lib)
+    out = []
+    for w in workloads.WORKLOADS:
+        epi = w.epilogues[-1]
+        A, B, bias = workloads.make_inputs(w.M, w.N, w.K, w.dist, with_bias=(epi != "none"), seed=w.seed)
+        rows = w.M if w.flops <= max_gflop * 1e9 else max(1, int(max_gflop * 1e9 // (2 * w.N * w.K)))
+        runs = [(threads, "threads")]
+        if w.name in ("gemm_256", "gemm_ragged_1000x3000x777"):
+            runs.append((1, "one_thread"))
+        rec = {"workload": w.name, "epilogue": epi, "rows": rows}
+        for n, key in runs:
+            oracle.set_num_threads(n, lib)
+            t0 = time.perf_counter()
+            oracle.gemm(A[:rows].contiguous(), B, bias, epi, lib=lib)
+            el = time.perf_counter() - t0
+            rec[key] = {"threads": n, "seconds": el, "gflops": 2.0 * rows * w.N * w.K / el / 1e9}
+        oracle.set_num_threads(threads, lib)
+        out.append(rec)
+    return out
 
 
 def run_workload(lib, w, epi, steps, warmup, config=None):
@@ -125,7 +222,8 @@ def run_workload(lib, w, epi, steps, warmup, config=None):
     bias = bias.to(dev) if bias is not None else None
     out = torch.empty((w.M, w.N), dtype=torch.float16, device=dev)
     cid = lib.select(A, B, bias, epi, out=out) if config is None else lib.config_id(config)
-    wall_ms, event_ms, kernel_ms = time_gemm(lib, A, B, bias, epi, out, steps, warmup, config)
+    wall_ms, event_ms, kernel_ms, kernel_med, kernel_min = time_gemm(lib, A, B, bias, epi, out,
+                                                                     steps, warmup, config)
     tflops = w.flops / (wall_ms * 1e-3) / 1e12
     return {
         "workload": w.name, "M": w.M, "N": w.N, "K": w.K, "epilogue": epi,
@@ -134,6 +232,9 @@ def run_workload(lib, w, epi, steps, warmup, config=None):
         "pct_of_peak": 100.0 * tflops / PEAK_FP16_TFLOPS,
         "event_us": event_ms * 1e3,
         "kernel_us": kernel_ms * 1e3,
+        "kernel_median_us": kernel_med * 1e3,
+        "kernel_min_us": kernel_min * 1e3,
+        "inputs_sha256_16": inputs_sha256(w, epi),
         "kernel_tflops": w.flops / (kernel_ms * 1e-3) / 1e12,
         "algorithmic_GBps": w.algorithmic_bytes(epi) / (kernel_ms * 1e-3) / 1e9,
         "steps": steps,
@@ -252,6 +353,19 @@ def run_attention(lib, B, H, S, D, causal, steps, warmup):
     return out
 
 
+def host_info():
+    cpu = None
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                cpu = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    return {"cpu_model": cpu, "affinity_cpus": len(os.sched_getaffinity(0)),
+            "omp_num_threads": os.environ.get("OMP_NUM_THREADS")}
+
+
 def calibrate_copy(reps=5, mib=256):
     """A plain device-to-device copy of known size (mib MiB read, mib MiB written), for
     scaling rocprofv3's FETCH_SIZE / WRITE_SIZE counters."""
@@ -314,21 +428,22 @@ def main():
             for e in ew.epilogues:
                 if ew.name == w.name and e == epi:
                     continue
-                steps = 50 if ew.M >= 8192 else 300
+                steps = 20 if ew.M >= 8192 else (1000 if ew.M <= 256 else 200)
                 r = run_workload(lib, ew, e, steps, 10)
                 print("bench: %s %s %.2f us/step, kernel %.2f us, %.1f TFLOP/s"
                       % (ew.name, e, r["us"], r["kernel_us"], r["tflops"]),
                       file=sys.stderr, flush=True)
                 extra.append(r)
 
+    others = not args.no_extra and not args.gemm_only
     vadd = None
-    if not args.no_extra:
+    if others:
         vadd = run_vector_add(lib, 1 << 28, 50, 5)
         print("bench: vector_add n=2^28 %.2f us %.1f GB/s (torch %.1f GB/s)"
               % (vadd["us"], vadd["GBps"], vadd["torch_GBps"]), file=sys.stderr, flush=True)
 
     softmax = []
-    if not args.no_extra:
+    if others:
         for (M, N) in ((8192, 8192), (4096, 4096), (64, 65536)):
             r = run_softmax(lib, M, N, 100, 5)
             print("bench: softmax %dx%d %.2f us %.1f GB/s (torch %.1f GB/s)"
@@ -336,7 +451,7 @@ def main():
             softmax.append(r)
 
     attention = []
-    if not args.no_extra:
+    if others:
         for (D, causal) in ((128, False), (128, True), (64, False), (64, True)):
             r = run_attention(lib, 4, 32, 4096, D, causal, 20, 3)
             print("bench: attention 4x32x4096 d%d %s %.1f us %.1f TFLOP/s (torch sdpa %.1f TFLOP/s)"
@@ -344,9 +459,19 @@ def main():
                   file=sys.stderr, flush=True)
             attention.append(r)
 
+    cold = None
+    if others:
+        cold = run_cold(lib, w, 200)
+        print("bench: %s %.2f us/launch over %d input copies (%.0f MiB)"
+              % (cold["workload"], cold["kernel_us"], cold["copies"], cold["bytes_rotated"] / 2**20),
+              file=sys.stderr, flush=True)
+
     cpu = None
+    cpu_all = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(w, epi, args.cpu_seconds)
+        if others:
+            cpu_all = cpu_oracle_by_workload()
 
     props = torch.cuda.get_device_properties(0)
     line = {
@@ -375,6 +500,10 @@ def main():
                      "frac": head["kernel_tflops"] / PEAK_FP16_TFLOPS,
                      "traffic": traffic_for(head["kernel_config"])},
         "cpu_baseline": cpu,
+        "cpu_oracle_by_workload": cpu_all,
+        "host": host_info(),
+        "cold": cold,
+        "peak_derived": derived_peak(),
         "memory_roofline": vadd,
         "softmax": softmax,
         "attention": attention,

@@ -464,8 +464,8 @@ __global__ void __launch_bounds__(T::NT) gemm_direct(GemmArgs p)
     // wave's next k-step and, in the first k-step, a share of the HBM -> LDS copy of stage
     // kt+STAGES-1 into the slot freed by stage kt-1.  The last k-step first waits for
     // stage kt+1's copy and crosses the barrier, then reads the next stage's fragments
-    // while its MFMAs run.  The body has no branches on data; past the end of K it copies
-    // zeros, multiplies zeros and reads fragments it never uses.
+    // while its MFMAs run.  The body has no branches on data; near the end of K it copies
+    // zeros for the stages past the end and reads fragments it never uses.
     auto stage = [&](auto Jc, int kt) {
         constexpr int J = decltype(Jc)::value;
         St &cur = ring[J];
@@ -518,11 +518,14 @@ __global__ void __launch_bounds__(T::NT) gemm_direct(GemmArgs p)
         w.read_all(ring[0], 0, 0);
 
         // ---- main loop, unrolled over the ring so every slot address is a constant.
-        // The step count is rounded up to a whole number of ring turns: the extra
-        // stages lie past the end of K, hold zeros, and add nothing to the sums.
-        const int nk_ring = (nk + T::STAGES - 1) / T::STAGES * T::STAGES;
-        for (int kt = 0; kt < nk_ring; kt += T::STAGES) {
-            static_for<T::STAGES>([&](auto jc) { stage(jc, kt + decltype(jc)::value); });
+        // The last ring turn stops at the end of K (a branch on a workgroup-uniform
+        // value); the copies and fragment reads the last stage issued for the stages
+        // after it read zeros and are never used.
+        for (int kt = 0; kt < nk; kt += T::STAGES) {
+            static_for<T::STAGES>([&](auto jc) {
+                const int k = kt + decltype(jc)::value;
+                if (k < nk) stage(jc, k);
+            });
         }
         // the copies past the end of K are still landing; none may outlive the kernel
         // (and with k-groups the ring is reused below)

@@ -85,6 +85,8 @@ def _declare(lib: ctypes.CDLL) -> None:
     lib.oracle_attention_rows.restype = ctypes.c_int
     lib.oracle_num_threads.argtypes = []
     lib.oracle_num_threads.restype = ctypes.c_int
+    lib.oracle_set_num_threads.argtypes = [ctypes.c_int]
+    lib.oracle_set_num_threads.restype = None
     for name in ("oracle_f16_to_f64_array", "oracle_f64_to_f16_array", "oracle_gelu_array"):
         getattr(lib, name).argtypes = [i64, p, p]
         getattr(lib, name).restype = None
@@ -137,6 +139,11 @@ def gelu(x, lib=None) -> np.ndarray:
     out = np.empty(x.shape, dtype=np.float64)
     lib.oracle_gelu_array(x.size, _ptr(x), _ptr(out))
     return out
+
+
+def set_num_threads(n: int, lib=None) -> None:
+    """Threads the oracle's OpenMP loops use from now on in this process."""
+    (lib or load()).oracle_set_num_threads(int(n))
 
 
 def num_threads(lib=None) -> int:

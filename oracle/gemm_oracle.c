@@ -46,6 +46,12 @@ int oracle_num_threads(void)
     return omp_get_max_threads();
 }
 
+/* Threads for the following calls (for single-thread timings); n < 1 is ignored. */
+void oracle_set_num_threads(int n)
+{
+    if (n >= 1) omp_set_num_threads(n);
+}
+
 /* binary16 -> double, exact for every bit pattern. */
 double oracle_f16_to_f64(uint16_t h)
 {
