@@ -365,12 +365,17 @@ mi355gemm_status mi355gemm_softmax(int64_t M, int64_t N, const void *x, void *y,
     const hipStream_t st = static_cast<hipStream_t>(stream);
     const int n = (int)N;
     const dim3 rows_grid((unsigned)((M + 3) / 4));
+    // one wavefront per row up to 2048 elements, four per row up to 16384, sixteen up to
+    // 65536 (measured crossovers on MI355X), then two passes by one workgroup per row
+    const dim3 one_row((unsigned)M);
     if (N <= 512) hipLaunchKernelGGL(softmax_rows<1>, rows_grid, dim3(kSoftmaxThreads), 0, st, xs, ys, M, n);
     else if (N <= 1024) hipLaunchKernelGGL(softmax_rows<2>, rows_grid, dim3(kSoftmaxThreads), 0, st, xs, ys, M, n);
     else if (N <= 2048) hipLaunchKernelGGL(softmax_rows<4>, rows_grid, dim3(kSoftmaxThreads), 0, st, xs, ys, M, n);
-    else if (N <= 4096) hipLaunchKernelGGL(softmax_rows<8>, rows_grid, dim3(kSoftmaxThreads), 0, st, xs, ys, M, n);
-    else if (N <= 8192) hipLaunchKernelGGL(softmax_rows<16>, rows_grid, dim3(kSoftmaxThreads), 0, st, xs, ys, M, n);
-    else if (N <= 16384) hipLaunchKernelGGL(softmax_rows<32>, rows_grid, dim3(kSoftmaxThreads), 0, st, xs, ys, M, n);
+    else if (N <= 4096) hipLaunchKernelGGL((softmax_wg<2, 256>), one_row, dim3(256), 0, st, xs, ys, n);
+    else if (N <= 8192) hipLaunchKernelGGL((softmax_wg<4, 256>), one_row, dim3(256), 0, st, xs, ys, n);
+    else if (N <= 16384) hipLaunchKernelGGL((softmax_wg<8, 256>), one_row, dim3(256), 0, st, xs, ys, n);
+    else if (N <= 32768) hipLaunchKernelGGL((softmax_wg<4, 1024>), one_row, dim3(1024), 0, st, xs, ys, n);
+    else if (N <= 65536) hipLaunchKernelGGL((softmax_wg<8, 1024>), one_row, dim3(1024), 0, st, xs, ys, n);
     else hipLaunchKernelGGL(softmax_long, dim3((unsigned)M), dim3(kSoftmaxLongThreads), 0, st, xs, ys, n);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess)

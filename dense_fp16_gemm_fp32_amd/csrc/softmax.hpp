@@ -6,12 +6,20 @@
 // x and y M x N fp16 row-major, arithmetic in fp32, one rounding to fp16 at the store.
 // HBM-bound: 4 bytes move per element.
 //
+// Dispatch (measured crossovers): softmax_rows up to 2048 elements per row, softmax_wg with
+// 4 wavefronts per row up to 16384 and with 16 up to 65536, softmax_long beyond.
+//
 // softmax_rows<VPL> (N <= 512 * VPL): one wavefront per row, the row held in registers as
 //   fp16 (VPL 16-byte vectors per lane, vector c = lane + 64 k covering elements
 //   8c .. 8c+7, so every load and store instruction of a wave touches one contiguous
 //   span).  Max and sum are reduced across the wave with cross-lane shuffles; exp is
 //   evaluated twice per element (for the sum and for the output) rather than holding
 //   fp32 copies, which keeps the register footprint at VPL * 4.
+// softmax_wg<VPL, NT> (N <= 8 * NT * VPL): one NT-thread workgroup per row, the row held
+//   in the registers of its NT / 64 wavefronts (VPL 16-byte vectors per lane, vector
+//   c = thread + NT k), maximum and sum reduced across each wave by shuffles and across
+//   the waves through LDS: still one read and one write per element, with more loads in
+//   flight per row than one wavefront can hold.
 // softmax_long (any N): one 1024-thread workgroup per row, two passes over the row: an
 //   online running (max, sum) per thread -- when a larger value arrives the sum so far is
 //   rescaled by exp(old max - new max) -- combined across the workgroup, then a pass that
@@ -56,6 +64,7 @@ __device__ __forceinline__ float wave_sum(float v)
 
 constexpr int kSoftmaxThreads = 256;       // 4 rows per workgroup in softmax_rows
 constexpr int kSoftmaxLongThreads = 1024;  // one row per workgroup in softmax_long
+constexpr int kSoftmaxWgThreads = 1024;    // default workgroup of softmax_wg
 
 template <int VPL>
 __global__ void __launch_bounds__(kSoftmaxThreads)
@@ -95,6 +104,69 @@ softmax_rows(const sf16 *x, sf16 *y, int64_t M, int N)
 #pragma unroll
     for (int k = 0; k < VPL; ++k) {
         const int e0 = 8 * (lane + 64 * k);
+        sf16x8 o;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) o[i] = (sf16)(exp_f32((float)v[k][i] - m) * inv);
+        if (e0 + 8 <= N) {
+            *reinterpret_cast<sf16x8u *>(yr + e0) = o;
+        } else {
+#pragma unroll
+            for (int i = 0; i < 8; ++i)
+                if (e0 + i < N) yr[e0 + i] = o[i];
+        }
+    }
+}
+
+template <int VPL, int NT = kSoftmaxWgThreads>
+__global__ void __launch_bounds__(NT)
+softmax_wg(const sf16 *x, sf16 *y, int N)
+{
+    constexpr int NWV = NT / 64;
+    __shared__ float red[NWV];
+    const int64_t row = blockIdx.x;
+    const sf16 *xr = x + row * (int64_t)N;
+    sf16 *yr = y + row * (int64_t)N;
+    const int t = threadIdx.x, lane = t & 63, wv = t >> 6;
+    const sf16 ninf = (sf16)(-__builtin_inff());
+
+    sf16x8 v[VPL];
+#pragma unroll
+    for (int k = 0; k < VPL; ++k) {
+        const int e0 = 8 * (t + NT * k);
+        if (e0 + 8 <= N) {
+            v[k] = *reinterpret_cast<const sf16x8u *>(xr + e0);
+        } else {
+#pragma unroll
+            for (int i = 0; i < 8; ++i) v[k][i] = (e0 + i < N) ? xr[e0 + i] : ninf;
+        }
+    }
+    // the workgroup's maximum, then its sum: per wave by shuffles, across waves in LDS
+    auto wg_reduce = [&](float a, bool is_max) {
+        a = is_max ? wave_max(a) : wave_sum(a);
+        if (lane == 0) red[wv] = a;
+        __syncthreads();
+        float r = red[0];
+#pragma unroll
+        for (int w = 1; w < NWV; ++w) r = is_max ? fmaxf(r, red[w]) : r + red[w];
+        __syncthreads();   // red is reused by the next reduction
+        return r;
+    };
+    float m = -__builtin_inff();
+#pragma unroll
+    for (int k = 0; k < VPL; ++k)
+#pragma unroll
+        for (int i = 0; i < 8; ++i) m = fmaxf(m, (float)v[k][i]);
+    m = wg_reduce(m, true);
+    float s = 0.0f;
+#pragma unroll
+    for (int k = 0; k < VPL; ++k)
+#pragma unroll
+        for (int i = 0; i < 8; ++i) s += exp_f32((float)v[k][i] - m);
+    s = wg_reduce(s, false);
+    const float inv = 1.0f / s;
+#pragma unroll
+    for (int k = 0; k < VPL; ++k) {
+        const int e0 = 8 * (t + NT * k);
         sf16x8 o;
 #pragma unroll
         for (int i = 0; i < 8; ++i) o[i] = (sf16)(exp_f32((float)v[k][i] - m) * inv);

@@ -127,8 +127,9 @@ mi355gemm_status mi355gemm_vector_add(int64_t n, const void *a, const void *b, v
  * y        device pointer to M x N fp16 (written), leading dimension N; may equal x.
  * stream   hipStream_t to enqueue on; NULL is the default stream.
  *
- * Rows of up to 16384 elements are held in registers by one wavefront; longer rows take
- * two passes over the row by one workgroup.  IEEE rules give the edge cases: a row with
+ * Rows of up to 65536 elements are held in registers (by one wavefront up to 2048
+ * elements, by 4 up to 16384, by 16 beyond); longer rows take two passes over the row by
+ * one workgroup.  IEEE rules give the edge cases: a row with
  * a NaN or +inf entry, or with every entry -inf, comes out NaN.  Pointers must be 2-byte
  * aligned (any such alignment and any N are served).  The caller owns the buffers; the
  * call allocates nothing and returns after the enqueue.  Errors: EINVAL for negative

@@ -49,8 +49,10 @@ def _run(x, out=None):
     return y
 
 
-SHAPES = [(1, 1), (3, 7), (5, 8), (64, 512), (33, 513), (4, 1000), (7, 4096), (9, 8191),
-          (3, 16384), (2, 16385), (2, 70001), (1000, 3000), (4096, 256)]
+SHAPES = [(1, 1), (3, 7), (5, 8), (64, 512), (33, 513), (4, 1000), (5, 2048), (5, 2049),
+          (7, 4096), (6, 4097), (9, 8191), (4, 8193),
+          (3, 16384), (2, 16385), (3, 32768), (2, 32769), (5, 65536), (2, 70001),
+          (2, 131072), (2, 131073), (1000, 3000), (4096, 256)]
 
 
 @pytest.mark.parametrize("shape", SHAPES, ids=["%dx%d" % s for s in SHAPES])
@@ -61,7 +63,7 @@ def test_softmax_parity(shape):
     _check(_bits(_run(x)), oracle.softmax(x), "%dx%d" % shape)
 
 
-@pytest.mark.parametrize("N", [6, 300, 20000])
+@pytest.mark.parametrize("N", [6, 300, 20000, 100000, 200000])
 def test_softmax_edge_rows(N):
     x = _x(6, N, N, scale=2.0)
     x[0, ::3] = -np.inf                 # some -inf: finite result
