@@ -121,8 +121,10 @@ def time_gemm(lib, A, B, bias, epi, out, steps, warmup, config=None):
 
 
 def _sha16(t) -> str:
+    """First 16 hex digits of the sha256 of a CPU fp16 tensor's bytes."""
     import hashlib
-    return hashlib.sha256(t.contiguous().view(-1).view(dtype=__import__("torch").int16).numpy().tobytes()).hexdigest()[:16]
+    import torch
+    return hashlib.sha256(t.contiguous().view(-1).view(torch.int16).numpy().tobytes()).hexdigest()[:16]
 
 
 def inputs_sha256(w, epi) -> dict:
