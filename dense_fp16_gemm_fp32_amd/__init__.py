@@ -298,36 +298,49 @@ def attention(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, causal: bool = 
               scale: float | None = None, out: torch.Tensor | None = None,
               lse: torch.Tensor | None = None,
               stream: torch.cuda.Stream | None = None) -> torch.Tensor:
-    """Attention forward of contiguous fp16 (batch, heads, seq, head_dim) tensors on the
-    GPU; ``scale`` defaults to 1/sqrt(head_dim).  ``lse`` (optional, fp32, (batch, heads,
-    seq_q)) receives the natural-log sum of exp of each query row's scores."""
+    """Attention forward of contiguous fp16 tensors on the GPU: q (..., seq_q, head_dim),
+    k and v (..., seq_k, head_dim) with the same leading dimensions (typically batch and
+    heads; every leading index is one independent problem).  ``scale`` defaults to
+    1/sqrt(head_dim).  ``lse`` (optional, fp32, shaped like q without its last
+    dimension) receives the natural-log sum of exp of each query row's scores."""
     for t, n in ((q, "q"), (k, "k"), (v, "v")):
-        _check_tensor(t, n, 4)
-    B, H, Sq, D = q.shape
-    Sk = k.shape[2]
-    if k.shape != (B, H, Sk, D) or v.shape != k.shape:
-        raise ValueError("k and v must be (batch, heads, seq_k, head_dim) like q; got %s %s %s"
-                         % (tuple(q.shape), tuple(k.shape), tuple(v.shape)))
+        if not isinstance(t, torch.Tensor):
+            raise TypeError("%s must be a torch.Tensor" % n)
+        if t.dtype != torch.float16:
+            raise TypeError("%s must be float16, got %s" % (n, t.dtype))
+        if t.device.type != "cuda":
+            raise ValueError("%s must be on a GPU device" % n)
+        if t.dim() < 2 or not t.is_contiguous():
+            raise ValueError("%s must be a contiguous tensor of at least 2 dimensions" % n)
+    lead, (Sq, D) = tuple(q.shape[:-2]), tuple(q.shape[-2:])
+    Sk = k.shape[-2]
+    if k.shape != lead + (Sk, D) or v.shape != k.shape:
+        raise ValueError("k and v must be (..., seq_k, head_dim) with q's leading dimensions; "
+                         "got %s %s %s" % (tuple(q.shape), tuple(k.shape), tuple(v.shape)))
     if k.device != q.device or v.device != q.device:
         raise ValueError("q, k and v must be on one device")
     if out is None:
         out = torch.empty_like(q)
     else:
-        _check_tensor(out, "out", 4)
+        _check_tensor(out, "out", q.dim())
         if out.shape != q.shape or out.device != q.device:
             raise ValueError("out must be shaped like q on its device")
     lse_ptr = None
     if lse is not None:
-        if (lse.dtype != torch.float32 or lse.device != q.device or lse.shape != (B, H, Sq)
+        if (lse.dtype != torch.float32 or lse.device != q.device or tuple(lse.shape) != lead + (Sq,)
                 or not lse.is_contiguous()):
-            raise ValueError("lse must be a contiguous float32 (batch, heads, seq_q) tensor on q's device")
+            raise ValueError("lse must be a contiguous float32 tensor shaped like q without "
+                             "its last dimension, on q's device")
         lse_ptr = lse.data_ptr()
     if scale is None:
         scale = 1.0 / float(D) ** 0.5
+    pairs = 1
+    for d in lead:
+        pairs *= d
     lib = _lib if _lib is not None else library()
     idx = q.device.index if q.device.index is not None else torch.cuda.current_device()
     sptr = stream.cuda_stream if stream is not None else _raw_stream(idx)
-    args = (B, H, Sq, Sk, D, q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse_ptr,
+    args = (pairs, 1, Sq, Sk, D, q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse_ptr,
             float(scale), int(bool(causal)), sptr)
     if idx == torch.cuda.current_device():
         st = lib.mi355gemm_attention(*args)

@@ -183,3 +183,24 @@ def test_attention_empty_and_errors():
     with pytest.raises(g.GemmError) as e:
         g.attention(q96, q96, q96)
     assert e.value.status == g.EUNSUPPORTED
+
+
+def test_attention_leading_dimensions():
+    """Any leading dimensions: 3-D (heads, seq, d) and 5-D tensors give the same rows as
+    the 4-D call on the same data."""
+    q, k, v = _qkv(2, 3, 150, 170, 64, seed=123)
+    o4 = _np(g.attention(_t(q), _t(k), _t(v), causal=True))
+    q3, k3, v3 = (x.reshape(6, *x.shape[2:]) for x in (q, k, v))
+    o3 = _np(g.attention(_t(q3), _t(k3), _t(v3), causal=True))
+    q5, k5, v5 = (x.reshape(1, 2, 3, *x.shape[2:]) for x in (q, k, v))
+    lse = torch.empty((1, 2, 3, 150), dtype=torch.float32, device=DEV)
+    o5 = _np(g.attention(_t(q5), _t(k5), _t(v5), causal=True, lse=lse))
+    torch.cuda.synchronize()
+    assert np.array_equal(o3.reshape(o4.shape), o4) and np.array_equal(o5.reshape(o4.shape), o4)
+    ro, rl, re = oracle.attention(q, k, v, causal=True)
+    _check(o4, ro, re, "leading dims")
+    assert np.allclose(lse.cpu().numpy().reshape(rl.shape), rl, atol=1e-3)
+    q2 = _t(q[0, 0])          # (seq, d): one problem
+    o2 = _np(g.attention(q2, _t(k[0, 0]), _t(v[0, 0]), causal=True))
+    torch.cuda.synchronize()
+    assert np.array_equal(o2, o4[0, 0])
