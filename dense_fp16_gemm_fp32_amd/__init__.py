@@ -266,18 +266,22 @@ def vector_add(a: torch.Tensor, b: torch.Tensor, out: torch.Tensor | None = None
 
 def softmax(x: torch.Tensor, out: torch.Tensor | None = None,
             stream: torch.cuda.Stream | None = None) -> torch.Tensor:
-    """Row-wise softmax of a contiguous 2-D fp16 tensor on the GPU (over the last dim)."""
-    _check_tensor(x, "x", 2)
+    """Softmax over the last dimension of a contiguous fp16 tensor on the GPU (every
+    leading index is one row)."""
+    if not isinstance(x, torch.Tensor) or x.dtype != torch.float16:
+        raise TypeError("x must be a float16 torch.Tensor")
+    if x.device.type != "cuda" or x.dim() < 1 or not x.is_contiguous():
+        raise ValueError("x must be a contiguous tensor of at least 1 dimension on a GPU device")
     if out is None:
         out = torch.empty_like(x)
-    else:
-        _check_tensor(out, "out", 2)
-        if out.shape != x.shape or out.device != x.device:
-            raise ValueError("out must be shaped like x on its device")
+    elif (not isinstance(out, torch.Tensor) or out.dtype != torch.float16 or out.shape != x.shape
+          or out.device != x.device or not out.is_contiguous()):
+        raise ValueError("out must be a contiguous float16 tensor shaped like x on its device")
     lib = _lib if _lib is not None else library()
     idx = x.device.index if x.device.index is not None else torch.cuda.current_device()
     sptr = stream.cuda_stream if stream is not None else _raw_stream(idx)
-    M, N = x.shape
+    N = x.shape[-1]
+    M = x.numel() // N if N > 0 else 0
     if idx == torch.cuda.current_device():
         st = lib.mi355gemm_softmax(M, N, x.data_ptr(), out.data_ptr(), sptr)
     else:

@@ -97,3 +97,16 @@ def test_softmax_rows_sum_to_one():
     x = _x(256, 4096, 5)
     y = _run(x).float()
     assert torch.allclose(y.sum(dim=1), torch.ones(256, device=DEV), atol=4096 * 2.0 ** -12)
+
+
+def test_softmax_leading_dimensions():
+    """Any leading dimensions: a 3-D tensor and a 1-D vector are softmaxed over the last
+    dimension, row by row, exactly as the 2-D call on the same rows."""
+    x = _x(12, 777, 9)
+    y2 = _bits(_run(x))
+    t3 = torch.from_numpy(x.view(np.int16)).view(torch.float16).to(DEV).reshape(3, 4, 777)
+    y3 = _bits(g.softmax(t3))
+    t1 = torch.from_numpy(x[5].copy().view(np.int16)).view(torch.float16).to(DEV)
+    y1 = _bits(g.softmax(t1))
+    torch.cuda.synchronize()
+    assert np.array_equal(y3.reshape(y2.shape), y2) and np.array_equal(y1, y2[5])
