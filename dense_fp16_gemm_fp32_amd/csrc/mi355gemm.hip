@@ -228,9 +228,14 @@ int choose(const Request &r)
     if (tuned >= 0) return tuned;
     constexpr int64_t kCUs = 256;
     if (bv) {
-        if (tiles(r, 256, 256) >= kCUs) return find_direct(256, 256, 64, 8, 1);
-        if (tiles(r, 128, 128) >= kCUs) return find_direct(128, 128, 64, 4, 1);
-        if (tiles(r, 128, 128) >= kCUs / 2) return find_direct(128, 128, 64, 8, 2);
+        // measured with the interleaved tuner on MI355X (the table file records the runs)
+        const int64_t t256 = tiles(r, 256, 256), t256x128 = tiles(r, 256, 128), t128 = tiles(r, 128, 128);
+        if (t256 >= 4 * kCUs) return find_direct(256, 256, 64, 8, 1);   // several waves of big tiles
+        if (t256 >= kCUs) return find_direct(256, 256, 32, 8, 1);        // about one wave of them
+        if (t256x128 >= kCUs) return find_direct(256, 128, 64, 8, 2);    // e.g. one GPU's share of 8192^3
+        if (t128 >= kCUs) return r.K >= 4096 ? find_direct(128, 128, 64, 8, 2)   // long K: k-groups
+                                             : find_direct(128, 128, 64, 4, 1);
+        if (t128 >= kCUs / 4) return find_direct(128, 128, 64, 8, 2);    // part of the chip idle
     }
     if (tiles(r, 128, 128) >= kCUs / 2) return find_staged(128, 128, av, bv);
     return find_staged(64, 64, av, bv);

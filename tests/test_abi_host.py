@@ -286,3 +286,22 @@ def test_attention_argument_checks(args, want):
     st = g.mi355gemm_attention(a["B"], a["H"], a["Sq"], a["Sk"], a["D"], a["q"], a["k"], a["v"],
                                a["o"], a["lse"], a["scale"], a["causal"], None)
     assert st == want, g.mi355gemm_last_error()
+
+
+@pytest.mark.parametrize("shape,want", [
+    ((8192, 8192, 8192), "d256x256x64_w2x4_s2"),      # four waves of 256 x 256 tiles
+    ((4096, 4096, 4096), "d256x256x32_w2x4_s4"),      # one wave of them
+    ((16384, 2048, 1024), "d256x256x32_w2x4_s4"),
+    ((8192, 1024, 8192), "d256x128x64_w2x2k2_s3"),    # one GPU's N share of 8192^3
+    ((1024, 8192, 8192), "d256x128x64_w2x2k2_s3"),    # its M share
+    ((2048, 2048, 8192), "d128x128x64_w2x2k2_s4"),    # 256 tiles, long K
+    ((2048, 2048, 2048), "d128x128x64_w2x2_s4"),      # 256 tiles, K = 2048
+    ((1024, 1024, 1024), "d128x128x64_w2x2k2_s4"),    # 64 tiles
+    ((1000, 3000, 777), "d128x128x64_w2x2k2_s4"),     # 192 tiles
+    ((256, 256, 256), "s64x64x64_w2x1_av_bv"),        # a handful of tiles
+])
+def test_selector_rules_pick_the_measured_winners(shape, want):
+    """The rules' choice for shapes the interleaved tuner measured (they have no table
+    entry: the rule already picks the winner)."""
+    M, N, K = shape
+    assert g.mi355gemm_config_name(_select(M, N, K)) == want
