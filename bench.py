@@ -76,6 +76,8 @@ def parse():
     ap.add_argument("--no-extra", action="store_true")
     ap.add_argument("--gemm-only", action="store_true",
                     help="extra GEMM workloads only (no vector add, softmax, attention, cold run)")
+    ap.add_argument("--no-gemm-extras", action="store_true",
+                    help="skip the extra GEMM workloads and the cold run (profiling the other kernels)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run a 256 MiB device copy (counter calibration for rocprofv3)")
@@ -425,7 +427,7 @@ def main():
         calibrate_copy()
 
     extra = []
-    if not args.no_extra:
+    if not args.no_extra and not args.no_gemm_extras:
         for ew in workloads.WORKLOADS:
             for e in ew.epilogues:
                 if ew.name == w.name and e == epi:
@@ -462,7 +464,7 @@ def main():
             attention.append(r)
 
     cold = None
-    if others:
+    if others and not args.no_gemm_extras:
         cold = run_cold(lib, w, 200)
         print("bench: %s %.2f us/launch over %d input copies (%.0f MiB)"
               % (cold["workload"], cold["kernel_us"], cold["copies"], cold["bytes_rotated"] / 2**20),
