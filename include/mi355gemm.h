@@ -65,8 +65,9 @@ typedef enum {
  *
  * Errors: EINVAL for negative sizes, null pointers with work to do, an unknown
  * epilogue, a bias epilogue with bias == NULL, or a misaligned pointer; EUNSUPPORTED
- * if K or N exceeds 2^21 (the per-tile 32-bit buffer offsets); EHIP if the launch
- * fails.  A non-OK return leaves C untouched and sets mi355gemm_last_error().
+ * if K or N is 2^22 or more (the per-tile buffer descriptors use 32-bit byte offsets)
+ * or M is 2^31 or more; EHIP if the launch fails.  A non-OK return leaves C untouched
+ * and sets mi355gemm_last_error().
  */
 mi355gemm_status mi355gemm_gemm(int64_t M, int64_t N, int64_t K,
                                 const void *A, const void *B, void *C, const void *bias,
@@ -167,9 +168,10 @@ mi355gemm_status mi355gemm_softmax(int64_t M, int64_t N, const void *x, void *y,
  * enqueue.  batch * heads == 0 or seq_q == 0 does nothing and returns OK.  Errors:
  * EINVAL for negative sizes, seq_k == 0 with work to do (the softmax over no keys is
  * undefined), a scale that is not finite and positive, NULL or misaligned pointers (q, k,
- * v, o need 16-byte alignment, lse 4-byte); EUNSUPPORTED for another head_dim or sizes
+ * v, o need 16-byte alignment, lse 4-byte); EUNSUPPORTED for another head_dim, sizes
  * past the 32-bit offsets the kernel uses ((seq + 1024) * head_dim * 2 bytes must stay
- * below 2^31 per pair); EHIP if the launch fails.
+ * below 2^31 per pair) or batch * heads * ceil(seq_q / 256) of 2^31 or more; EHIP if the
+ * launch fails.
  */
 mi355gemm_status mi355gemm_attention(int64_t batch, int64_t heads, int64_t seq_q, int64_t seq_k,
                                      int64_t head_dim, const void *q, const void *k,
@@ -193,7 +195,10 @@ typedef struct {
 /* Number of compiled configurations (ids 0 .. n-1). Host-only. */
 int mi355gemm_num_configs(void);
 
-/* Static name of a configuration ("128x128x64_w2x2_av_bv", ...), or NULL. Host-only. */
+/* Static name of a configuration, or NULL for an unknown id.  Host-only.  Names read
+ * <d|s><BM>x<BN>x<BK>_w<waves_m>x<waves_n>[k<k_groups>]_...: d = direct HBM -> LDS kernel
+ * (suffix s<stages>), s = register-staged kernel (suffix av/an: A in 16-byte / 2-byte
+ * loads, bv/bn: B and C likewise), e.g. "d128x128x64_w2x2_s4", "s64x64x64_w2x1_av_bv". */
 const char *mi355gemm_config_name(int config_id);
 
 /* Fill *out for config_id; EINVAL for an unknown id or NULL out. Host-only. */
