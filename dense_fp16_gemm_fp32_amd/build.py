@@ -11,7 +11,7 @@ import sys
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 SOURCES = [os.path.join(PKG, "csrc", "mi355gemm.hip")]
-HEADERS = [os.path.join(PKG, "csrc", "gemm_common.hpp"), os.path.join(PKG, "csrc", "gemm_direct.hpp"), os.path.join(PKG, "csrc", "gemm_staged.hpp"), os.path.join(PKG, "csrc", "tuned_table.inc"), os.path.join(PKG, "csrc", "vector_add.hpp"), os.path.join(PKG, "csrc", "softmax.hpp"), os.path.join(PKG, "csrc", "attention.hpp"), os.path.join(ROOT, "include", "mi355gemm.h")]
+HEADERS = [os.path.join(PKG, "csrc", "gemm_common.hpp"), os.path.join(PKG, "csrc", "gemm_direct.hpp"), os.path.join(PKG, "csrc", "gemm_staged.hpp"), os.path.join(PKG, "csrc", "gemm_narrow.hpp"), os.path.join(PKG, "csrc", "tuned_table.inc"), os.path.join(PKG, "csrc", "vector_add.hpp"), os.path.join(PKG, "csrc", "softmax.hpp"), os.path.join(PKG, "csrc", "attention.hpp"), os.path.join(ROOT, "include", "mi355gemm.h")]
 LIBRARY = os.path.join(PKG, "libmi355gemm.so")
 ROCM = os.environ.get("ROCM_PATH", "/opt/rocm")
 ARCH = "gfx950"

@@ -46,10 +46,19 @@ struct GemmArgs {
     const f16 *B;
     f16 *C;
     const f16 *bias;
-    int M, N, K;
+    int M, N, K;      // N: the columns this launch computes (of B, C and bias)
+    int ldb, ldc;     // row strides of B and C in elements (>= N); A's is K
     int tiles_m, tiles_n;
     int group_m;
 };
+
+// Bytes a buffer descriptor must cover for `rows` rows of `width` elements each, rows
+// `ld` elements apart, starting at the descriptor's base: up to the last element of the
+// last row and not beyond it (so the descriptor never reaches past the operand).
+__device__ __forceinline__ uint32_t span_bytes(int rows, int ld, int width)
+{
+    return rows > 0 ? (uint32_t)((rows - 1) * ld + width) * 2u : 0u;
+}
 
 // ---------------------------------------------------------------- tile order --------
 // Workgroups are handed to the 8 XCDs round-robin (id % 8).  Renumber them so each XCD
@@ -125,9 +134,9 @@ __device__ __forceinline__ void store_tile(const f32x16 (&acc)[FM][FN], const Ge
                                            int lane)
 {
     const int cols_valid = p.N - n0;
-    // C covers rows [m0, m0 + tile_rows) from column n0
+    // C covers rows [m0, m0 + tile_rows), columns [n0, N)
     const __amdgpu_buffer_rsrc_t c_rs =
-        make_rsrc(p.C + (int64_t)m0 * p.N + n0, (uint32_t)(tile_rows * p.N - n0) * 2u);
+        make_rsrc(p.C + (int64_t)m0 * p.ldc + n0, span_bytes(tile_rows, p.ldc, cols_valid));
     // bias covers columns [n0, N); with no epilogue it is never read
     const __amdgpu_buffer_rsrc_t b_rs =
         make_rsrc(EPI != 0 ? p.bias + n0 : p.C, EPI != 0 ? (uint32_t)cols_valid * 2u : 0u);
@@ -166,14 +175,14 @@ __device__ __forceinline__ void store_tile(const f32x16 (&acc)[FM][FN], const Ge
                     hb[e] = __builtin_bit_cast(uint16_t, h);
                 }
                 if constexpr (BV) {
-                    const uint32_t off = masked_offset((uint32_t)(m * p.N + n) * 2u, n < cols_valid);
+                    const uint32_t off = masked_offset((uint32_t)(m * p.ldc + n) * 2u, n < cols_valid);
                     const u32x2 packed = {hb[0] | (hb[1] << 16), hb[2] | (hb[3] << 16)};
                     __builtin_amdgcn_raw_buffer_store_b64(packed, c_rs, off, 0, 0);
                 } else {
 #pragma unroll
                     for (int e = 0; e < 4; ++e) {
                         const uint32_t off =
-                            masked_offset((uint32_t)(m * p.N + n + e) * 2u, n + e < cols_valid);
+                            masked_offset((uint32_t)(m * p.ldc + n + e) * 2u, n + e < cols_valid);
                         __builtin_amdgcn_raw_buffer_store_b16((uint16_t)hb[e], c_rs, off, 0, 0);
                     }
                 }

@@ -142,7 +142,7 @@ template <class T>
 struct DirectWave {
     using St = Stage<T>;
     int lane, wave, kg, wm, wn;
-    int K, N, n0;
+    int K, N, ldb, n0;
     const f16 *B;
     __amdgpu_buffer_rsrc_t a_rs;
     uint32_t a_off[T::GA];
@@ -174,6 +174,7 @@ struct DirectWave {
         wn = wc % T::WAVES_N;
         K = p.K;
         N = p.N;
+        ldb = p.ldb;
         n0 = n0_;
         B = p.B;
         // A: slot s of the stage (16 B each) holds row s / CA, physical chunk s % CA, which
@@ -193,7 +194,7 @@ struct DirectWave {
             const int s = (g * T::NW + wave) * 64 + lane;
             const int row = s / T::CB;
             const int c = (s % T::CB) ^ swz_b(row);
-            b_off[g] = masked_offset((uint32_t)(row * N + 8 * c) * 2u, 8 * c < cols_valid);
+            b_off[g] = masked_offset((uint32_t)(row * ldb + 8 * c) * 2u, 8 * c < cols_valid);
         }
         // A fragment: row wm*WTM + i*32 + r32, logical chunk 2*kk + h -> physical chunk
         // ^ swz_a(row); swz_a depends on the row only through r32 (WTM and 32 are
@@ -302,8 +303,7 @@ struct DirectWave {
             const int gb = g - T::GA;
             const int rows_k = min(T::BK, K - k0);
             const __amdgpu_buffer_rsrc_t b_rs =
-                make_rsrc(B + (int64_t)min(k0, K) * N + n0,
-                          rows_k > 0 ? (uint32_t)(rows_k * N - n0) * 2u : 0u);
+                make_rsrc(B + (int64_t)min(k0, K) * ldb + n0, span_bytes(rows_k, ldb, N - n0));
             lds_dma16(b_rs, dst.b + (gb * T::NW + wave) * 512, b_off[gb]);
         }
     }
@@ -416,13 +416,13 @@ __device__ __forceinline__ void lds_to_c(const GemmArgs &p, int m0, int n0, int 
     static_assert(T::BM * CW % T::NT == 0, "tile must split evenly over the threads");
     const int cols_valid = p.N - n0;
     const __amdgpu_buffer_rsrc_t c_rs =
-        make_rsrc(p.C + (int64_t)m0 * p.N + n0, (uint32_t)(rows_valid * p.N - n0) * 2u);
+        make_rsrc(p.C + (int64_t)m0 * p.ldc + n0, span_bytes(rows_valid, p.ldc, cols_valid));
 #pragma unroll
     for (int k = 0; k < PER; ++k) {
         const int q = threadIdx.x + k * T::NT;
         const int r = q / CW, c = q % CW;
         const u32x4 v = *reinterpret_cast<const u32x4 *>(ctile + (r * T::BN + 8 * (c ^ c_chunk_swz<T>(r))) * 2);
-        const uint32_t off = masked_offset((uint32_t)(r * p.N + 8 * c) * 2u, 8 * c < cols_valid);
+        const uint32_t off = masked_offset((uint32_t)(r * p.ldc + 8 * c) * 2u, 8 * c < cols_valid);
         __builtin_amdgcn_raw_buffer_store_b128(v, c_rs, off, 0, 0);
     }
 }

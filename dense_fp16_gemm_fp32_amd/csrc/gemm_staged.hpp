@@ -109,14 +109,13 @@ struct BLoader {
     static_assert(Q * CN % T::NT == 0, "B tile must split evenly over threads");
     u32x4 r[PER][4];
 
-    // Loads rows [k0, k0 + BK) x columns [n0, n0 + BN) of B; rows >= K and columns >= N
-    // read 0.
-    __device__ __forceinline__ void load(const f16 *B, int N, int K, int n0, int k0, int tid)
+    // Loads rows [k0, k0 + BK) x columns [n0, n0 + BN) of B (rows ldb apart); rows >= K
+    // and columns >= N read 0.
+    __device__ __forceinline__ void load(const f16 *B, int ldb, int N, int K, int n0, int k0, int tid)
     {
         const int rows_k = min(T::BK, K - k0);
         const int cols = N - n0;
-        const __amdgpu_buffer_rsrc_t rs =
-            make_rsrc(B + (int64_t)k0 * N + n0, (uint32_t)(rows_k * N - n0) * 2u);
+        const __amdgpu_buffer_rsrc_t rs = make_rsrc(B + (int64_t)k0 * ldb + n0, span_bytes(rows_k, ldb, cols));
 #pragma unroll
         for (int i = 0; i < PER; ++i) {
             const int p = tid + i * T::NT;
@@ -125,15 +124,15 @@ struct BLoader {
             for (int j = 0; j < 4; ++j) {
                 const int row = 4 * q + j;
                 if constexpr (VEC) {
-                    const uint32_t off = masked_offset((uint32_t)(row * N + 8 * c) * 2u, 8 * c < cols);
+                    const uint32_t off = masked_offset((uint32_t)(row * ldb + 8 * c) * 2u, 8 * c < cols);
                     r[i][j] = __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, 0);
                 } else {
                     uint32_t w[4];
 #pragma unroll
                     for (int s = 0; s < 4; ++s) {
                         const int na = 8 * c + 2 * s, nb = na + 1;
-                        const uint32_t oa = masked_offset((uint32_t)(row * N + na) * 2u, na < cols);
-                        const uint32_t ob = masked_offset((uint32_t)(row * N + nb) * 2u, nb < cols);
+                        const uint32_t oa = masked_offset((uint32_t)(row * ldb + na) * 2u, na < cols);
+                        const uint32_t ob = masked_offset((uint32_t)(row * ldb + nb) * 2u, nb < cols);
                         const uint32_t lo = __builtin_amdgcn_raw_buffer_load_b16(rs, oa, 0, 0);
                         const uint32_t hi = __builtin_amdgcn_raw_buffer_load_b16(rs, ob, 0, 0);
                         w[s] = lo | (hi << 16);
@@ -204,13 +203,13 @@ __global__ void __launch_bounds__(T::NT) gemm_staged(GemmArgs p)
 
     if (nk > 0) {
         al.load(a_rs, 0, p.K, tid);
-        bl.load(p.B, p.N, p.K, n0, 0, tid);
+        bl.load(p.B, p.ldb, p.N, p.K, n0, 0, tid);
         al.store(As, tid);
         bl.store(Bs, tid);
         __syncthreads();
         if (nk > 1) {
             al.load(a_rs, T::BK, p.K, tid);
-            bl.load(p.B, p.N, p.K, n0, T::BK, tid);
+            bl.load(p.B, p.ldb, p.N, p.K, n0, T::BK, tid);
         }
     }
 
@@ -241,7 +240,7 @@ __global__ void __launch_bounds__(T::NT) gemm_staged(GemmArgs p)
             bl.store(Bs + (cur ^ 1) * T::B_STAGE, tid);
             if (kt + 2 < nk) {
                 al.load(a_rs, (kt + 2) * T::BK, p.K, tid);
-                bl.load(p.B, p.N, p.K, n0, (kt + 2) * T::BK, tid);
+                bl.load(p.B, p.ldb, p.N, p.K, n0, (kt + 2) * T::BK, tid);
             }
         }
         __syncthreads();

@@ -14,6 +14,7 @@
 
 #include "attention.hpp"
 #include "gemm_direct.hpp"
+#include "gemm_narrow.hpp"
 #include "gemm_staged.hpp"
 #include "softmax.hpp"
 #include "vector_add.hpp"
@@ -45,6 +46,9 @@ MI355_DIRECT(D256x128)
 MI355_DIRECT(D128)
 MI355_DIRECT(D128w4)
 #undef MI355_DIRECT
+template __global__ void gemm_narrow<0>(GemmArgs);
+template __global__ void gemm_narrow<1>(GemmArgs);
+template __global__ void gemm_narrow<2>(GemmArgs);
 }  // namespace mi355
 
 namespace {
@@ -227,7 +231,9 @@ int choose(const Request &r)
     const int tuned = tuned_choice(r, av, bv);
     if (tuned >= 0) return tuned;
     constexpr int64_t kCUs = 256;
-    if (bv) {
+    // rows of B and C that are not 16-byte friendly still take the direct kernel for all
+    // but their last N % 8 columns (run() splits the launch)
+    if (bv || r.N >= 64) {
         // measured with the interleaved tuner on MI355X (the table file records the runs)
         const int64_t t256 = tiles(r, 256, 256), t256x128 = tiles(r, 256, 128), t128 = tiles(r, 128, 128);
         if (t256 >= 4 * kCUs) return find_direct(256, 256, 64, 8, 1);   // several waves of big tiles
@@ -258,18 +264,22 @@ mi355gemm_status check_config(const Config &c, const Request &r)
     return MI355GEMM_OK;
 }
 
-mi355gemm_status launch(const Config &c, const Request &r, hipStream_t stream)
+// Launch configuration c on columns [n_begin, n_begin + n_width) of the request (B, C and
+// bias offset by n_begin, rows still N apart).
+mi355gemm_status launch(const Config &c, const Request &r, int64_t n_begin, int64_t n_width,
+                        hipStream_t stream)
 {
     GemmArgs a;
     a.A = static_cast<const f16 *>(r.A);
-    a.B = static_cast<const f16 *>(r.B);
-    a.C = static_cast<f16 *>(r.C);
-    a.bias = static_cast<const f16 *>(r.bias);
+    a.B = r.B != nullptr ? static_cast<const f16 *>(r.B) + n_begin : nullptr;
+    a.C = static_cast<f16 *>(r.C) + n_begin;
+    a.bias = r.bias != nullptr ? static_cast<const f16 *>(r.bias) + n_begin : nullptr;
     a.M = (int)r.M;
-    a.N = (int)r.N;
+    a.N = (int)n_width;
     a.K = (int)r.K;
+    a.ldb = a.ldc = (int)r.N;
     a.tiles_m = (int)((r.M + c.bm - 1) / c.bm);
-    a.tiles_n = (int)((r.N + c.bn - 1) / c.bn);
+    a.tiles_n = (int)((n_width + c.bn - 1) / c.bn);
     a.group_m = c.group_m;
     const int64_t grid = (int64_t)a.tiles_m * a.tiles_n;
     if (grid >= ((int64_t)1 << 31))
@@ -278,6 +288,29 @@ mi355gemm_status launch(const Config &c, const Request &r, hipStream_t stream)
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess)
         return fail(MI355GEMM_EHIP, "launch of %s failed: %s", c.name, hipGetErrorString(e));
+    return MI355GEMM_OK;
+}
+
+// Launch the narrow kernel on columns [n_begin, n_begin + n_width), n_width <= 8.
+mi355gemm_status launch_narrow(const Request &r, int64_t n_begin, int64_t n_width, hipStream_t stream)
+{
+    GemmArgs a;
+    a.A = static_cast<const f16 *>(r.A);
+    a.B = r.B != nullptr ? static_cast<const f16 *>(r.B) + n_begin : nullptr;
+    a.C = static_cast<f16 *>(r.C) + n_begin;
+    a.bias = r.bias != nullptr ? static_cast<const f16 *>(r.bias) + n_begin : nullptr;
+    a.M = (int)r.M;
+    a.N = (int)n_width;
+    a.K = (int)r.K;
+    a.ldb = a.ldc = (int)r.N;
+    a.tiles_m = (int)((r.M + Narrow::RW - 1) / Narrow::RW);
+    a.tiles_n = 1;
+    a.group_m = 1;
+    static void (*const fn[3])(GemmArgs) = {gemm_narrow<0>, gemm_narrow<1>, gemm_narrow<2>};
+    hipLaunchKernelGGL(fn[r.epi], dim3((unsigned)a.tiles_m), dim3(Narrow::NT), 0, stream, a);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess)
+        return fail(MI355GEMM_EHIP, "launch of the narrow kernel failed: %s", hipGetErrorString(e));
     return MI355GEMM_OK;
 }
 
@@ -294,7 +327,18 @@ mi355gemm_status run(const Request &r, void *stream, int forced)
     if (r.M == 0 || r.N == 0) return MI355GEMM_OK;
     const int id = forced >= 0 ? forced : choose(r);
     if (id < 0) return fail(MI355GEMM_EUNSUPPORTED, "no configuration serves this request");
-    return launch(kConfigs[id], r, static_cast<hipStream_t>(stream));
+    const hipStream_t hs = static_cast<hipStream_t>(stream);
+    const Config &c = kConfigs[id];
+    if (forced < 0 && c.direct && !bc_vector_ok(r)) {
+        // B, C or bias rows not 16-byte friendly: the direct kernel takes the columns up
+        // to the last multiple of 8 (at any 2-byte alignment its 16-byte pieces then never
+        // straddle the end of a row's columns), the narrow kernel the last N % 8
+        const int64_t n8 = r.N & ~(int64_t)7;
+        const mi355gemm_status s2 = launch(c, r, 0, n8, hs);
+        if (s2 != MI355GEMM_OK || n8 == r.N) return s2;
+        return launch_narrow(r, n8, r.N - n8, hs);
+    }
+    return launch(c, r, 0, r.N, hs);
 }
 
 }  // namespace

@@ -61,7 +61,13 @@ typedef enum {
  * per-call state and needs no workspace.  The call is asynchronous (it returns after
  * the enqueue) and thread-safe.  C must not overlap A, B or bias (not checked).
  * Every pointer must be at least 2-byte aligned; shapes or pointers that are not
- * 16-byte friendly are served by narrow-load kernels, never rejected.
+ * 16-byte friendly are served, never rejected.  Where the chosen configuration is a
+ * direct one but the rows of B and C are not 16-byte friendly (N % 8 != 0, B or C not
+ * 16-byte aligned, or the bias not 8-byte aligned), the call makes two launches on
+ * `stream`: the direct kernel computes columns [0, N & ~7) with unaligned 16-byte
+ * accesses, and a narrow kernel (fp32 vector multiply-adds, 8 rows per workgroup) the
+ * last N % 8 columns.  Smaller problems take the register-staged kernels, whose
+ * 2-byte load variants accept any alignment.
  *
  * Errors: EINVAL for negative sizes, null pointers with work to do, an unknown
  * epilogue, a bias epilogue with bias == NULL, or a misaligned pointer; EUNSUPPORTED
@@ -91,7 +97,9 @@ mi355gemm_status mi355gemm_gemm_config(int64_t M, int64_t N, int64_t K,
  * last_error set) if the arguments are invalid.  Host-only: makes no HIP call.
  * The choice is keyed on the shape and on pointer/leading-dimension alignment; the
  * tutorial notes the best schedule depends on the architecture and the shape
- * (thecryptopost.io page, section 3).
+ * (thecryptopost.io page, section 3).  A direct configuration returned for rows of B
+ * and C that are not 16-byte friendly is the one that computes columns [0, N & ~7);
+ * mi355gemm_gemm then adds the narrow kernel for the last N % 8 columns.
  */
 int mi355gemm_select(int64_t M, int64_t N, int64_t K, int epi,
                      const void *A, const void *B, const void *C, const void *bias);

@@ -318,3 +318,76 @@ def test_direct_kernel_k_tail_and_misaligned_a(shape):
                 torch.cuda.synchronize()
                 assert torch.isnan(buf[:pad]).all().item() and torch.isnan(buf[pad + M * N:]).all().item()
                 assert_parity(out, refs[e], "%s %s %s %s" % (cfg["name"], shape, how, e))
+
+
+# ---- rows of B and C that are not 16-byte friendly on large problems ---------------------
+# The direct kernel takes the columns up to the last multiple of 8 (at any 2-byte
+# alignment) and a narrow-load kernel the last N % 8 columns, on the same stream.
+
+SPLIT_SHAPES = [(1024, 1031, 300), (2048, 2047, 2048), (1000, 3001, 777), (768, 2050, 64),
+                (1300, 1029, 1001), (1040, 1031, 4999)]
+
+
+@pytest.mark.parametrize("shape", SPLIT_SHAPES, ids=["x".join(map(str, s)) for s in SPLIT_SHAPES])
+def test_odd_n_takes_the_direct_kernel_and_a_narrow_strip(shape):
+    M, N, K = shape
+    A, B, bias = workloads.make_inputs(M, N, K, "uniform", with_bias=True, seed=M + N + K)
+    Ad, Bd, biasd = _dev(A), _dev(B), _dev(bias)
+    pad = 4096
+    for e in EPIS:
+        buf = torch.full((M * N + 2 * pad,), float("nan"), dtype=torch.float16, device=DEV)
+        out = buf[pad:pad + M * N].view(M, N)
+        cid = g.select(Ad, Bd, biasd if e != "none" else None, e, out=out)
+        assert g.mi355gemm_config_info(cid)["direct"] == 1, g.mi355gemm_config_name(cid)
+        print("odd N", shape, e, g.mi355gemm_config_name(cid), flush=True)
+        g.gemm(Ad, Bd, biasd if e != "none" else None, e, out=out)
+        torch.cuda.synchronize()
+        assert torch.isnan(buf[:pad]).all().item() and torch.isnan(buf[pad + M * N:]).all().item()
+        rep = assert_parity(out, oracle.gemm(A, B, bias, e), "odd N %s %s" % (shape, e))
+        print("   ", rep, flush=True)
+
+
+@pytest.mark.parametrize("which", ["B", "C", "bias", "all"])
+def test_misaligned_b_c_bias_on_the_direct_kernel(which):
+    """N % 8 == 0 but B, C or the bias only 2-byte aligned: the direct kernel serves every
+    column with unaligned 16-byte copies and stores."""
+    M, N, K = 1024, 1024, 520
+    A, B, bias = workloads.make_inputs(M, N, K, "normal", with_bias=True, seed=31)
+
+    def shifted(t, on):
+        t = t.to(DEV).reshape(-1)
+        if not on:
+            return t
+        b = torch.zeros(t.numel() + 1, dtype=torch.float16, device=DEV)
+        b[1:] = t
+        return b[1:]
+    Bd = shifted(B, which in ("B", "all")).view(K, N)
+    biasd = shifted(bias, which in ("bias", "all"))
+    pad = 4096 + (1 if which in ("C", "all") else 0)
+    buf = torch.full((M * N + 2 * pad,), float("nan"), dtype=torch.float16, device=DEV)
+    out = buf[pad:pad + M * N].view(M, N)
+    cid = g.select(_dev(A), Bd, biasd, "bias_gelu", out=out)
+    assert g.mi355gemm_config_info(cid)["direct"] == 1
+    g.gemm(_dev(A), Bd, biasd, "bias_gelu", out=out)
+    torch.cuda.synchronize()
+    assert torch.isnan(buf[:pad]).all().item() and torch.isnan(buf[pad + M * N:]).all().item()
+    assert_parity(out, oracle.gemm(A, B, bias, "bias_gelu"), "misaligned " + which)
+
+
+def test_odd_n_strip_ignores_the_next_rows_values():
+    """The last N % 8 columns are read as 16-byte pieces whose padding comes from the start
+    of the next row of B: an inf there must reach no stored output but its own column's."""
+    M, N, K = 1000, 1029, 777
+    A, B, bias = workloads.make_inputs(M, N, K, "uniform", with_bias=True, seed=5)
+    B = B.clone()
+    B[:, 0] = float("inf")
+    out = g.gemm(_dev(A), _dev(B), _dev(bias), "bias")
+    torch.cuda.synchronize()
+    ref = oracle.gemm(A, B, bias, "bias")
+    got = out.cpu().numpy()
+    ref16 = ref.view(np.float16)
+    assert np.array_equal(np.isnan(got[:, 0]), np.isnan(ref16[:, 0]))
+    assert np.array_equal(np.isinf(got[:, 0]), np.isinf(ref16[:, 0]))
+    assert np.isfinite(got[:, 1:]).all()
+    assert_parity(out[:, 1:].contiguous(), np.ascontiguousarray(ref.view(np.float16)[:, 1:]).view(np.uint16),
+                  "strip after an inf column")
