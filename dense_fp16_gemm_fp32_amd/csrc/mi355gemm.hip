@@ -291,9 +291,13 @@ mi355gemm_status launch(const Config &c, const Request &r, int64_t n_begin, int6
     return MI355GEMM_OK;
 }
 
-// Launch the narrow kernel on columns [n_begin, n_begin + n_width), n_width <= 8.
+// Launch the narrow kernel on columns [n_begin, n_begin + n_width), n_width <= 8.  Its
+// 16-byte B pieces stay inside B only when rows are at least 8 elements apart.
 mi355gemm_status launch_narrow(const Request &r, int64_t n_begin, int64_t n_width, hipStream_t stream)
 {
+    if (n_width < 1 || n_width > Narrow::NC || r.N < 8)
+        return fail(MI355GEMM_EUNSUPPORTED, "narrow kernel needs 1..8 columns and N >= 8 (N=%lld)",
+                    (long long)r.N);
     GemmArgs a;
     a.A = static_cast<const f16 *>(r.A);
     a.B = r.B != nullptr ? static_cast<const f16 *>(r.B) + n_begin : nullptr;

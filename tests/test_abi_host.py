@@ -305,3 +305,19 @@ def test_selector_rules_pick_the_measured_winners(shape, want):
     entry: the rule already picks the winner)."""
     M, N, K = shape
     assert g.mi355gemm_config_name(_select(M, N, K)) == want
+
+
+@pytest.mark.parametrize("shape,ptr_off,want", [
+    ((2048, 2047, 2048), 0, "d128x128x64_w2x2_s4"),   # odd N: direct on the first 2040 columns
+    ((8192, 8191, 8192), 0, "d256x256x64_w2x4_s2"),
+    ((1000, 3001, 777), 0, "d128x128x64_w2x2k2_s4"),
+    ((2048, 2048, 2048), 2, "d128x128x64_w2x2_s4"),   # B and C only 2-byte aligned
+    ((8192, 63, 8192), 0, "s64x64x64_w2x1_av_bn"),    # N < 64: no direct launch to split
+    ((512, 1031, 64), 0, "s64x64x64_w2x1_av_bn"),     # too few tiles
+])
+def test_selector_splits_unfriendly_rows(shape, ptr_off, want):
+    """Rows of B and C that are not 16-byte friendly keep the direct kernel from N >= 64
+    with enough tiles (the call adds the narrow kernel for the last N % 8 columns)."""
+    M, N, K = shape
+    cid = g.mi355gemm_select(M, N, K, 2, P16, P16 + ptr_off, P16 + ptr_off, P16)
+    assert g.mi355gemm_config_name(cid) == want, g.mi355gemm_last_error()

@@ -391,3 +391,28 @@ def test_odd_n_strip_ignores_the_next_rows_values():
     assert np.isfinite(got[:, 1:]).all()
     assert_parity(out[:, 1:].contiguous(), np.ascontiguousarray(ref.view(np.float16)[:, 1:]).view(np.uint16),
                   "strip after an inf column")
+
+
+SPLIT_EDGES = [(1024, 1031, 0), (1024, 1031, 1), (1024, 1031, 5), (1024, 1031, 8), (1024, 1031, 9),
+               (1024, 1031, 16), (1024, 1033, 517), (1, 8191, 64), (13, 8199, 40)]
+
+
+@pytest.mark.parametrize("shape", SPLIT_EDGES, ids=["x".join(map(str, s)) for s in SPLIT_EDGES])
+def test_split_path_edges(shape):
+    """Through the direct + narrow split: K entirely inside the narrow kernel's element tail
+    (K <= 8), at its boundaries (8, 9, 16), one k-block plus a tail, K = 0 (C = epilogue of
+    the bias), and a single row or 13 rows of A."""
+    M, N, K = shape
+    A, B, bias = workloads.make_inputs(M, N, K, "normal", with_bias=True, seed=K + 7)
+    Ad, Bd, biasd = _dev(A), _dev(B), _dev(bias)
+    for e in ("bias", "bias_gelu"):
+        pad = 1024
+        buf = torch.full((M * N + 2 * pad,), float("nan"), dtype=torch.float16, device=DEV)
+        out = buf[pad:pad + M * N].view(M, N)
+        cid = g.select(Ad, Bd, biasd, e, out=out)
+        assert g.mi355gemm_config_info(cid)["direct"] == 1, g.mi355gemm_config_name(cid)
+        print("split edge", shape, e, g.mi355gemm_config_name(cid), flush=True)
+        g.gemm(Ad, Bd, biasd, e, out=out)
+        torch.cuda.synchronize()
+        assert torch.isnan(buf[:pad]).all().item() and torch.isnan(buf[pad + M * N:]).all().item()
+        assert_parity(out, oracle.gemm(A, B, bias, e), "split edge %s %s" % (shape, e))
