@@ -46,9 +46,13 @@ MI355_DIRECT(D256x128)
 MI355_DIRECT(D128)
 MI355_DIRECT(D128w4)
 #undef MI355_DIRECT
-template __global__ void gemm_narrow<0>(GemmArgs);
-template __global__ void gemm_narrow<1>(GemmArgs);
-template __global__ void gemm_narrow<2>(GemmArgs);
+#define MI355_NARROW(KS)                                   \
+    template __global__ void gemm_narrow<0, KS>(GemmArgs); \
+    template __global__ void gemm_narrow<1, KS>(GemmArgs); \
+    template __global__ void gemm_narrow<2, KS>(GemmArgs);
+MI355_NARROW(4)
+MI355_NARROW(1)
+#undef MI355_NARROW
 }  // namespace mi355
 
 namespace {
@@ -75,6 +79,7 @@ struct Config {
     bool a_vec, bc_vec;
     int group_m;
     KernelFn fn[3];   // per epilogue
+    bool narrow;      // vector-ALU kernel for at most bn (8) columns
 };
 
 template <class T, bool AV, bool BV>
@@ -82,7 +87,8 @@ Config staged_config(const char *name, int group_m)
 {
     return Config{name, false, T::BM, T::BN, T::BK, T::STAGES, T::WAVES_M, T::WAVES_N, 1, T::NT,
                   T::LDS_BYTES, AV, BV, group_m,
-                  {gemm_staged<T, AV, BV, 0>, gemm_staged<T, AV, BV, 1>, gemm_staged<T, AV, BV, 2>}};
+                  {gemm_staged<T, AV, BV, 0>, gemm_staged<T, AV, BV, 1>, gemm_staged<T, AV, BV, 2>},
+                  false};
 }
 
 template <class T>
@@ -91,7 +97,17 @@ Config direct_config(const char *name, int group_m)
     return Config{name, true, T::BM, T::BN, T::BK, T::STAGES, T::WAVES_M, T::WAVES_N, T::KGROUPS,
                   T::NT,
                   T::LDS_BYTES, false, true, group_m,
-                  {gemm_direct<T, 0>, gemm_direct<T, 1>, gemm_direct<T, 2>}};
+                  {gemm_direct<T, 0>, gemm_direct<T, 1>, gemm_direct<T, 2>}, false};
+}
+
+// Up to 8 columns; 4 waves per workgroup, KS of them splitting K for each 8-row group
+template <int KS>
+Config narrow_config(const char *name)
+{
+    using T = Narrow<KS>;
+    return Config{name, false, T::BM, T::NC, T::KB, 1, T::RG, 1, KS, T::NT,
+                  KS > 1 ? (int)(T::NW * 64 * sizeof(float)) : 0, false, false, 1,
+                  {gemm_narrow<0, KS>, gemm_narrow<1, KS>, gemm_narrow<2, KS>}, true};
 }
 
 const Config kConfigs[] = {
@@ -109,6 +125,8 @@ const Config kConfigs[] = {
     staged_config<T64, true, false>("s64x64x64_w2x1_av_bn", 8),
     staged_config<T64, false, true>("s64x64x64_w2x1_an_bv", 8),
     staged_config<T64, false, false>("s64x64x64_w2x1_an_bn", 8),
+    narrow_config<4>("n8x8x512_w1x1k4"),
+    narrow_config<1>("n32x8x512_w4x1"),
 };
 constexpr int kNumConfigs = (int)(sizeof(kConfigs) / sizeof(kConfigs[0]));
 
@@ -164,11 +182,24 @@ int64_t tiles(const Request &r, int bm, int bn)
     return ((r.M + bm - 1) / bm) * ((r.N + bn - 1) / bn);
 }
 
+int find_narrow(int k_groups)
+{
+    for (int i = 0; i < kNumConfigs; ++i)
+        if (kConfigs[i].narrow && kConfigs[i].k_groups == k_groups) return i;
+    return -1;
+}
+
+// Narrow variant for M rows (interleaved timings on MI355X, N = 1..8 and the last N % 8
+// columns of odd N): from 16384 rows the 4 waves on 4 row groups win (K = 4096: 39 us
+// against 47; 131072 x 512: 50 against 175), below it the 4 waves splitting K of 8 rows
+// (1024 x 65536: 62 us against 222).
+int narrow_for(int64_t M) { return find_narrow(M >= 16384 ? 1 : 4); }
+
 int find_staged(int bm, int bn, bool av, bool bv)
 {
     for (int i = 0; i < kNumConfigs; ++i) {
         const Config &c = kConfigs[i];
-        if (!c.direct && c.bm == bm && c.bn == bn && c.a_vec == av && c.bc_vec == bv) return i;
+        if (!c.direct && !c.narrow && c.bm == bm && c.bn == bn && c.a_vec == av && c.bc_vec == bv) return i;
     }
     return -1;
 }
@@ -187,7 +218,8 @@ int find_direct(int bm, int bn, int bk, int waves, int k_groups)
 // Can configuration c serve request r?  (Silent version of check_config.)
 bool config_fits(const Config &c, const Request &r)
 {
-    return c.lds_bytes <= kLdsBudget && (!c.a_vec || a_vector_ok(r)) && (!c.bc_vec || bc_vector_ok(r));
+    return c.lds_bytes <= kLdsBudget && (!c.a_vec || a_vector_ok(r)) && (!c.bc_vec || bc_vector_ok(r)) &&
+           (!c.narrow || r.N <= c.bn);
 }
 
 // Measured winners for exact shapes, written by the package's tune.py (an interleaved
@@ -243,6 +275,8 @@ int choose(const Request &r)
                                              : find_direct(128, 128, 64, 4, 1);
         if (t128 >= kCUs / 4) return find_direct(128, 128, 64, 8, 2);    // part of the chip idle
     }
+    // at most 8 columns: no tile contraction left; the narrow kernel reads A once
+    if (r.N <= 8) return narrow_for(r.M);
     if (tiles(r, 128, 128) >= kCUs / 2) return find_staged(128, 128, av, bv);
     return find_staged(64, 64, av, bv);
 }
@@ -261,6 +295,9 @@ mi355gemm_status check_config(const Config &c, const Request &r)
         return fail(MI355GEMM_EUNSUPPORTED,
                     "config %s moves B and C in vectors: needs N %% 8 == 0, 16-byte aligned B and C "
                     "and an 8-byte aligned bias", c.name);
+    if (c.narrow && r.N > c.bn)
+        return fail(MI355GEMM_EUNSUPPORTED, "config %s computes at most %d columns (N=%lld)", c.name,
+                    c.bn, (long long)r.N);
     return MI355GEMM_OK;
 }
 
@@ -291,33 +328,6 @@ mi355gemm_status launch(const Config &c, const Request &r, int64_t n_begin, int6
     return MI355GEMM_OK;
 }
 
-// Launch the narrow kernel on columns [n_begin, n_begin + n_width), n_width <= 8.  Its
-// 16-byte B pieces stay inside B only when rows are at least 8 elements apart.
-mi355gemm_status launch_narrow(const Request &r, int64_t n_begin, int64_t n_width, hipStream_t stream)
-{
-    if (n_width < 1 || n_width > Narrow::NC || r.N < 8)
-        return fail(MI355GEMM_EUNSUPPORTED, "narrow kernel needs 1..8 columns and N >= 8 (N=%lld)",
-                    (long long)r.N);
-    GemmArgs a;
-    a.A = static_cast<const f16 *>(r.A);
-    a.B = r.B != nullptr ? static_cast<const f16 *>(r.B) + n_begin : nullptr;
-    a.C = static_cast<f16 *>(r.C) + n_begin;
-    a.bias = r.bias != nullptr ? static_cast<const f16 *>(r.bias) + n_begin : nullptr;
-    a.M = (int)r.M;
-    a.N = (int)n_width;
-    a.K = (int)r.K;
-    a.ldb = a.ldc = (int)r.N;
-    a.tiles_m = (int)((r.M + Narrow::RW - 1) / Narrow::RW);
-    a.tiles_n = 1;
-    a.group_m = 1;
-    static void (*const fn[3])(GemmArgs) = {gemm_narrow<0>, gemm_narrow<1>, gemm_narrow<2>};
-    hipLaunchKernelGGL(fn[r.epi], dim3((unsigned)a.tiles_m), dim3(Narrow::NT), 0, stream, a);
-    const hipError_t e = hipGetLastError();
-    if (e != hipSuccess)
-        return fail(MI355GEMM_EHIP, "launch of the narrow kernel failed: %s", hipGetErrorString(e));
-    return MI355GEMM_OK;
-}
-
 mi355gemm_status run(const Request &r, void *stream, int forced)
 {
     mi355gemm_status st = validate(r);
@@ -340,7 +350,7 @@ mi355gemm_status run(const Request &r, void *stream, int forced)
         const int64_t n8 = r.N & ~(int64_t)7;
         const mi355gemm_status s2 = launch(c, r, 0, n8, hs);
         if (s2 != MI355GEMM_OK || n8 == r.N) return s2;
-        return launch_narrow(r, n8, r.N - n8, hs);
+        return launch(kConfigs[narrow_for(r.M)], r, n8, r.N - n8, hs);
     }
     return launch(c, r, 0, r.N, hs);
 }
@@ -516,6 +526,7 @@ mi355gemm_status mi355gemm_config_info(int config_id, mi355gemm_config_desc *out
     out->bc_vector = c.bc_vec;
     out->group_m = c.group_m;
     out->direct = c.direct;
+    out->narrow = c.narrow;
     return MI355GEMM_OK;
 }
 

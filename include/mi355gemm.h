@@ -65,9 +65,10 @@ typedef enum {
  * direct one but the rows of B and C are not 16-byte friendly (N % 8 != 0, B or C not
  * 16-byte aligned, or the bias not 8-byte aligned), the call makes two launches on
  * `stream`: the direct kernel computes columns [0, N & ~7) with unaligned 16-byte
- * accesses, and a narrow kernel (fp32 vector multiply-adds, 8 rows per workgroup) the
- * last N % 8 columns.  Smaller problems take the register-staged kernels, whose
- * 2-byte load variants accept any alignment.
+ * accesses, and a narrow kernel (fp32 vector multiply-adds, any alignment) the last
+ * N % 8 columns.  Problems with at most 8 columns that the direct kernel does not take
+ * run on the narrow kernel alone; other small problems take the register-staged
+ * kernels, whose 2-byte load variants accept any alignment.
  *
  * Errors: EINVAL for negative sizes, null pointers with work to do, an unknown
  * epilogue, a bias epilogue with bias == NULL, or a misaligned pointer; EUNSUPPORTED
@@ -198,15 +199,19 @@ typedef struct {
     int bc_vector;                  /* 1: B loaded and C stored in vectors (N % 8 == 0) */
     int group_m;                    /* tile-rows per group in the tile order */
     int direct;                     /* 1: HBM -> LDS copies without register staging */
+    int narrow;                     /* 1: vector-ALU kernel for at most block_n (8) columns:
+                                       block_m rows per workgroup, k_groups waves on
+                                       interleaved block_k-wide k-blocks, no LDS tiles */
 } mi355gemm_config_desc;
 
 /* Number of compiled configurations (ids 0 .. n-1). Host-only. */
 int mi355gemm_num_configs(void);
 
 /* Static name of a configuration, or NULL for an unknown id.  Host-only.  Names read
- * <d|s><BM>x<BN>x<BK>_w<waves_m>x<waves_n>[k<k_groups>]_...: d = direct HBM -> LDS kernel
+ * <d|s|n><BM>x<BN>x<BK>_w<waves_m>x<waves_n>[k<k_groups>]_...: d = direct HBM -> LDS kernel
  * (suffix s<stages>), s = register-staged kernel (suffix av/an: A in 16-byte / 2-byte
- * loads, bv/bn: B and C likewise), e.g. "d128x128x64_w2x2_s4", "s64x64x64_w2x1_av_bv". */
+ * loads, bv/bn: B and C likewise), n = narrow vector-ALU kernel for N <= 8 (any
+ * alignment), e.g. "d128x128x64_w2x2_s4", "s64x64x64_w2x1_av_bv", "n8x8x512_w1x1k4". */
 const char *mi355gemm_config_name(int config_id);
 
 /* Fill *out for config_id; EINVAL for an unknown id or NULL out. Host-only. */

@@ -52,7 +52,18 @@ def test_config_table_is_consistent():
     names = [c["name"] for c in cfgs]
     assert len(set(names)) == len(names)
     assert any(c["direct"] for c in cfgs) and any(not c["direct"] for c in cfgs)
+    assert sorted(c["k_groups"] for c in cfgs if c["narrow"]) == [1, 4]
     for c in cfgs:
+        if c["narrow"]:
+            # 4 waves: waves_m groups of 8 rows, k_groups waves splitting K for each, over
+            # 512-wide k-blocks and 8 columns; LDS holds only the k-groups' partial sums
+            # (one fp32 per lane and wave); any alignment
+            assert c["waves_m"] * c["k_groups"] == 4 and c["waves_n"] == 1
+            assert (c["block_m"], c["block_n"], c["block_k"]) == (8 * c["waves_m"], 8, 512)
+            assert c["threads"] == 256
+            assert c["lds_bytes"] == (4 * 64 * 4 if c["k_groups"] > 1 else 0)
+            assert c["a_vector"] == 0 and c["bc_vector"] == 0 and c["direct"] == 0
+            continue
         if c["direct"]:
             # ring of STAGES buffers of the A (BM x BK) and B (BK x BN) tiles, XOR-swizzled;
             # A may have any alignment (unaligned LDS-DMA, K tail patched), B and C not
@@ -321,3 +332,26 @@ def test_selector_splits_unfriendly_rows(shape, ptr_off, want):
     M, N, K = shape
     cid = g.mi355gemm_select(M, N, K, 2, P16, P16 + ptr_off, P16 + ptr_off, P16)
     assert g.mi355gemm_config_name(cid) == want, g.mi355gemm_last_error()
+
+
+@pytest.mark.parametrize("shape,c_off,want", [
+    ((8192, 1, 8192), 0, "n8x8x512_w1x1k4"),       # at most 8 columns: the narrow kernel,
+    ((2048, 7, 2048), 0, "n8x8x512_w1x1k4"),       # 4 waves splitting K below 16384 rows,
+    ((1024, 3, 65536), 0, "n8x8x512_w1x1k4"),
+    ((16384, 1, 4096), 0, "n32x8x512_w4x1"),       # 4 row groups from 16384 rows
+    ((131072, 5, 512), 0, "n32x8x512_w4x1"),
+    ((2048, 8, 2048), 0, "n8x8x512_w1x1k4"),       # N = 8 below the direct kernel's 64 tiles
+    ((16384, 8, 4096), 0, "d128x128x64_w2x2k2_s4"),  # N = 8, enough tiles: direct
+    ((16384, 8, 4096), 2, "n32x8x512_w4x1"),       # the same with C only 2-byte aligned
+])
+def test_selector_narrow_rules(shape, c_off, want):
+    M, N, K = shape
+    cid = g.mi355gemm_select(M, N, K, 0, P16, P16, P16 + c_off, None)
+    assert g.mi355gemm_config_name(cid) == want, g.mi355gemm_last_error()
+
+
+def test_forced_narrow_config_rejects_more_than_8_columns():
+    for c in g.configs():
+        if c["narrow"]:
+            assert _status(64, 9, 64, config=c["id"]) == g.EUNSUPPORTED
+            assert "at most 8 columns" in g.mi355gemm_last_error()

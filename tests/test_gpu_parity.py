@@ -34,6 +34,8 @@ def _run(A, B, bias, epi, config=None, out=None):
 
 
 def _compatible(cfg, M, N, K):
+    if cfg["narrow"] and N > cfg["block_n"]:
+        return False
     if cfg["a_vector"] and K % 8:
         return False
     if cfg["bc_vector"] and N % 8:
@@ -325,7 +327,7 @@ def test_direct_kernel_k_tail_and_misaligned_a(shape):
 # alignment) and a narrow-load kernel the last N % 8 columns, on the same stream.
 
 SPLIT_SHAPES = [(1024, 1031, 300), (2048, 2047, 2048), (1000, 3001, 777), (768, 2050, 64),
-                (1300, 1029, 1001), (1040, 1031, 4999)]
+                (1300, 1029, 1001), (1040, 1031, 4999), (16389, 1027, 75)]
 
 
 @pytest.mark.parametrize("shape", SPLIT_SHAPES, ids=["x".join(map(str, s)) for s in SPLIT_SHAPES])
@@ -416,3 +418,74 @@ def test_split_path_edges(shape):
         torch.cuda.synchronize()
         assert torch.isnan(buf[:pad]).all().item() and torch.isnan(buf[pad + M * N:]).all().item()
         assert_parity(out, oracle.gemm(A, B, bias, e), "split edge %s %s" % (shape, e))
+
+
+
+# ---- at most 8 columns: the narrow kernel -------------------------------------------------
+
+NARROW_SHAPES = [(1, 1, 1), (7, 1, 8), (9, 2, 9), (64, 3, 15), (130, 4, 16), (1000, 5, 17),
+                 (257, 6, 100), (64, 7, 511), (200, 8, 512), (33, 1, 513), (520, 3, 2055),
+                 (1024, 8, 0), (1024, 7, 4097)]
+
+
+@pytest.mark.parametrize("shape", NARROW_SHAPES, ids=["x".join(map(str, s)) for s in NARROW_SHAPES])
+def test_narrow_kernel_parity(shape):
+    """N <= 8 takes the narrow kernel: K inside its element tail (K < 16 with rows closer than
+    8 elements), at block boundaries, several blocks per wave; ragged M; every epilogue;
+    guard bands around C."""
+    M, N, K = shape
+    A, B, bias = workloads.make_inputs(M, N, K, "normal", with_bias=True, seed=M * 31 + N * 7 + K)
+    Ad, Bd, biasd = _dev(A), _dev(B), _dev(bias)
+    for e in EPIS:
+        pad = 256
+        buf = torch.full((M * N + 2 * pad,), float("nan"), dtype=torch.float16, device=DEV)
+        out = buf[pad:pad + M * N].view(M, N)
+        cid = g.select(Ad, Bd, biasd if e != "none" else None, e, out=out)
+        assert g.mi355gemm_config_info(cid)["narrow"] == 1, g.mi355gemm_config_name(cid)
+        print("narrow", shape, e, flush=True)
+        g.gemm(Ad, Bd, biasd if e != "none" else None, e, out=out)
+        torch.cuda.synchronize()
+        assert torch.isnan(buf[:pad]).all().item() and torch.isnan(buf[pad + M * N:]).all().item()
+        ref = oracle.gemm(A, B, bias, e)
+        assert_parity(out, ref, "narrow %s %s" % (shape, e))
+        for cfg in all_configs():
+            if not cfg["narrow"]:
+                continue
+            print("   forced", cfg["name"], flush=True)
+            out.fill_(float("nan"))
+            g.gemm(Ad, Bd, biasd if e != "none" else None, e, out=out, config=cfg["id"])
+            torch.cuda.synchronize()
+            assert torch.isnan(buf[:pad]).all().item() and torch.isnan(buf[pad + M * N:]).all().item()
+            assert_parity(out, ref, "narrow %s %s %s" % (cfg["name"], shape, e))
+
+
+@pytest.mark.parametrize("N", [1, 3, 8])
+def test_narrow_kernel_at_any_alignment(N):
+    """A, B, C and bias each shifted by one element (2-byte aligned only)."""
+    M, K = 300, 1001
+    A, B, bias = workloads.make_inputs(M, N, K, "uniform", with_bias=True, seed=N)
+
+    def shifted(t):
+        t = t.to(DEV).reshape(-1)
+        b = torch.zeros(t.numel() + 1, dtype=torch.float16, device=DEV)
+        b[1:] = t
+        return b[1:]
+    Ad, Bd, biasd = shifted(A).view(M, K), shifted(B).view(K, N), shifted(bias)
+    buf = torch.full((M * N + 2 * 65,), float("nan"), dtype=torch.float16, device=DEV)
+    out = buf[65:65 + M * N].view(M, N)
+    cid = g.select(Ad, Bd, biasd, "bias_gelu", out=out)
+    assert g.mi355gemm_config_info(cid)["narrow"] == 1
+    g.gemm(Ad, Bd, biasd, "bias_gelu", out=out)
+    torch.cuda.synchronize()
+    assert torch.isnan(buf[:65]).all().item() and torch.isnan(buf[65 + M * N:]).all().item()
+    assert_parity(out, oracle.gemm(A, B, bias, "bias_gelu"), "narrow misaligned N=%d" % N)
+
+
+def test_narrow_config_rejects_wide_problems():
+    cid = [c["id"] for c in all_configs() if c["narrow"]][0]
+    A = torch.zeros((16, 16), dtype=torch.float16, device=DEV)
+    B = torch.zeros((16, 9), dtype=torch.float16, device=DEV)
+    C = torch.zeros((16, 9), dtype=torch.float16, device=DEV)
+    st = g.mi355gemm_gemm_config(16, 9, 16, A.data_ptr(), B.data_ptr(), C.data_ptr(), None, 0,
+                                 torch.cuda.current_stream().cuda_stream, cid)
+    assert st == g.EUNSUPPORTED and "at most 8 columns" in g.mi355gemm_last_error()
