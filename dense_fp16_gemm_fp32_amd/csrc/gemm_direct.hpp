@@ -1,7 +1,10 @@
 // Direct-to-LDS GEMM kernel for gfx950: the fast path whenever B and C rows are 16-byte
 // friendly (N % 8 == 0, 16-byte aligned B and C, 8-byte aligned bias).  A may have any
 // 2-byte alignment and any K: the LDS-DMA copy takes unaligned source offsets, and the
-// one chunk per row that straddles K (K % 8 != 0) is patched in LDS (see load_tail).
+// one chunk per row that straddles K (K % 8 != 0) is patched in LDS (see load_tail) by
+// the KTAIL variant of the kernel.  The variant for K % 8 == 0 leaves the patch out: the
+// patch holds 8 registers per A piece through the whole K loop, which made the
+// 256x256x64 eight-wave tile spill.
 //
 // One workgroup computes one BM x BN macro-tile of C with WAVES_M x WAVES_N x KGROUPS
 // wavefronts (two per SIMD in the shipped configurations, so one wave's LDS reads and
@@ -439,7 +442,8 @@ __device__ __forceinline__ void static_for(F &&f)
     static_for(std::make_integer_sequence<int, N>{}, f);
 }
 
-template <class T, int EPI>
+// KTAIL = false: the variant for K % 8 == 0, without the K-tail patch.
+template <class T, int EPI, bool KTAIL>
 __global__ void __launch_bounds__(T::NT) gemm_direct(GemmArgs p)
 {
     using St = Stage<T>;
@@ -454,7 +458,7 @@ __global__ void __launch_bounds__(T::NT) gemm_direct(GemmArgs p)
     DirectWave<T> w;
     w.init(p, m0, n0, rows_valid, p.N - n0);
     if constexpr (EPI != 0) w.load_bias(p);
-    const bool k_tail = (p.K & 7) != 0;
+    const bool k_tail = KTAIL && (p.K & 7) != 0;
     if (k_tail && nk > 0) w.load_tail(nk);
 
     St *const ring = reinterpret_cast<St *>(lds_raw);

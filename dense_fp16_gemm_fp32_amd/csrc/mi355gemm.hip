@@ -36,10 +36,13 @@ using T256 = Tile<256, 256, 64, 2, 2>;           // 4 waves of 128x128
 
 // Explicit instantiations: every kernel the configuration table points at gets a host
 // launch stub.
-#define MI355_DIRECT(T)                                   \
-    template __global__ void gemm_direct<T, 0>(GemmArgs); \
-    template __global__ void gemm_direct<T, 1>(GemmArgs); \
-    template __global__ void gemm_direct<T, 2>(GemmArgs);
+#define MI355_DIRECT(T)                                          \
+    template __global__ void gemm_direct<T, 0, false>(GemmArgs); \
+    template __global__ void gemm_direct<T, 1, false>(GemmArgs); \
+    template __global__ void gemm_direct<T, 2, false>(GemmArgs); \
+    template __global__ void gemm_direct<T, 0, true>(GemmArgs);  \
+    template __global__ void gemm_direct<T, 1, true>(GemmArgs);  \
+    template __global__ void gemm_direct<T, 2, true>(GemmArgs);
 MI355_DIRECT(D256)
 MI355_DIRECT(D256k64)
 MI355_DIRECT(D256x128)
@@ -78,7 +81,7 @@ struct Config {
     int bm, bn, bk, stages, waves_m, waves_n, k_groups, threads, lds_bytes;
     bool a_vec, bc_vec;
     int group_m;
-    KernelFn fn[3];   // per epilogue
+    KernelFn fn[2][3];   // [K % 8 != 0][epilogue]
     bool narrow;      // vector-ALU kernel for at most bn (8) columns
 };
 
@@ -87,7 +90,8 @@ Config staged_config(const char *name, int group_m)
 {
     return Config{name, false, T::BM, T::BN, T::BK, T::STAGES, T::WAVES_M, T::WAVES_N, 1, T::NT,
                   T::LDS_BYTES, AV, BV, group_m,
-                  {gemm_staged<T, AV, BV, 0>, gemm_staged<T, AV, BV, 1>, gemm_staged<T, AV, BV, 2>},
+                  {{gemm_staged<T, AV, BV, 0>, gemm_staged<T, AV, BV, 1>, gemm_staged<T, AV, BV, 2>},
+                   {gemm_staged<T, AV, BV, 0>, gemm_staged<T, AV, BV, 1>, gemm_staged<T, AV, BV, 2>}},
                   false};
 }
 
@@ -97,7 +101,9 @@ Config direct_config(const char *name, int group_m)
     return Config{name, true, T::BM, T::BN, T::BK, T::STAGES, T::WAVES_M, T::WAVES_N, T::KGROUPS,
                   T::NT,
                   T::LDS_BYTES, false, true, group_m,
-                  {gemm_direct<T, 0>, gemm_direct<T, 1>, gemm_direct<T, 2>}, false};
+                  {{gemm_direct<T, 0, false>, gemm_direct<T, 1, false>, gemm_direct<T, 2, false>},
+                   {gemm_direct<T, 0, true>, gemm_direct<T, 1, true>, gemm_direct<T, 2, true>}},
+                  false};
 }
 
 // Up to 8 columns; 4 waves per workgroup, KS of them splitting K for each 8-row group
@@ -107,7 +113,9 @@ Config narrow_config(const char *name)
     using T = Narrow<KS>;
     return Config{name, false, T::BM, T::NC, T::KB, 1, T::RG, 1, KS, T::NT,
                   KS > 1 ? (int)(T::NW * 64 * sizeof(float)) : 0, false, false, 1,
-                  {gemm_narrow<0, KS>, gemm_narrow<1, KS>, gemm_narrow<2, KS>}, true};
+                  {{gemm_narrow<0, KS>, gemm_narrow<1, KS>, gemm_narrow<2, KS>},
+                   {gemm_narrow<0, KS>, gemm_narrow<1, KS>, gemm_narrow<2, KS>}},
+                  true};
 }
 
 const Config kConfigs[] = {
@@ -321,7 +329,7 @@ mi355gemm_status launch(const Config &c, const Request &r, int64_t n_begin, int6
     const int64_t grid = (int64_t)a.tiles_m * a.tiles_n;
     if (grid >= ((int64_t)1 << 31))
         return fail(MI355GEMM_EUNSUPPORTED, "too many tiles (%lld)", (long long)grid);
-    hipLaunchKernelGGL(c.fn[r.epi], dim3((unsigned)grid), dim3(c.threads), 0, stream, a);
+    hipLaunchKernelGGL(c.fn[(r.K & 7) != 0][r.epi], dim3((unsigned)grid), dim3(c.threads), 0, stream, a);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess)
         return fail(MI355GEMM_EHIP, "launch of %s failed: %s", c.name, hipGetErrorString(e));
