@@ -262,7 +262,9 @@ int tuned_choice(const Request &r, bool av, bool bv)
 // runs at its power limit, where the lighter configurations are the steadier ones:
 // 256x256x64 tiles (8 waves, 2 stages) from one full wave of them, 128x128 tiles with 4
 // waves when they fill the chip; with part of the chip idle (fewer than 256 128x128
-// tiles) the two k-groups' extra latency hiding wins.  The register-staged kernels take
+// tiles) the two k-groups' extra latency hiding wins.  The 256x256x64 tile took over one
+// wave of big tiles from the 256x256x32 one once the K-tail patch moved into its own
+// kernel variant (the 64-deep tile had spilled registers before).  The register-staged kernels take
 // small problems and those whose B or C rows are not 16-byte friendly (the direct kernels
 // need N % 8 == 0 and 16-byte aligned B and C; A may have any alignment).
 int choose(const Request &r)
@@ -276,8 +278,7 @@ int choose(const Request &r)
     if (bv || r.N >= 64) {
         // measured with the interleaved tuner on MI355X (the table file records the runs)
         const int64_t t256 = tiles(r, 256, 256), t256x128 = tiles(r, 256, 128), t128 = tiles(r, 128, 128);
-        if (t256 >= 4 * kCUs) return find_direct(256, 256, 64, 8, 1);   // several waves of big tiles
-        if (t256 >= kCUs) return find_direct(256, 256, 32, 8, 1);        // about one wave of them
+        if (t256 >= kCUs) return find_direct(256, 256, 64, 8, 1);        // a wave of big tiles or more
         if (t256x128 >= kCUs) return find_direct(256, 128, 64, 8, 2);    // e.g. one GPU's share of 8192^3
         if (t128 >= kCUs) return r.K >= 4096 ? find_direct(128, 128, 64, 8, 2)   // long K: k-groups
                                              : find_direct(128, 128, 64, 4, 1);

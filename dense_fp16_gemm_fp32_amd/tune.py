@@ -13,12 +13,18 @@ as a wrong kernel would fail the sweep's numerical check).
 
 MI355X runs these GEMMs at its power limit, so single timings move by several percent
 from run to run: candidates are timed in interleaved rounds and compared by their median.
+The engine clock reacts to load within milliseconds, so the candidate timed first after
+a pause runs on a cooler part: the order reverses every other round, and each timing
+covers ``--ms`` milliseconds of back-to-back calls (default 20), long enough for the
+clock to settle.
 A shape gets a table entry only when its winner beats the configuration the selector's
 rules would pick by at least ``--margin`` (default 3%); otherwise the rules stand.
 
 The table is C source, ``csrc/tuned_table.inc``, compiled into the library (rebuild after
 writing it); ``mi355gemm_select`` consults it for an exact (M, N, K, epilogue, alignment)
-match before the rules.
+match before the rules.  Tune on a library built with an empty table: the rule choice the
+winners are compared with comes from ``mi355gemm_select``, so a shape that already has an
+entry would be compared with that entry and lose it.
 
 Usage (on the GPU):
   python -m dense_fp16_gemm_fp32_amd.tune [--shapes MxNxK[:epilogue[:dist]] ...]
@@ -83,7 +89,7 @@ def _time(fn, steps):
     return a.elapsed_time(b) / steps * 1e3   # us per call
 
 
-def tune(shapes, rounds=7, margin=0.03, log=print):
+def tune(shapes, rounds=7, margin=0.03, log=print, ms=20.0):
     """Returns a list of dicts, one per shape: the rule choice, every candidate's median
     time, the winner and whether it earns a table entry."""
     import torch
@@ -102,7 +108,8 @@ def tune(shapes, rounds=7, margin=0.03, log=print):
         ref = g.gemm(A, B, b_arg, epi).float()
         ref_norm = float(ref.norm())
         flops = 2.0 * M * N * K
-        steps = max(3, min(300, int(3e-3 / max(flops / 1e15, 1e-9))))   # about 3 ms per timing
+        # about `ms` milliseconds per timing at 1 PFLOP/s
+        steps = max(3, min(20000, int(ms * 1e-3 / max(flops / 1e15, 1e-9))))
         cands = []
         for cfg in g.configs():
             st = g.mi355gemm_gemm_config(M, N, K, A.data_ptr(), B.data_ptr(), out.data_ptr(),
@@ -119,8 +126,8 @@ def tune(shapes, rounds=7, margin=0.03, log=print):
                 continue
             cands.append(cfg)
         times = {c["name"]: [] for c in cands}
-        for _ in range(rounds):
-            for c in cands:
+        for rnd in range(rounds):
+            for c in (cands if rnd % 2 == 0 else cands[::-1]):
                 cid = c["id"]
                 for _ in range(2):
                     g.gemm(A, B, b_arg, epi, out=out, config=cid)
@@ -164,12 +171,13 @@ def main(argv=None):
     ap.add_argument("--shapes", nargs="*", default=None)
     ap.add_argument("--rounds", type=int, default=7)
     ap.add_argument("--margin", type=float, default=0.03)
+    ap.add_argument("--ms", type=float, default=20.0, help="milliseconds per timing")
     ap.add_argument("--write", action="store_true", help="write csrc/tuned_table.inc")
     ap.add_argument("--output", default=TABLE)
     args = ap.parse_args(argv)
     import torch
     shapes = [parse_shape(s) for s in args.shapes] if args.shapes else default_shapes()
-    res = tune(shapes, args.rounds, args.margin, log=lambda m: print(m, flush=True))
+    res = tune(shapes, args.rounds, args.margin, log=lambda m: print(m, flush=True), ms=args.ms)
     src = table_source(res, torch.cuda.get_device_properties(0).name)
     if args.write:
         with open(args.output, "w") as f:

@@ -301,8 +301,9 @@ def test_attention_argument_checks(args, want):
 
 @pytest.mark.parametrize("shape,want", [
     ((8192, 8192, 8192), "d256x256x64_w2x4_s2"),      # four waves of 256 x 256 tiles
-    ((4096, 4096, 4096), "d256x256x32_w2x4_s4"),      # one wave of them
-    ((16384, 2048, 1024), "d256x256x32_w2x4_s4"),
+    ((4096, 4096, 4096), "d256x256x64_w2x4_s2"),      # one wave of them
+    ((16384, 2048, 1024), "d256x256x64_w2x4_s2"),
+    ((2048, 8192, 4096), "d256x256x64_w2x4_s2"),
     ((8192, 1024, 8192), "d256x128x64_w2x2k2_s3"),    # one GPU's N share of 8192^3
     ((1024, 8192, 8192), "d256x128x64_w2x2k2_s3"),    # its M share
     ((2048, 2048, 8192), "d128x128x64_w2x2k2_s4"),    # 256 tiles, long K
