@@ -26,7 +26,8 @@ STATUS_NAMES = {OK: "OK", EINVAL: "EINVAL", EUNSUPPORTED: "EUNSUPPORTED", EHIP: 
 
 # Every symbol include/mi355gemm.h declares.
 EXPORTS = (
-    "mi355gemm_gemm", "mi355gemm_gemm_config", "mi355gemm_select", "mi355gemm_num_configs",
+    "mi355gemm_gemm", "mi355gemm_gemm_config", "mi355gemm_gemm_timed", "mi355gemm_select",
+    "mi355gemm_num_configs",
     "mi355gemm_config_name", "mi355gemm_config_info", "mi355gemm_lds_budget",
     "mi355gemm_last_error", "mi355gemm_version", "mi355gemm_vector_add", "mi355gemm_softmax",
     "mi355gemm_attention",
@@ -65,6 +66,8 @@ def library() -> ctypes.CDLL:
         lib.mi355gemm_gemm.restype = ci
         lib.mi355gemm_gemm_config.argtypes = [i64, i64, i64, p, p, p, p, ci, p, ci]
         lib.mi355gemm_gemm_config.restype = ci
+        lib.mi355gemm_gemm_timed.argtypes = [i64, i64, i64, p, p, p, p, ci, p, ci, p, p]
+        lib.mi355gemm_gemm_timed.restype = ci
         lib.mi355gemm_select.argtypes = [i64, i64, i64, ci, p, p, p, p]
         lib.mi355gemm_select.restype = ci
         lib.mi355gemm_num_configs.argtypes = []
@@ -98,6 +101,12 @@ def mi355gemm_gemm(M, N, K, A, B, C, bias, epi, stream) -> int:
 
 def mi355gemm_gemm_config(M, N, K, A, B, C, bias, epi, stream, config_id) -> int:
     return library().mi355gemm_gemm_config(M, N, K, A, B, C, bias, epi, stream, config_id)
+
+
+def mi355gemm_gemm_timed(M, N, K, A, B, C, bias, epi, stream, config_id, start_event,
+                         stop_event) -> int:
+    return library().mi355gemm_gemm_timed(M, N, K, A, B, C, bias, epi, stream, config_id,
+                                          start_event, stop_event)
 
 
 def mi355gemm_vector_add(n, a, b, c, stream) -> int:
@@ -191,11 +200,14 @@ except AttributeError:  # pragma: no cover - older torch
 
 def gemm(a: torch.Tensor, b: torch.Tensor, bias: torch.Tensor | None = None,
          epilogue="none", out: torch.Tensor | None = None, config: int | str | None = None,
-         stream: torch.cuda.Stream | None = None) -> torch.Tensor:
+         stream: torch.cuda.Stream | None = None, events=None) -> torch.Tensor:
     """``out = epilogue(a @ b [+ bias])`` on the GPU; a (M,K), b (K,N), bias (N,), fp16.
 
     Runs on `stream` (default: the current stream of a's device) and returns without
-    synchronising, like any other torch GPU op."""
+    synchronising, like any other torch GPU op.  `events`, a (start, stop) pair of
+    timing-enabled ``torch.cuda.Event`` that have been recorded at least once (so that
+    their HIP events exist), makes the kernels record them as they start and end
+    (``mi355gemm_gemm_timed``): ``start.elapsed_time(stop)`` is then the kernel time."""
     _check_tensor(a, "a", 2)
     _check_tensor(b, "b", 2)
     M, K = a.shape
@@ -222,14 +234,23 @@ def gemm(a: torch.Tensor, b: torch.Tensor, bias: torch.Tensor | None = None,
     idx = dev.index if dev.index is not None else torch.cuda.current_device()
     sptr = stream.cuda_stream if stream is not None else _raw_stream(idx)
     args = (M, N, K, a.data_ptr(), b.data_ptr(), out.data_ptr(), bptr, epi, sptr)
+    cid = -1 if config is None else (config_id(config) if isinstance(config, str) else int(config))
+    if events is not None:
+        ev = tuple(e.cuda_event if e is not None else None for e in events)
+        if len(ev) != 2 or any(h == 0 for h in ev):
+            raise ValueError("events must be a (start, stop) pair of torch.cuda.Event (or None), "
+                             "each recorded once before")
+
+    def call():
+        if events is not None:
+            return lib.mi355gemm_gemm_timed(*args, cid, ev[0], ev[1])
+        return lib.mi355gemm_gemm(*args) if cid < 0 else lib.mi355gemm_gemm_config(*args, cid)
     # the library launches on the calling thread's current HIP device
     if idx == torch.cuda.current_device():
-        st = (lib.mi355gemm_gemm(*args) if config is None else
-              lib.mi355gemm_gemm_config(*args, config_id(config) if isinstance(config, str) else int(config)))
+        st = call()
     else:
         with torch.cuda.device(idx):
-            st = (lib.mi355gemm_gemm(*args) if config is None else
-                  lib.mi355gemm_gemm_config(*args, config_id(config) if isinstance(config, str) else int(config)))
+            st = call()
     if st != OK:
         raise GemmError(st, mi355gemm_last_error())
     return out

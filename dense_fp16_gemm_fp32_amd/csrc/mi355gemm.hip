@@ -3,6 +3,7 @@
 // are documented in include/mi355gemm.h.
 #include "mi355gemm.h"
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
@@ -311,9 +312,11 @@ mi355gemm_status check_config(const Config &c, const Request &r)
 }
 
 // Launch configuration c on columns [n_begin, n_begin + n_width) of the request (B, C and
-// bias offset by n_begin, rows still N apart).
+// bias offset by n_begin, rows still N apart).  Non-null events are recorded by the
+// dispatch itself as the kernel starts (ev_start) and ends (ev_stop).
 mi355gemm_status launch(const Config &c, const Request &r, int64_t n_begin, int64_t n_width,
-                        hipStream_t stream)
+                        hipStream_t stream, hipEvent_t ev_start = nullptr,
+                        hipEvent_t ev_stop = nullptr)
 {
     GemmArgs a;
     a.A = static_cast<const f16 *>(r.A);
@@ -330,14 +333,20 @@ mi355gemm_status launch(const Config &c, const Request &r, int64_t n_begin, int6
     const int64_t grid = (int64_t)a.tiles_m * a.tiles_n;
     if (grid >= ((int64_t)1 << 31))
         return fail(MI355GEMM_EUNSUPPORTED, "too many tiles (%lld)", (long long)grid);
-    hipLaunchKernelGGL(c.fn[(r.K & 7) != 0][r.epi], dim3((unsigned)grid), dim3(c.threads), 0, stream, a);
+    const KernelFn fn = c.fn[(r.K & 7) != 0][r.epi];
+    if (ev_start != nullptr || ev_stop != nullptr)
+        hipExtLaunchKernelGGL(fn, dim3((unsigned)grid), dim3(c.threads), 0, stream, ev_start,
+                              ev_stop, 0, a);
+    else
+        hipLaunchKernelGGL(fn, dim3((unsigned)grid), dim3(c.threads), 0, stream, a);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess)
         return fail(MI355GEMM_EHIP, "launch of %s failed: %s", c.name, hipGetErrorString(e));
     return MI355GEMM_OK;
 }
 
-mi355gemm_status run(const Request &r, void *stream, int forced)
+mi355gemm_status run(const Request &r, void *stream, int forced, hipEvent_t ev_start = nullptr,
+                     hipEvent_t ev_stop = nullptr)
 {
     mi355gemm_status st = validate(r);
     if (st != MI355GEMM_OK) return st;
@@ -357,11 +366,12 @@ mi355gemm_status run(const Request &r, void *stream, int forced)
         // to the last multiple of 8 (at any 2-byte alignment its 16-byte pieces then never
         // straddle the end of a row's columns), the narrow kernel the last N % 8
         const int64_t n8 = r.N & ~(int64_t)7;
-        const mi355gemm_status s2 = launch(c, r, 0, n8, hs);
-        if (s2 != MI355GEMM_OK || n8 == r.N) return s2;
-        return launch(kConfigs[narrow_for(r.M)], r, n8, r.N - n8, hs);
+        const bool two = n8 != r.N;
+        const mi355gemm_status s2 = launch(c, r, 0, n8, hs, ev_start, two ? nullptr : ev_stop);
+        if (s2 != MI355GEMM_OK || !two) return s2;
+        return launch(kConfigs[narrow_for(r.M)], r, n8, r.N - n8, hs, nullptr, ev_stop);
     }
-    return launch(c, r, 0, r.N, hs);
+    return launch(c, r, 0, r.N, hs, ev_start, ev_stop);
 }
 
 }  // namespace
@@ -382,6 +392,17 @@ mi355gemm_status mi355gemm_gemm_config(int64_t M, int64_t N, int64_t K, const vo
     g_last_error[0] = 0;
     if (config_id < 0) return fail(MI355GEMM_EINVAL, "unknown config id %d", config_id);
     return run(Request{M, N, K, A, B, bias, C, epi}, stream, config_id);
+}
+
+mi355gemm_status mi355gemm_gemm_timed(int64_t M, int64_t N, int64_t K, const void *A,
+                                      const void *B, void *C, const void *bias, int epi,
+                                      void *stream, int config_id, void *start_event,
+                                      void *stop_event)
+{
+    g_last_error[0] = 0;
+    if (config_id < -1) return fail(MI355GEMM_EINVAL, "unknown config id %d", config_id);
+    return run(Request{M, N, K, A, B, bias, C, epi}, stream, config_id,
+               static_cast<hipEvent_t>(start_event), static_cast<hipEvent_t>(stop_event));
 }
 
 int mi355gemm_select(int64_t M, int64_t N, int64_t K, int epi, const void *A, const void *B,

@@ -94,6 +94,22 @@ mi355gemm_status mi355gemm_gemm_config(int64_t M, int64_t N, int64_t K,
                                        int config_id);
 
 /*
+ * As mi355gemm_gemm_config (config_id = -1: the selector's choice, as mi355gemm_gemm),
+ * and in addition records two caller-created HIP events (hipEvent_t with timing enabled)
+ * from the kernel dispatch itself: start_event as the call's first kernel starts,
+ * stop_event as its last kernel ends (hipExtLaunchKernel).  hipEventElapsedTime(start,
+ * stop) is then the kernels' own duration, the figure a kernel trace reports, without
+ * the dispatch latency that events recorded before and after the call on the stream
+ * also count.  For benchmarks: the tutorial times its kernels with device events
+ * (thecryptopost.io page, section 2, bench()).  Either event may be NULL.  A call with
+ * nothing to launch (M == 0 or N == 0) records neither; errors as mi355gemm_gemm_config.
+ */
+mi355gemm_status mi355gemm_gemm_timed(int64_t M, int64_t N, int64_t K,
+                                      const void *A, const void *B, void *C,
+                                      const void *bias, int epi, void *stream,
+                                      int config_id, void *start_event, void *stop_event);
+
+/*
  * The configuration mi355gemm_gemm would launch for these arguments, or -1 (with
  * last_error set) if the arguments are invalid.  Host-only: makes no HIP call.
  * The choice is keyed on the shape and on pointer/leading-dimension alignment; the

@@ -30,7 +30,7 @@ def header_functions():
 
 def test_library_exports_every_declared_symbol():
     declared = header_functions()
-    assert len(declared) == 12
+    assert len(declared) == 13
     assert sorted(g.EXPORTS) == declared
     lib = g.library()
     for name in declared:
@@ -113,12 +113,34 @@ def test_validation_errors(args, want):
     assert g.mi355gemm_last_error() != ""
 
 
+@pytest.mark.parametrize("args,want", [
+    (dict(M=-1, N=4, K=4), g.EINVAL),
+    (dict(M=4, N=4, K=4, C=None), g.EINVAL),
+    (dict(M=4, N=4, K=4, epi=2), g.EINVAL),          # bias epilogue without bias
+    (dict(M=4, N=4, K=4, A=P16 + 1), g.EINVAL),
+    (dict(M=4, N=1 << 22, K=4), g.EUNSUPPORTED),
+    (dict(M=4, N=4, K=4, config=99), g.EINVAL),
+    (dict(M=4, N=4, K=4, config=-2), g.EINVAL),      # -1 is the selector's choice
+])
+def test_timed_entry_validates_like_the_others(args, want):
+    """mi355gemm_gemm_timed checks its arguments as mi355gemm_gemm_config does, before any
+    HIP call (the events are never touched on an error)."""
+    a = dict(M=4, N=4, K=4, A=P16, B=P16, C=P16, bias=None, epi=0, config=-1)
+    a.update(args)
+    st = g.mi355gemm_gemm_timed(a["M"], a["N"], a["K"], a["A"], a["B"], a["C"], a["bias"],
+                                a["epi"], None, a["config"], None, None)
+    assert st == want
+    assert g.mi355gemm_last_error() != ""
+
+
 def test_empty_problems_are_ok_without_launch():
     # M == 0 or N == 0: nothing to compute, OK even with NULL pointers
     assert _status(0, 16, 16, A=None, B=None, C=None) == g.OK
     assert _status(16, 0, 16, A=None, B=None, C=None) == g.OK
     assert _status(0, 0, 0, A=None, B=None, C=None, epi=2) == g.OK
     assert g.mi355gemm_last_error() == ""
+    # the timed entry with nothing to launch records no event (none is passed here)
+    assert g.mi355gemm_gemm_timed(0, 16, 16, None, None, None, None, 0, None, -1, None, None) == g.OK
 
 
 def test_forced_vector_config_rejects_unaligned_shapes():
