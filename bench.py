@@ -70,6 +70,9 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=500)
     ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--min-warmup-ms", type=float, default=MIN_WARMUP_MS,
+                    help="keep warming up past --warmup calls until this many milliseconds "
+                         "have passed (0: exactly --warmup calls)")
     ap.add_argument("--workload", default=HEADLINE)
     ap.add_argument("--epilogue", default=None, help="override the workload's epilogue")
     ap.add_argument("--config", default=None, help="force a kernel configuration by name")
@@ -85,8 +88,38 @@ def parse():
     return ap.parse_args()
 
 
-def time_gemm(lib, A, B, bias, epi, out, steps, warmup, config=None):
-    """Two timed passes of `steps` calls each, after `warmup` untimed calls.
+# Untimed warm-up lasts at least this long by default.  After a pause the engine clock
+# needs tens of milliseconds of load to settle: on MI355X the 2048^3 step took 25.2 us
+# after 20 warm-up calls (0.5 ms) and 21.6 us after 2000 (45 ms); 8192^3 926 us after 20
+# and 902 us after 2000.
+MIN_WARMUP_MS = 100.0
+
+
+def warm_up(fn, calls, min_ms):
+    """`calls` untimed calls of fn, then more until at least `min_ms` milliseconds have
+    passed since the first, so the timed region starts on a settled clock.  Returns the
+    number of calls made."""
+    import torch
+    t0 = time.perf_counter()
+    n = 0
+    for _ in range(max(calls, 1)):
+        fn()
+        n += 1
+    torch.cuda.synchronize()
+    while True:
+        el = (time.perf_counter() - t0) * 1e3
+        if el >= min_ms:
+            return n
+        batch = max(1, min(100000, int((min_ms - el) / (el / n)) + 1))
+        for _ in range(batch):
+            fn()
+        n += batch
+        torch.cuda.synchronize()
+
+
+def time_gemm(lib, A, B, bias, epi, out, steps, warmup, config=None, min_warm_ms=0.0):
+    """Three timed passes of `steps` calls each, after `warmup` untimed calls (and more,
+    up to `min_warm_ms` milliseconds of them, see warm_up).
 
     Pass 1 (the step time): wall clock between synchronisations around the back-to-back
     calls, and device events at both ends of the same region on the launch stream.
@@ -97,12 +130,10 @@ def time_gemm(lib, A, B, bias, epi, out, steps, warmup, config=None):
     Pass 3: an event pair recorded on the stream around every call; it also counts the
     dispatch latency of each launch, about 1.6 us more than the kernel time at 2048^3.
     Returns (ms per step by wall clock, ms per step by events, mean, median and minimum
-    ms per launch from pass 2, mean ms per call from pass 3)."""
+    ms per launch from pass 2, mean ms per call from pass 3, warm-up calls made)."""
     import torch
     stream = torch.cuda.current_stream()
-    for _ in range(warmup):
-        lib.gemm(A, B, bias, epi, out=out, config=config)
-    torch.cuda.synchronize()
+    warm = warm_up(lambda: lib.gemm(A, B, bias, epi, out=out, config=config), warmup, min_warm_ms)
     start = torch.cuda.Event(enable_timing=True)
     stop = torch.cuda.Event(enable_timing=True)
     t0 = time.perf_counter()
@@ -132,7 +163,7 @@ def time_gemm(lib, A, B, bias, epi, out, steps, warmup, config=None):
         b.record(stream)
     torch.cuda.synchronize()
     call_ms = sum(a.elapsed_time(b) for a, b in pairs) / steps
-    return wall_ms, event_ms, kernel_ms, per[len(per) // 2], per[0], call_ms
+    return wall_ms, event_ms, kernel_ms, per[len(per) // 2], per[0], call_ms, warm
 
 
 def _sha16(t) -> str:
@@ -152,7 +183,7 @@ def inputs_sha256(w, epi) -> dict:
     return out
 
 
-def run_cold(lib, w, steps, min_bytes=256 << 20):
+def run_cold(lib, w, steps, min_warm_ms=MIN_WARMUP_MS, min_bytes=256 << 20):
     """The workload with cold caches: enough copies of A and B (more than min_bytes in
     all, past the L2s and the Infinity Cache) that each call reads operands the previous
     calls did not touch; kernel time from the dispatch's own events, mean and median."""
@@ -165,9 +196,12 @@ def run_cold(lib, w, steps, min_bytes=256 << 20):
     Bs = [B.to("cuda:0") for _ in range(n)]
     out = torch.empty((w.M, w.N), dtype=torch.float16, device="cuda:0")
     stream = torch.cuda.current_stream()
-    for i in range(n):
-        lib.gemm(As[i], Bs[i], out=out)
-    torch.cuda.synchronize()
+    turn = [0]
+
+    def call():
+        lib.gemm(As[turn[0] % n], Bs[turn[0] % n], out=out)
+        turn[0] += 1
+    warm_up(call, n, min_warm_ms)
     pairs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
              for _ in range(steps)]
     for a, b in pairs:              # creates the HIP events the launches re-record
@@ -232,7 +266,7 @@ def cpu_oracle_by_workload(max_gflop=20.0):
     return out
 
 
-def run_workload(lib, w, epi, steps, warmup, config=None):
+def run_workload(lib, w, epi, steps, warmup, config=None, min_warm_ms=MIN_WARMUP_MS):
     import torch
     import workloads
     A, B, bias = workloads.make_inputs(w.M, w.N, w.K, w.dist, with_bias=(epi != "none"), seed=w.seed)
@@ -241,8 +275,8 @@ def run_workload(lib, w, epi, steps, warmup, config=None):
     bias = bias.to(dev) if bias is not None else None
     out = torch.empty((w.M, w.N), dtype=torch.float16, device=dev)
     cid = lib.select(A, B, bias, epi, out=out) if config is None else lib.config_id(config)
-    wall_ms, event_ms, kernel_ms, kernel_med, kernel_min, call_ms = time_gemm(
-        lib, A, B, bias, epi, out, steps, warmup, config)
+    wall_ms, event_ms, kernel_ms, kernel_med, kernel_min, call_ms, warm = time_gemm(
+        lib, A, B, bias, epi, out, steps, warmup, config, min_warm_ms)
     tflops = w.flops / (wall_ms * 1e-3) / 1e12
     return {
         "workload": w.name, "M": w.M, "N": w.N, "K": w.K, "epilogue": epi,
@@ -254,6 +288,7 @@ def run_workload(lib, w, epi, steps, warmup, config=None):
         "kernel_median_us": kernel_med * 1e3,
         "kernel_min_us": kernel_min * 1e3,
         "call_event_pair_us": call_ms * 1e3,
+        "warmup_calls": warm,
         "inputs_sha256_16": inputs_sha256(w, epi),
         "kernel_tflops": w.flops / (kernel_ms * 1e-3) / 1e12,
         "algorithmic_GBps": w.algorithmic_bytes(epi) / (kernel_ms * 1e-3) / 1e9,
@@ -261,7 +296,7 @@ def run_workload(lib, w, epi, steps, warmup, config=None):
     }
 
 
-def run_vector_add(lib, n, steps, warmup):
+def run_vector_add(lib, n, steps, warmup, min_warm_ms=MIN_WARMUP_MS):
     """The tutorial's first kernel at n elements: c = a + b (fp16), 6 bytes per element.
     Its GB/s is the measured HBM roofline the GEMM's traffic figures are read against;
     torch's own a + b on the same tensors is timed beside it as context."""
@@ -275,9 +310,7 @@ def run_vector_add(lib, n, steps, warmup):
     out = {"workload": "vector_add", "n": n, "bytes": 6 * n}
     for name, fn in (("mi355gemm", lambda: lib.vector_add(a, b, out=c)),
                      ("torch", lambda: torch.add(a, b, out=c))):
-        for _ in range(warmup):
-            fn()
-        torch.cuda.synchronize()
+        warm_up(fn, warmup, min_warm_ms)
         e0 = torch.cuda.Event(enable_timing=True)
         e1 = torch.cuda.Event(enable_timing=True)
         e0.record(stream)
@@ -294,7 +327,7 @@ def run_vector_add(lib, n, steps, warmup):
     return out
 
 
-def run_softmax(lib, M, N, steps, warmup):
+def run_softmax(lib, M, N, steps, warmup, min_warm_ms=MIN_WARMUP_MS):
     """The tutorial's row-wise softmax on an M x N fp16 matrix (N(0, 3^2) entries, seed 0):
     4 bytes move per element (one read, one write), so its GB/s reads against HBM peak;
     torch.softmax on the same tensor is timed beside it as context."""
@@ -307,9 +340,7 @@ def run_softmax(lib, M, N, steps, warmup):
     out = {"workload": "softmax", "M": M, "N": N, "bytes": 4 * M * N}
     for name, fn in (("mi355gemm", lambda: lib.softmax(x, out=y)),
                      ("torch", lambda: torch.softmax(x, dim=1, out=y))):
-        for _ in range(warmup):
-            fn()
-        torch.cuda.synchronize()
+        warm_up(fn, warmup, min_warm_ms)
         e0 = torch.cuda.Event(enable_timing=True)
         e1 = torch.cuda.Event(enable_timing=True)
         e0.record(stream)
@@ -337,7 +368,7 @@ def attention_flops(B, H, Sq, Sk, D, causal):
     return 4.0 * B * H * D * pairs
 
 
-def run_attention(lib, B, H, S, D, causal, steps, warmup):
+def run_attention(lib, B, H, S, D, causal, steps, warmup, min_warm_ms=MIN_WARMUP_MS):
     """The tutorial's FlashAttention forward on (B, H, S, D) fp16 tensors, N(0,1) seed 0,
     scale 1/sqrt(D); torch's scaled_dot_product_attention on the same tensors is timed
     beside it as context."""
@@ -354,9 +385,7 @@ def run_attention(lib, B, H, S, D, causal, steps, warmup):
            "causal": causal, "flops": flops}
     for name, fn in (("mi355gemm", lambda: lib.attention(q, k, v, causal=causal, out=o)),
                      ("torch_sdpa", lambda: F.scaled_dot_product_attention(q, k, v, is_causal=causal))):
-        for _ in range(warmup):
-            fn()
-        torch.cuda.synchronize()
+        warm_up(fn, warmup, min_warm_ms)
         e0 = torch.cuda.Event(enable_timing=True)
         e1 = torch.cuda.Event(enable_timing=True)
         e0.record(stream)
@@ -435,7 +464,7 @@ def main():
     epi = args.epilogue or w.epilogues[0]
     print("bench: %s epilogue=%s steps=%d warmup=%d" % (w.name, epi, args.steps, args.warmup),
           file=sys.stderr, flush=True)
-    head = run_workload(lib, w, epi, args.steps, args.warmup, args.config)
+    head = run_workload(lib, w, epi, args.steps, args.warmup, args.config, args.min_warmup_ms)
     print("bench: headline %.2f us/step (events %.2f us), kernel %.2f us, %.1f TFLOP/s"
           % (head["us"], head["event_us"], head["kernel_us"], head["tflops"]),
           file=sys.stderr, flush=True)
@@ -449,7 +478,7 @@ def main():
                 if ew.name == w.name and e == epi:
                     continue
                 steps = 20 if ew.M >= 8192 else (1000 if ew.M <= 256 else 200)
-                r = run_workload(lib, ew, e, steps, 10)
+                r = run_workload(lib, ew, e, steps, 10, min_warm_ms=args.min_warmup_ms)
                 print("bench: %s %s %.2f us/step, kernel %.2f us, %.1f TFLOP/s"
                       % (ew.name, e, r["us"], r["kernel_us"], r["tflops"]),
                       file=sys.stderr, flush=True)
@@ -458,14 +487,14 @@ def main():
     others = not args.no_extra and not args.gemm_only
     vadd = None
     if others:
-        vadd = run_vector_add(lib, 1 << 28, 50, 5)
+        vadd = run_vector_add(lib, 1 << 28, 50, 5, args.min_warmup_ms)
         print("bench: vector_add n=2^28 %.2f us %.1f GB/s (torch %.1f GB/s)"
               % (vadd["us"], vadd["GBps"], vadd["torch_GBps"]), file=sys.stderr, flush=True)
 
     softmax = []
     if others:
         for (M, N) in ((8192, 8192), (4096, 4096), (64, 65536)):
-            r = run_softmax(lib, M, N, 100, 5)
+            r = run_softmax(lib, M, N, 100, 5, args.min_warmup_ms)
             print("bench: softmax %dx%d %.2f us %.1f GB/s (torch %.1f GB/s)"
                   % (M, N, r["us"], r["GBps"], r["torch_GBps"]), file=sys.stderr, flush=True)
             softmax.append(r)
@@ -473,7 +502,7 @@ def main():
     attention = []
     if others:
         for (D, causal) in ((128, False), (128, True), (64, False), (64, True)):
-            r = run_attention(lib, 4, 32, 4096, D, causal, 20, 3)
+            r = run_attention(lib, 4, 32, 4096, D, causal, 20, 3, args.min_warmup_ms)
             print("bench: attention 4x32x4096 d%d %s %.1f us %.1f TFLOP/s (torch sdpa %.1f TFLOP/s)"
                   % (D, "causal" if causal else "full", r["us"], r["tflops"], r["torch_sdpa_tflops"]),
                   file=sys.stderr, flush=True)
@@ -481,7 +510,7 @@ def main():
 
     cold = None
     if others and not args.no_gemm_extras:
-        cold = run_cold(lib, w, 200)
+        cold = run_cold(lib, w, 200, args.min_warmup_ms)
         print("bench: %s %.2f us/launch over %d input copies (%.0f MiB)"
               % (cold["workload"], cold["kernel_us"], cold["copies"], cold["bytes_rotated"] / 2**20),
               file=sys.stderr, flush=True)
@@ -501,6 +530,8 @@ def main():
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
+        "min_warmup_ms": args.min_warmup_ms,
+        "warmup_calls": head["warmup_calls"],
         "ms_per_step": head["ms"],
         "higher_is_better": True,
         "scaling": "weak",

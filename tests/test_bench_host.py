@@ -3,6 +3,7 @@ from __future__ import annotations
 
 import os
 import sys
+import time
 
 import numpy as np
 import pytest
@@ -30,3 +31,21 @@ def test_gpus_above_one_exit_with_a_message(capsys, monkeypatch):
         bench.main()
     assert e.value.code != 0
     assert "one GPU" in capsys.readouterr().err
+
+
+def test_warm_up_runs_the_calls_then_tops_up_to_the_minimum_time(monkeypatch):
+    """warm_up makes the requested calls, then more until the minimum time has passed;
+    with no minimum it makes exactly the requested calls."""
+    import torch
+    monkeypatch.setattr(torch.cuda, "synchronize", lambda *a, **k: None)
+    calls = []
+
+    def fn():
+        calls.append(1)
+        time.sleep(0.001)
+    t0 = time.perf_counter()
+    n = bench.warm_up(fn, 3, 30.0)
+    assert n == len(calls) and n > 3
+    assert (time.perf_counter() - t0) * 1e3 >= 30.0
+    calls.clear()
+    assert bench.warm_up(fn, 5, 0.0) == 5 == len(calls)
