@@ -260,12 +260,13 @@ int tuned_choice(const Request &r, bool av, bool bv)
 // Shape-keyed choice (host only), from interleaved timings of the candidates on several
 // MI355X boxes.  A launch should cover the 256 compute units; among the tiles that do,
 // the largest wins (fewer bytes per flop from L2 into LDS).  With every CU busy the part
-// runs at its power limit, where the lighter configurations are the steadier ones:
-// 256x256x64 tiles (8 waves, 2 stages) from one full wave of them, 128x128 tiles with 4
-// waves when they fill the chip; with part of the chip idle (fewer than 256 128x128
-// tiles) the two k-groups' extra latency hiding wins.  The 256x256x64 tile took over one
-// wave of big tiles from the 256x256x32 one once the K-tail patch moved into its own
-// kernel variant (the 64-deep tile had spilled registers before).  The register-staged kernels take
+// runs at its power limit: 256x256x64 tiles (8 waves, 2 stages) from one full wave of
+// them, else 256x128 tiles with two k-groups when they fill the chip, else 128x128 tiles
+// with two k-groups (two waves per SIMD hide each other's LDS reads and barrier waits).
+// The 256x256x64 tile took over one wave of big tiles from the 256x256x32 one once the
+// K-tail patch moved into its own kernel variant (the 64-deep tile had spilled registers
+// before).  At 2048^3 the k-groups beat the 4-wave 128x128 tile by 3-7% once the clock
+// has settled under load; timings taken right after a pause had favoured either one.  The register-staged kernels take
 // small problems and those whose B or C rows are not 16-byte friendly (the direct kernels
 // need N % 8 == 0 and 16-byte aligned B and C; A may have any alignment).
 int choose(const Request &r)
@@ -281,9 +282,7 @@ int choose(const Request &r)
         const int64_t t256 = tiles(r, 256, 256), t256x128 = tiles(r, 256, 128), t128 = tiles(r, 128, 128);
         if (t256 >= kCUs) return find_direct(256, 256, 64, 8, 1);        // a wave of big tiles or more
         if (t256x128 >= kCUs) return find_direct(256, 128, 64, 8, 2);    // e.g. one GPU's share of 8192^3
-        if (t128 >= kCUs) return r.K >= 4096 ? find_direct(128, 128, 64, 8, 2)   // long K: k-groups
-                                             : find_direct(128, 128, 64, 4, 1);
-        if (t128 >= kCUs / 4) return find_direct(128, 128, 64, 8, 2);    // part of the chip idle
+        if (t128 >= kCUs / 4) return find_direct(128, 128, 64, 8, 2);    // 128x128 k-groups
     }
     // at most 8 columns: no tile contraction left; the narrow kernel reads A once
     if (r.N <= 8) return narrow_for(r.M);
