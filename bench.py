@@ -166,6 +166,32 @@ def time_gemm(lib, A, B, bias, epi, out, steps, warmup, config=None, min_warm_ms
     return wall_ms, event_ms, kernel_ms, per[len(per) // 2], per[0], call_ms, warm
 
 
+def time_graph(lib, A, B, bias, epi, out, calls=100, replays=20, min_warm_ms=MIN_WARMUP_MS):
+    """`calls` back-to-back calls captured in one HIP graph, replayed `replays` times
+    after a warm-up: ms per call without the per-call host work of the binding."""
+    import torch
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        lib.gemm(A, B, bias, epi, out=out)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        for _ in range(calls):
+            lib.gemm(A, B, bias, epi, out=out)
+    warm_up(graph.replay, 1, min_warm_ms)
+    stream = torch.cuda.current_stream()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(replays):
+        graph.replay()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / (replays * calls)
+
+
 def _sha16(t) -> str:
     """First 16 hex digits of the sha256 of a CPU fp16 tensor's bytes."""
     import hashlib
@@ -278,6 +304,8 @@ def run_workload(lib, w, epi, steps, warmup, config=None, min_warm_ms=MIN_WARMUP
     wall_ms, event_ms, kernel_ms, kernel_med, kernel_min, call_ms, warm = time_gemm(
         lib, A, B, bias, epi, out, steps, warmup, config, min_warm_ms)
     tflops = w.flops / (wall_ms * 1e-3) / 1e12
+    # launch-bound sizes: the same calls replayed from a captured graph
+    graph_ms = time_graph(lib, A, B, bias, epi, out, min_warm_ms=min_warm_ms) if w.M <= 256 else None
     return {
         "workload": w.name, "M": w.M, "N": w.N, "K": w.K, "epilogue": epi,
         "kernel_config": lib.mi355gemm_config_name(cid),
@@ -289,6 +317,7 @@ def run_workload(lib, w, epi, steps, warmup, config=None, min_warm_ms=MIN_WARMUP
         "kernel_min_us": kernel_min * 1e3,
         "call_event_pair_us": call_ms * 1e3,
         "warmup_calls": warm,
+        "graph_us_per_call": graph_ms * 1e3 if graph_ms is not None else None,
         "inputs_sha256_16": inputs_sha256(w, epi),
         "kernel_tflops": w.flops / (kernel_ms * 1e-3) / 1e12,
         "algorithmic_GBps": w.algorithmic_bytes(epi) / (kernel_ms * 1e-3) / 1e9,
@@ -479,8 +508,10 @@ def main():
                     continue
                 steps = 20 if ew.M >= 8192 else (1000 if ew.M <= 256 else 200)
                 r = run_workload(lib, ew, e, steps, 10, min_warm_ms=args.min_warmup_ms)
-                print("bench: %s %s %.2f us/step, kernel %.2f us, %.1f TFLOP/s"
-                      % (ew.name, e, r["us"], r["kernel_us"], r["tflops"]),
+                print("bench: %s %s %.2f us/step, kernel %.2f us, %.1f TFLOP/s%s"
+                      % (ew.name, e, r["us"], r["kernel_us"], r["tflops"],
+                         "" if r["graph_us_per_call"] is None
+                         else ", %.2f us/call from a graph" % r["graph_us_per_call"]),
                       file=sys.stderr, flush=True)
                 extra.append(r)
 
