@@ -234,17 +234,22 @@ def gemm(a: torch.Tensor, b: torch.Tensor, bias: torch.Tensor | None = None,
     idx = dev.index if dev.index is not None else torch.cuda.current_device()
     sptr = stream.cuda_stream if stream is not None else _raw_stream(idx)
     args = (M, N, K, a.data_ptr(), b.data_ptr(), out.data_ptr(), bptr, epi, sptr)
-    cid = -1 if config is None else (config_id(config) if isinstance(config, str) else int(config))
+    # config None: the selector's choice; any given id goes to the library, which rejects
+    # ids out of range (the timed entry reads -1 as the selector's choice, so a negative
+    # id given here is rejected before it)
+    cid = None if config is None else (config_id(config) if isinstance(config, str) else int(config))
     if events is not None:
         ev = tuple(e.cuda_event if e is not None else None for e in events)
         if len(ev) != 2 or any(h == 0 for h in ev):
             raise ValueError("events must be a (start, stop) pair of torch.cuda.Event (or None), "
                              "each recorded once before")
+        if cid is not None and cid < 0:
+            raise GemmError(EINVAL, "unknown config id %d" % cid)
 
     def call():
         if events is not None:
-            return lib.mi355gemm_gemm_timed(*args, cid, ev[0], ev[1])
-        return lib.mi355gemm_gemm(*args) if cid < 0 else lib.mi355gemm_gemm_config(*args, cid)
+            return lib.mi355gemm_gemm_timed(*args, -1 if cid is None else cid, ev[0], ev[1])
+        return lib.mi355gemm_gemm(*args) if cid is None else lib.mi355gemm_gemm_config(*args, cid)
     # the library launches on the calling thread's current HIP device
     if idx == torch.cuda.current_device():
         st = call()

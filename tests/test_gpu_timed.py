@@ -68,3 +68,11 @@ def test_unrecorded_events_are_rejected_before_any_launch():
     fresh = (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
     with pytest.raises(ValueError):
         g.gemm(A, A, events=fresh)
+
+
+def test_negative_config_ids_are_rejected_with_and_without_events():
+    A = torch.zeros((64, 64), dtype=torch.float16, device="cuda:0")
+    k0, k1 = _recorded_pair()
+    for events in (None, (k0, k1)):
+        with pytest.raises(g.GemmError):
+            g.gemm(A, A, config=-1, events=events)
