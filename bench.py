@@ -102,7 +102,7 @@ def warm_up(fn, calls, min_ms):
     import torch
     t0 = time.perf_counter()
     n = 0
-    for _ in range(max(calls, 1)):
+    for _ in range(calls):
         fn()
         n += 1
     torch.cuda.synchronize()
@@ -110,7 +110,7 @@ def warm_up(fn, calls, min_ms):
         el = (time.perf_counter() - t0) * 1e3
         if el >= min_ms:
             return n
-        batch = max(1, min(100000, int((min_ms - el) / (el / n)) + 1))
+        batch = 1 if n == 0 else max(1, min(100000, int((min_ms - el) / (el / n)) + 1))
         for _ in range(batch):
             fn()
         n += batch

@@ -49,3 +49,6 @@ def test_warm_up_runs_the_calls_then_tops_up_to_the_minimum_time(monkeypatch):
     assert (time.perf_counter() - t0) * 1e3 >= 30.0
     calls.clear()
     assert bench.warm_up(fn, 5, 0.0) == 5 == len(calls)
+    calls.clear()
+    assert bench.warm_up(fn, 0, 0.0) == 0 == len(calls)
+    assert bench.warm_up(fn, 0, 5.0) >= 1
