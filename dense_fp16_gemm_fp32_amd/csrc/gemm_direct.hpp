@@ -139,6 +139,17 @@ __device__ __forceinline__ void lds_dma16(__amdgpu_buffer_rsrc_t rsrc, const voi
                  : "s"(lds_addr), "v"(voffset), "s"(rsrc));
 }
 
+// The same copy with a wave-uniform byte offset `soffset` added in the instruction's
+// scalar offset field, so a per-lane offset that does not change can be reused as is.
+__device__ __forceinline__ void lds_dma16(__amdgpu_buffer_rsrc_t rsrc, const void *lds,
+                                          uint32_t voffset, uint32_t soffset)
+{
+    const uint32_t lds_addr = (uint32_t)(uintptr_t)lds_ptr(lds);
+    asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
+                 :
+                 : "s"(lds_addr), "v"(voffset), "s"(rsrc), "s"(soffset));
+}
+
 // Per-lane state of one wavefront: DMA source offsets, fragment read addresses, the
 // accumulators and the double-buffered operand fragments.
 template <class T>
@@ -295,13 +306,21 @@ struct DirectWave {
     // Piece g (0 <= g < G) of the HBM -> LDS copy of stage kt (A rows [m0, m0+BM) x k
     // [k0, k0+BK), B k-rows x columns [n0, n0+BN)) into dst.  A stage past the end of K
     // copies zeros (every offset falls out of range), which keeps the issue pattern, and
-    // so the counter arithmetic below, the same in every iteration.
+    // so the counter arithmetic below, the same in every iteration.  FULL: the stage lies
+    // wholly below K, so no A chunk needs the K mask and the stage's K offset rides in
+    // the scalar offset field (no vector instruction per piece); rows past M still fall
+    // outside the descriptor's range.
+    template <bool FULL = false>
     __device__ __forceinline__ void issue_piece(St &dst, int kt, int g) const
     {
         const int k0 = kt * T::BK;
         if (g < T::GA) {
-            const uint32_t off = masked_offset(a_off[g] + (uint32_t)k0 * 2u, k0 + a_kc[g] < K);
-            lds_dma16(a_rs, dst.a + (g * T::NW + wave) * 512, off);
+            if constexpr (FULL) {
+                lds_dma16(a_rs, dst.a + (g * T::NW + wave) * 512, a_off[g], (uint32_t)k0 * 2u);
+            } else {
+                const uint32_t off = masked_offset(a_off[g] + (uint32_t)k0 * 2u, k0 + a_kc[g] < K);
+                lds_dma16(a_rs, dst.a + (g * T::NW + wave) * 512, off);
+            }
         } else {
             const int gb = g - T::GA;
             const int rows_k = min(T::BK, K - k0);
@@ -311,10 +330,11 @@ struct DirectWave {
         }
     }
 
+    template <bool FULL = false>
     __device__ __forceinline__ void issue_stage(St &dst, int kt) const
     {
 #pragma unroll
-        for (int g = 0; g < T::G; ++g) issue_piece(dst, kt, g);
+        for (int g = 0; g < T::G; ++g) issue_piece<FULL>(dst, kt, g);
     }
 
     // Read r (0 <= r < NREAD) of the fragments for this wave's k-step q of stage src, into
@@ -470,8 +490,9 @@ __global__ void __launch_bounds__(T::NT) gemm_direct(GemmArgs p)
     // stage kt+1's copy and crosses the barrier, then reads the next stage's fragments
     // while its MFMAs run.  The body has no branches on data; near the end of K it copies
     // zeros for the stages past the end and reads fragments it never uses.
-    auto stage = [&](auto Jc, int kt) {
+    auto stage = [&](auto Jc, int kt, auto full_c) {
         constexpr int J = decltype(Jc)::value;
+        constexpr bool FULL = decltype(full_c)::value;   // the stage copied here is below K
         St &cur = ring[J];
         St &nxt = ring[(J + 1) % T::STAGES];
         St &dst = ring[(J + T::STAGES - 1) % T::STAGES];
@@ -480,7 +501,7 @@ __global__ void __launch_bounds__(T::NT) gemm_direct(GemmArgs p)
             constexpr int buf = (J * T::Q + q) & 1;
             constexpr bool last = (q == T::Q - 1);
             if constexpr (T::Q == 1) {
-                w.issue_stage(dst, kt + T::STAGES - 1);
+                w.template issue_stage<FULL>(dst, kt + T::STAGES - 1);
             }
             if constexpr (last) {
                 // stage kt+1 has landed once at most the STAGES-2 later copies are in
@@ -505,7 +526,7 @@ __global__ void __launch_bounds__(T::NT) gemm_direct(GemmArgs p)
                     constexpr int g0 = m * T::G / T::NMFMA;
                     constexpr int g1 = (m + 1) * T::G / T::NMFMA;
 #pragma unroll
-                    for (int g = g0; g < g1; ++g) w.issue_piece(dst, kt + T::STAGES - 1, g);
+                    for (int g = g0; g < g1; ++g) w.template issue_piece<FULL>(dst, kt + T::STAGES - 1, g);
                 }
                 __builtin_amdgcn_sched_barrier(0);
             });
@@ -525,10 +546,15 @@ __global__ void __launch_bounds__(T::NT) gemm_direct(GemmArgs p)
         // The last ring turn stops at the end of K (a branch on a workgroup-uniform
         // value); the copies and fragment reads the last stage issued for the stages
         // after it read zeros and are never used.
-        for (int kt = 0; kt < nk; kt += T::STAGES) {
+        // Whole ring turns whose copies (up to stage kt + 2*STAGES - 2) all lie below K
+        // take the copy without the K mask; the turns after them the general one.
+        int kt = 0;
+        for (; (kt + 2 * T::STAGES - 1) * T::BK <= p.K; kt += T::STAGES)
+            static_for<T::STAGES>([&](auto jc) { stage(jc, kt + decltype(jc)::value, std::true_type{}); });
+        for (; kt < nk; kt += T::STAGES) {
             static_for<T::STAGES>([&](auto jc) {
                 const int k = kt + decltype(jc)::value;
-                if (k < nk) stage(jc, k);
+                if (k < nk) stage(jc, k, std::false_type{});
             });
         }
         // the copies past the end of K are still landing; none may outlive the kernel
