@@ -27,6 +27,7 @@ using D256k64 = DTile<256, 256, 64, 2, 4, 1, 2>;    // 8 waves of 128x64, 128 Ki
 using D256x128 = DTile<256, 128, 64, 2, 2, 2, 3>;   // 2 x 4 waves of 128x64, 144 KiB
 using D128 = DTile<128, 128, 64, 2, 2, 2, 4>;       // 2 x 4 waves of 64x64, 128 KiB
 using D128w4 = DTile<128, 128, 64, 2, 2, 1, 4>;     // 4 waves of 64x64, 128 KiB
+using D256w4 = DTile<256, 256, 32, 2, 2, 1, 4>;     // 4 waves of 128x128, 128 KiB
 // attention: head dim, keys per block, waves (32 query rows each), LDS stages
 using A128 = ATile<128, 128, 8, 2>;  // 256 query rows, 128-key blocks, 128 KiB LDS
 using A64 = ATile<64, 64, 8, 3>;     // 256 query rows, 64-key blocks, 48 KiB LDS
@@ -49,6 +50,7 @@ MI355_DIRECT(D256k64)
 MI355_DIRECT(D256x128)
 MI355_DIRECT(D128)
 MI355_DIRECT(D128w4)
+MI355_DIRECT(D256w4)
 #undef MI355_DIRECT
 #define MI355_NARROW(KS)                                   \
     template __global__ void gemm_narrow<0, KS>(GemmArgs); \
@@ -125,6 +127,7 @@ const Config kConfigs[] = {
     direct_config<D256x128>("d256x128x64_w2x2k2_s3", 8),
     direct_config<D128>("d128x128x64_w2x2k2_s4", 8),
     direct_config<D128w4>("d128x128x64_w2x2_s4", 8),
+    direct_config<D256w4>("d256x256x32_w2x2_s4", 4),
     staged_config<T256, true, true>("s256x256x64_w2x2_av_bv", 8),
     staged_config<T128, true, true>("s128x128x64_w2x2_av_bv", 8),
     staged_config<T128, true, false>("s128x128x64_w2x2_av_bn", 8),
@@ -260,9 +263,12 @@ int tuned_choice(const Request &r, bool av, bool bv)
 // Shape-keyed choice (host only), from interleaved timings of the candidates on several
 // MI355X boxes.  A launch should cover the 256 compute units; among the tiles that do,
 // the largest wins (fewer bytes per flop from L2 into LDS).  With every CU busy the part
-// runs at its power limit: 256x256x64 tiles (8 waves, 2 stages) from one full wave of
-// them, else 256x128 tiles with two k-groups when they fill the chip, else 128x128 tiles
-// with two k-groups (two waves per SIMD hide each other's LDS reads and barrier waits).
+// runs at its power limit: 256x256x32 tiles on 4 waves of 128x128 from four full waves
+// of them, 256x256x64 tiles (8 waves, 2 stages) from one, else 256x128 tiles with two
+// k-groups when they fill the chip, else 128x128 tiles with two k-groups (two waves per
+// SIMD hide each other's LDS reads and barrier waits).  The 4-wave 256x256 tile reads a
+// third less LDS per flop; it overtook the 8-wave one at 8192^3 once the copies lost
+// their vector instructions.
 // The 256x256x64 tile took over one wave of big tiles from the 256x256x32 one once the
 // K-tail patch moved into its own kernel variant (the 64-deep tile had spilled registers
 // before).  At 2048^3 the k-groups beat the 4-wave 128x128 tile by 3-7% once the clock
@@ -280,7 +286,8 @@ int choose(const Request &r)
     if (bv || r.N >= 64) {
         // measured with the interleaved tuner on MI355X (the table file records the runs)
         const int64_t t256 = tiles(r, 256, 256), t256x128 = tiles(r, 256, 128), t128 = tiles(r, 128, 128);
-        if (t256 >= kCUs) return find_direct(256, 256, 64, 8, 1);        // a wave of big tiles or more
+        if (t256 >= 4 * kCUs) return find_direct(256, 256, 32, 4, 1);   // several waves of big tiles
+        if (t256 >= kCUs) return find_direct(256, 256, 64, 8, 1);        // about one wave of them
         if (t256x128 >= kCUs) return find_direct(256, 128, 64, 8, 2);    // e.g. one GPU's share of 8192^3
         if (t128 >= kCUs / 4) return find_direct(128, 128, 64, 8, 2);    // 128x128 k-groups
     }

@@ -322,7 +322,8 @@ def test_attention_argument_checks(args, want):
 
 
 @pytest.mark.parametrize("shape,want", [
-    ((8192, 8192, 8192), "d256x256x64_w2x4_s2"),      # four waves of 256 x 256 tiles
+    ((8192, 8192, 8192), "d256x256x32_w2x2_s4"),      # four waves of 256 x 256 tiles
+    ((16384, 8192, 4096), "d256x256x32_w2x2_s4"),
     ((4096, 4096, 4096), "d256x256x64_w2x4_s2"),      # one wave of them
     ((16384, 2048, 1024), "d256x256x64_w2x4_s2"),
     ((2048, 8192, 4096), "d256x256x64_w2x4_s2"),
@@ -343,7 +344,7 @@ def test_selector_rules_pick_the_measured_winners(shape, want):
 
 @pytest.mark.parametrize("shape,ptr_off,want", [
     ((2048, 2047, 2048), 0, "d128x128x64_w2x2k2_s4"), # odd N: direct on the first 2040 columns
-    ((8192, 8191, 8192), 0, "d256x256x64_w2x4_s2"),
+    ((8192, 8191, 8192), 0, "d256x256x32_w2x2_s4"),
     ((1000, 3001, 777), 0, "d128x128x64_w2x2k2_s4"),
     ((2048, 2048, 2048), 2, "d128x128x64_w2x2k2_s4"), # B and C only 2-byte aligned
     ((8192, 63, 8192), 0, "s64x64x64_w2x1_av_bn"),    # N < 64: no direct launch to split
