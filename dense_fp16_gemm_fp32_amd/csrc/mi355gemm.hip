@@ -265,14 +265,16 @@ int tuned_choice(const Request &r, bool av, bool bv)
 // the largest wins (fewer bytes per flop from L2 into LDS).  With every CU busy the part
 // runs at its power limit: 256x256x32 tiles on 4 waves of 128x128 from four full waves
 // of them, 256x256x64 tiles (8 waves, 2 stages) from one, else 256x128 tiles with two
-// k-groups when they fill the chip, else 128x128 tiles with two k-groups (two waves per
-// SIMD hide each other's LDS reads and barrier waits).  The 4-wave 256x256 tile reads a
-// third less LDS per flop; it overtook the 8-wave one at 8192^3 once the copies lost
-// their vector instructions.
+// k-groups when they fill the chip, else 128x128 tiles: 4 waves when they fill the chip
+// with K below 4096, two k-groups for long K or with part of the chip idle (two waves per
+// SIMD hide each other's LDS reads and barrier waits).  The 4-wave tiles took over
+// (256x256 at 8192^3) or kept (128x128 at 2048^3) their shapes once the copies lost their
+// vector instructions: with one wave per SIMD nothing else hid them.
 // The 256x256x64 tile took over one wave of big tiles from the 256x256x32 one once the
 // K-tail patch moved into its own kernel variant (the 64-deep tile had spilled registers
-// before).  At 2048^3 the k-groups beat the 4-wave 128x128 tile by 3-7% once the clock
-// has settled under load; timings taken right after a pause had favoured either one.  The register-staged kernels take
+// before).  At 2048^3 the two 128x128 tiles trade places from box to box; the 4-wave one
+// is faster on average and its spread is far smaller (20.6-21.7 us against 19.7-23.8
+// over four boxes).  The register-staged kernels take
 // small problems and those whose B or C rows are not 16-byte friendly (the direct kernels
 // need N % 8 == 0 and 16-byte aligned B and C; A may have any alignment).
 int choose(const Request &r)
@@ -289,7 +291,9 @@ int choose(const Request &r)
         if (t256 >= 4 * kCUs) return find_direct(256, 256, 32, 4, 1);   // several waves of big tiles
         if (t256 >= kCUs) return find_direct(256, 256, 64, 8, 1);        // about one wave of them
         if (t256x128 >= kCUs) return find_direct(256, 128, 64, 8, 2);    // e.g. one GPU's share of 8192^3
-        if (t128 >= kCUs / 4) return find_direct(128, 128, 64, 8, 2);    // 128x128 k-groups
+        if (t128 >= kCUs) return r.K >= 4096 ? find_direct(128, 128, 64, 8, 2)   // long K: k-groups
+                                             : find_direct(128, 128, 64, 4, 1);
+        if (t128 >= kCUs / 4) return find_direct(128, 128, 64, 8, 2);    // part of the chip idle
     }
     // at most 8 columns: no tile contraction left; the narrow kernel reads A once
     if (r.N <= 8) return narrow_for(r.M);
