@@ -323,9 +323,10 @@ struct DirectWave {
             }
         } else {
             const int gb = g - T::GA;
-            const int rows_k = min(T::BK, K - k0);
+            // B rows [k0, k0 + rows_k) of this tile's columns; FULL: all BK rows
+            const int rows_k = FULL ? T::BK : min(T::BK, K - k0);
             const __amdgpu_buffer_rsrc_t b_rs =
-                make_rsrc(B + (int64_t)min(k0, K) * ldb + n0, span_bytes(rows_k, ldb, N - n0));
+                make_rsrc(B + (int64_t)(FULL ? k0 : min(k0, K)) * ldb + n0, span_bytes(rows_k, ldb, N - n0));
             lds_dma16(b_rs, dst.b + (gb * T::NW + wave) * 512, b_off[gb]);
         }
     }
