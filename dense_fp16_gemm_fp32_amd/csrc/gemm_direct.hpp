@@ -7,8 +7,8 @@
 // 256x256x64 eight-wave tile spill.
 //
 // One workgroup computes one BM x BN macro-tile of C with WAVES_M x WAVES_N x KGROUPS
-// wavefronts (two per SIMD in the shipped configurations, so one wave's LDS reads and
-// barrier waits are covered by the other's MFMAs):
+// wavefronts: one per SIMD (4 waves, the larger wave tiles) or two per SIMD (8 waves, so
+// one wave's LDS reads and barrier waits are covered by the other's MFMAs):
 //   1. tile order  -- tile_coords(): XCD-contiguous ranges, GROUP_M tile-rows per sweep;
 //   2. loader      -- buffer_load_dwordx4 ... lds: HBM -> LDS with no VGPR staging, into a
 //                     ring of STAGES buffers; the copy for stage kt+STAGES-1 is in flight

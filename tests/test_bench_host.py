@@ -52,3 +52,11 @@ def test_warm_up_runs_the_calls_then_tops_up_to_the_minimum_time(monkeypatch):
     calls.clear()
     assert bench.warm_up(fn, 0, 0.0) == 0 == len(calls)
     assert bench.warm_up(fn, 0, 5.0) >= 1
+
+
+def test_kernel_hash_ignores_comments_but_not_code():
+    """The traffic figure is keyed to the kernels' code: a comment or blank line changes
+    nothing, a changed statement changes the text that is hashed."""
+    src = "int a = 1;  // one\n\n// a note\nint b = a + 2;\n"
+    assert bench.code_text(src) == bench.code_text("int a = 1;\nint b = a + 2;  // two\n")
+    assert bench.code_text(src) != bench.code_text("int a = 1;\nint b = a + 3;\n")
