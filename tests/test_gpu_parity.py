@@ -258,6 +258,27 @@ def test_rejects_bad_tensors():
         g.gemm(A, B, None, "bias_gelu")
 
 
+# ---- the direct kernel's two K loops --------------------------------------------------
+
+def test_direct_kernel_full_turn_boundary_bitexact():
+    """The direct kernel runs whole ring turns whose copies all lie below K with the
+    copy's K offset in the scalar offset field, then the rest with masked copies.  The
+    switch sits at K = (2 * stages - 1) * block_k; K just below, at and above it, a turn
+    later, and with a K tail (K % 8 != 0) must give the oracle's bits.  Integer inputs:
+    every partial sum is an integer below 2^24, exact in fp32 in any order, so the one
+    rounding to fp16 is the oracle's."""
+    for cfg in all_configs():
+        if not cfg["direct"]:
+            continue
+        kb = (2 * cfg["stages"] - 1) * cfg["block_k"]
+        M, N = cfg["block_m"] + 3, cfg["block_n"] + 8
+        for K in (kb - 8, kb, kb + 3, kb + 8, kb + cfg["stages"] * cfg["block_k"]):
+            print("turn boundary", cfg["name"], (M, N, K), flush=True)
+            A, B = _small_int_inputs(M, N, K)
+            C = _run(A, B, None, "none", config=cfg["id"])
+            assert_bitexact(C, oracle.gemm(A, B), "%s K=%d" % (cfg["name"], K))
+
+
 # ---- the fused GELU over every finite fp16 input -------------------------------------
 
 def _ordered(bits: np.ndarray) -> np.ndarray:
