@@ -60,6 +60,12 @@ struct DTile {
     static constexpr int GA = A_BYTES / (1024 * NW);   // 1 KiB LDS-DMA loads per wave
     static constexpr int GB = B_BYTES / (1024 * NW);
     static constexpr int G = GA + GB;
+    // Copies of a stage issued in its first k-step, before the end-of-stage wait: all of
+    // them with a ring of 2 stages (the next stage's copy must land before that wait) or
+    // one k-step per stage; else half, and the rest after the barrier.  VM_WAIT: the
+    // copies younger than the next stage's when the wait is reached.
+    static constexpr int G_EARLY = (STAGES >= 3 && KK / KGROUPS >= 2) ? G / 2 : G;
+    static constexpr int VM_WAIT = G * (STAGES - 3) + G_EARLY;
     static constexpr int LDS_BYTES = STAGES * STAGE_BYTES;
     // k-group exchange at the end: every wave hands half of its 32x32 fp32 blocks (4 KiB
     // each) to its partner in the other group
@@ -73,6 +79,7 @@ struct DTile {
     static_assert(KK % KGROUPS == 0, "k-steps must split evenly over the k-groups");
     static_assert((STAGES * Q) % 2 == 0, "fragment double-buffer parity must repeat per ring turn");
     static_assert(STAGES >= 2 && STAGES <= 5 && G * (STAGES - 2) <= 63, "ring size / vmcnt range");
+    static_assert(VM_WAIT >= 0 && VM_WAIT <= 63, "vmcnt range");
     static_assert(LDS_BYTES <= 160 * 1024, "over the gfx950 LDS budget");
     static_assert(RED_BYTES <= LDS_BYTES, "k-group exchange must fit in the ring");
     static_assert(BM * BN * 2 <= LDS_BYTES, "the C tile is staged in the ring");
@@ -505,9 +512,10 @@ __global__ void __launch_bounds__(T::NT) gemm_direct(GemmArgs p)
                 w.template issue_stage<FULL>(dst, kt + T::STAGES - 1);
             }
             if constexpr (last) {
-                // stage kt+1 has landed once at most the STAGES-2 later copies are in
-                // flight; this wave's reads of stage kt were issued before the barrier
-                wait_counts<T::G * (T::STAGES - 2), 15>();
+                // stage kt+1 has landed once at most the copies issued after it are in
+                // flight (stages kt+2 .. kt+STAGES-2 and the early part of kt+STAGES-1);
+                // this wave's reads of stage kt were issued before the barrier
+                wait_counts<T::VM_WAIT, 15>();
                 if (k_tail && kt + 1 == nk - 1) w.patch_tail(nxt);
                 workgroup_barrier();
             }
@@ -524,8 +532,16 @@ __global__ void __launch_bounds__(T::NT) gemm_direct(GemmArgs p)
                         w.read_one(cur, q + 1, buf ^ 1, r);
                 }
                 if constexpr (q == 0 && T::Q > 1) {
-                    constexpr int g0 = m * T::G / T::NMFMA;
-                    constexpr int g1 = (m + 1) * T::G / T::NMFMA;
+                    constexpr int g0 = m * T::G_EARLY / T::NMFMA;
+                    constexpr int g1 = (m + 1) * T::G_EARLY / T::NMFMA;
+#pragma unroll
+                    for (int g = g0; g < g1; ++g) w.template issue_piece<FULL>(dst, kt + T::STAGES - 1, g);
+                }
+                if constexpr (last && T::Q > 1 && T::G_EARLY < T::G) {
+                    // the rest after the barrier: slot dst held stage kt-1, which no wave
+                    // has read since the previous barrier
+                    constexpr int g0 = T::G_EARLY + m * (T::G - T::G_EARLY) / T::NMFMA;
+                    constexpr int g1 = T::G_EARLY + (m + 1) * (T::G - T::G_EARLY) / T::NMFMA;
 #pragma unroll
                     for (int g = g0; g < g1; ++g) w.template issue_piece<FULL>(dst, kt + T::STAGES - 1, g);
                 }
