@@ -41,7 +41,7 @@ HEADLINE = "gemm_2048"
 # --calibrate-copy run).  Reported only while the kernel sources hash to the version the
 # counters were taken on (profiles/ holds the summary); otherwise null.
 TRAFFIC = {"kernel_config": "d128x128x64_w2x2_s4", "sources_sha256_16": "e11f0a1a2ce65db5",
-           "bytes": 58910050}
+           "bytes": 58912777}
 
 
 # The files whose text defines the GEMM kernels (the configuration name fixes the template

@@ -28,6 +28,7 @@ using D256x128 = DTile<256, 128, 64, 2, 2, 2, 3>;   // 2 x 4 waves of 128x64, 14
 using D128 = DTile<128, 128, 64, 2, 2, 2, 4>;       // 2 x 4 waves of 64x64, 128 KiB
 using D128w4 = DTile<128, 128, 64, 2, 2, 1, 4>;     // 4 waves of 64x64, 128 KiB
 using D256w4 = DTile<256, 256, 32, 2, 2, 1, 4>;     // 4 waves of 128x128, 128 KiB
+using D128k32 = DTile<128, 128, 32, 2, 2, 1, 4>;    // 4 waves of 64x64, 64 KiB
 // attention: head dim, keys per block, waves (32 query rows each), LDS stages
 using A128 = ATile<128, 128, 8, 2>;  // 256 query rows, 128-key blocks, 128 KiB LDS
 using A64 = ATile<64, 64, 8, 3>;     // 256 query rows, 64-key blocks, 48 KiB LDS
@@ -51,6 +52,7 @@ MI355_DIRECT(D256x128)
 MI355_DIRECT(D128)
 MI355_DIRECT(D128w4)
 MI355_DIRECT(D256w4)
+MI355_DIRECT(D128k32)
 #undef MI355_DIRECT
 #define MI355_NARROW(KS)                                   \
     template __global__ void gemm_narrow<0, KS>(GemmArgs); \
@@ -128,6 +130,7 @@ const Config kConfigs[] = {
     direct_config<D128>("d128x128x64_w2x2k2_s4", 8),
     direct_config<D128w4>("d128x128x64_w2x2_s4", 8),
     direct_config<D256w4>("d256x256x32_w2x2_s4", 4),
+    direct_config<D128k32>("d128x128x32_w2x2_s4", 8),
     staged_config<T256, true, true>("s256x256x64_w2x2_av_bv", 8),
     staged_config<T128, true, true>("s128x128x64_w2x2_av_bv", 8),
     staged_config<T128, true, false>("s128x128x64_w2x2_av_bn", 8),
@@ -291,6 +294,8 @@ int choose(const Request &r)
         if (t256 >= 4 * kCUs) return find_direct(256, 256, 32, 4, 1);   // several waves of big tiles
         if (t256 >= kCUs) return find_direct(256, 256, 64, 8, 1);        // about one wave of them
         if (t256x128 >= kCUs) return find_direct(256, 128, 64, 8, 2);    // e.g. one GPU's share of 8192^3
+        // short K: 32-deep stages, so the ring fills and the last stage drains sooner
+        if (t128 >= kCUs / 4 && r.K < 1024) return find_direct(128, 128, 32, 4, 1);
         if (t128 >= kCUs) return r.K >= 4096 ? find_direct(128, 128, 64, 8, 2)   // long K: k-groups
                                              : find_direct(128, 128, 64, 4, 1);
         if (t128 >= kCUs / 4) return find_direct(128, 128, 64, 8, 2);    // part of the chip idle

@@ -331,8 +331,13 @@ def test_attention_argument_checks(args, want):
     ((1024, 8192, 8192), "d256x128x64_w2x2k2_s3"),    # its M share
     ((2048, 2048, 8192), "d128x128x64_w2x2k2_s4"),    # 256 tiles, long K
     ((2048, 2048, 2048), "d128x128x64_w2x2_s4"),      # 256 tiles, K = 2048
+    ((2048, 2048, 1024), "d128x128x64_w2x2_s4"),      # 256 tiles, K = 1024
+    ((2048, 2048, 768), "d128x128x32_w2x2_s4"),       # 256 tiles, K < 1024
+    ((2048, 2048, 512), "d128x128x32_w2x2_s4"),
     ((1024, 1024, 1024), "d128x128x64_w2x2k2_s4"),    # 64 tiles
-    ((1000, 3000, 777), "d128x128x64_w2x2k2_s4"),     # 192 tiles
+    ((1000, 3000, 1024), "d128x128x64_w2x2k2_s4"),    # 192 tiles, K = 1024
+    ((1000, 3000, 777), "d128x128x32_w2x2_s4"),       # 192 tiles, K < 1024
+    ((3000, 1000, 777), "d128x128x32_w2x2_s4"),
     ((256, 256, 256), "s64x64x64_w2x1_av_bv"),        # a handful of tiles
 ])
 def test_selector_rules_pick_the_measured_winners(shape, want):
@@ -345,7 +350,7 @@ def test_selector_rules_pick_the_measured_winners(shape, want):
 @pytest.mark.parametrize("shape,ptr_off,want", [
     ((2048, 2047, 2048), 0, "d128x128x64_w2x2_s4"),   # odd N: direct on the first 2040 columns
     ((8192, 8191, 8192), 0, "d256x256x32_w2x2_s4"),
-    ((1000, 3001, 777), 0, "d128x128x64_w2x2k2_s4"),
+    ((1000, 3001, 777), 0, "d128x128x32_w2x2_s4"),
     ((2048, 2048, 2048), 2, "d128x128x64_w2x2_s4"),   # B and C only 2-byte aligned
     ((8192, 63, 8192), 0, "s64x64x64_w2x1_av_bn"),    # N < 64: no direct launch to split
     ((512, 1031, 64), 0, "s64x64x64_w2x1_av_bn"),     # too few tiles
