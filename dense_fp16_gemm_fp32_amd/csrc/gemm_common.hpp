@@ -94,17 +94,18 @@ __device__ __forceinline__ void tile_coords(int bid, int tiles_m, int tiles_n, i
 // reciprocal are the hardware v_exp_f32 / v_rcp_f32.
 __device__ __forceinline__ float gelu_erf(float x)
 {
-    constexpr float p = 0.3275911f;
-    constexpr float a1 = 0.254829592f, a2 = -0.284496736f, a3 = 1.421413741f,
-                    a4 = -1.453152027f, a5 = 1.061405429f;
-    constexpr float kRsqrt2 = 0.70710678118654752f;
+    // erfc(z) ~ t (a1 + a2 t + ... + a5 t^4) exp(-z^2), t = 1 / (1 + p z), z = |x| / sqrt(2);
+    // the coefficients below are a1..a5 halved (exact in binary), so the polynomial times
+    // exp(-z^2) is h = erfc(z) / 2 = Phi(-|x|) directly, and p is premultiplied by 1/sqrt(2).
+    constexpr float p = 0.3275911f * 0.70710678118654752f;
+    constexpr float a1 = 0.5f * 0.254829592f, a2 = 0.5f * -0.284496736f, a3 = 0.5f * 1.421413741f,
+                    a4 = 0.5f * -1.453152027f, a5 = 0.5f * 1.061405429f;
     constexpr float kHalfLog2e = 0.72134752044448170f;   // log2(e) / 2: exp(-z^2) = 2^(-x^2 log2(e) / 2)
-    const float z = fabsf(x) * kRsqrt2;
-    const float t = __builtin_amdgcn_rcpf(fmaf(p, z, 1.0f));
+    const float t = __builtin_amdgcn_rcpf(fmaf(p, fabsf(x), 1.0f));
     const float poly = t * fmaf(t, fmaf(t, fmaf(t, fmaf(t, a5, a4), a3), a2), a1);
-    const float q = poly * __builtin_amdgcn_exp2f(-(x * x) * kHalfLog2e);   // erfc(z)
-    const float phi = (x >= 0.0f) ? fmaf(-0.5f, q, 1.0f) : 0.5f * q;
-    return x * phi;
+    const float h = poly * __builtin_amdgcn_exp2f(-(x * x) * kHalfLog2e);   // Phi(-|x|)
+    // Phi(x) = 1 - Phi(-x) for x >= 0; for x < 0 it is h itself, with no cancellation
+    return x * ((x >= 0.0f) ? 1.0f - h : h);
 }
 
 template <int EPI>
