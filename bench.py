@@ -84,6 +84,9 @@ def parse():
     ap.add_argument("--workload", default=HEADLINE)
     ap.add_argument("--epilogue", default=None, help="override the workload's epilogue")
     ap.add_argument("--config", default=None, help="force a kernel configuration by name")
+    ap.add_argument("--calibrate", action="store_true",
+                    help="before timing each GEMM workload, time its tile size's configurations "
+                         "on this device and install the fastest (tune.calibrate)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extra", action="store_true")
     ap.add_argument("--gemm-only", action="store_true",
@@ -300,7 +303,8 @@ def cpu_oracle_by_workload(max_gflop=20.0):
     return out
 
 
-def run_workload(lib, w, epi, steps, warmup, config=None, min_warm_ms=MIN_WARMUP_MS):
+def run_workload(lib, w, epi, steps, warmup, config=None, min_warm_ms=MIN_WARMUP_MS,
+                 calibrate=False):
     import torch
     import workloads
     A, B, bias = workloads.make_inputs(w.M, w.N, w.K, w.dist, with_bias=(epi != "none"), seed=w.seed)
@@ -308,6 +312,10 @@ def run_workload(lib, w, epi, steps, warmup, config=None, min_warm_ms=MIN_WARMUP
     A, B = A.to(dev), B.to(dev)
     bias = bias.to(dev) if bias is not None else None
     out = torch.empty((w.M, w.N), dtype=torch.float16, device=dev)
+    calibration = None
+    if calibrate and config is None:
+        from dense_fp16_gemm_fp32_amd import tune
+        calibration = tune.calibrate(A, B, bias, epi, out=out)[1]
     cid = lib.select(A, B, bias, epi, out=out) if config is None else lib.config_id(config)
     wall_ms, event_ms, kernel_ms, kernel_med, kernel_min, call_ms, warm = time_gemm(
         lib, A, B, bias, epi, out, steps, warmup, config, min_warm_ms)
@@ -317,6 +325,7 @@ def run_workload(lib, w, epi, steps, warmup, config=None, min_warm_ms=MIN_WARMUP
     return {
         "workload": w.name, "M": w.M, "N": w.N, "K": w.K, "epilogue": epi,
         "kernel_config": lib.mi355gemm_config_name(cid),
+        "calibration_us": calibration,
         "ms": wall_ms, "us": wall_ms * 1e3, "tflops": tflops,
         "pct_of_peak": 100.0 * tflops / PEAK_FP16_TFLOPS,
         "event_us": event_ms * 1e3,
@@ -501,7 +510,8 @@ def main():
     epi = args.epilogue or w.epilogues[0]
     print("bench: %s epilogue=%s steps=%d warmup=%d" % (w.name, epi, args.steps, args.warmup),
           file=sys.stderr, flush=True)
-    head = run_workload(lib, w, epi, args.steps, args.warmup, args.config, args.min_warmup_ms)
+    head = run_workload(lib, w, epi, args.steps, args.warmup, args.config, args.min_warmup_ms,
+                        args.calibrate)
     print("bench: headline %.2f us/step (events %.2f us), kernel %.2f us, %.1f TFLOP/s"
           % (head["us"], head["event_us"], head["kernel_us"], head["tflops"]),
           file=sys.stderr, flush=True)
@@ -515,7 +525,8 @@ def main():
                 if ew.name == w.name and e == epi:
                     continue
                 steps = 20 if ew.M >= 8192 else (1000 if ew.M <= 256 else 200)
-                r = run_workload(lib, ew, e, steps, 10, min_warm_ms=args.min_warmup_ms)
+                r = run_workload(lib, ew, e, steps, 10, min_warm_ms=args.min_warmup_ms,
+                                 calibrate=args.calibrate)
                 print("bench: %s %s %.2f us/step, kernel %.2f us, %.1f TFLOP/s%s"
                       % (ew.name, e, r["us"], r["kernel_us"], r["tflops"],
                          "" if r["graph_us_per_call"] is None
@@ -579,7 +590,8 @@ def main():
         "data": "synthetic",
         "config": {"workload": w.name, "M": w.M, "N": w.N, "K": w.K, "epilogue": epi,
                    "inputs": "%s seed %d" % (w.dist, w.seed),
-                   "kernel_config": head["kernel_config"]},
+                   "kernel_config": head["kernel_config"],
+                   "calibrated": head["calibration_us"] is not None},
         "pct_of_peak": head["pct_of_peak"],
         "event_ms_per_step": head["event_us"] * 1e-3,
         "kernel_us": head["kernel_us"],

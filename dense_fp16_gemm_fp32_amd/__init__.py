@@ -30,7 +30,7 @@ EXPORTS = (
     "mi355gemm_num_configs",
     "mi355gemm_config_name", "mi355gemm_config_info", "mi355gemm_lds_budget",
     "mi355gemm_last_error", "mi355gemm_version", "mi355gemm_vector_add", "mi355gemm_softmax",
-    "mi355gemm_attention",
+    "mi355gemm_attention", "mi355gemm_set_choice", "mi355gemm_clear_choices",
 )
 
 
@@ -87,6 +87,10 @@ def library() -> ctypes.CDLL:
         lib.mi355gemm_attention.argtypes = [i64, i64, i64, i64, i64, p, p, p, p, p,
                                             ctypes.c_float, ci, p]
         lib.mi355gemm_attention.restype = ci
+        lib.mi355gemm_set_choice.argtypes = [i64, i64, i64, ci, ci, ci, ci]
+        lib.mi355gemm_set_choice.restype = ci
+        lib.mi355gemm_clear_choices.argtypes = []
+        lib.mi355gemm_clear_choices.restype = None
         lib.mi355gemm_version.argtypes = []
         lib.mi355gemm_version.restype = ctypes.c_char_p
         _lib = lib
@@ -119,6 +123,14 @@ def mi355gemm_softmax(M, N, x, y, stream) -> int:
 
 def mi355gemm_select(M, N, K, epi, A, B, C, bias) -> int:
     return library().mi355gemm_select(M, N, K, epi, A, B, C, bias)
+
+
+def mi355gemm_set_choice(M, N, K, epi, a_vector, bc_vector, config_id) -> int:
+    return library().mi355gemm_set_choice(M, N, K, epi, a_vector, bc_vector, config_id)
+
+
+def mi355gemm_clear_choices() -> None:
+    library().mi355gemm_clear_choices()
 
 
 def mi355gemm_num_configs() -> int:
@@ -380,6 +392,21 @@ def attention(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, causal: bool = 
     if st != OK:
         raise GemmError(st, mi355gemm_last_error())
     return out
+
+
+def set_choice(M: int, N: int, K: int, epilogue="none", a_vector: bool = True,
+               bc_vector: bool = True, config=None) -> None:
+    """Install ``config`` (a name or id) for requests of exactly this shape, epilogue and
+    alignment class in this process (``mi355gemm_set_choice``)."""
+    cid = config_id(config) if isinstance(config, str) else int(config)
+    st = mi355gemm_set_choice(M, N, K, _epi(epilogue), int(bool(a_vector)), int(bool(bc_vector)), cid)
+    if st != OK:
+        raise GemmError(st, mi355gemm_last_error())
+
+
+def clear_choices() -> None:
+    """Remove every installed choice (``mi355gemm_clear_choices``)."""
+    mi355gemm_clear_choices()
 
 
 def select(a: torch.Tensor, b: torch.Tensor, bias=None, epilogue="none", out=None) -> int:

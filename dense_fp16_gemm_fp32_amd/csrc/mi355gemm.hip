@@ -7,6 +7,8 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <atomic>
+#include <mutex>
 
 #include <stdarg.h>
 #include <stdint.h>
@@ -280,9 +282,39 @@ int tuned_choice(const Request &r, bool av, bool bv)
 // over four boxes).  The register-staged kernels take
 // small problems and those whose B or C rows are not 16-byte friendly (the direct kernels
 // need N % 8 == 0 and 16-byte aligned B and C; A may have any alignment).
+// Choices installed by the caller at run time (mi355gemm_set_choice), for example from
+// timings on the device in hand: some tiles run up to 25% slower on some MI355X boxes than
+// on others, so the best tile for a shape is a property of the box as well.  Host memory
+// only, one table per process; a mutex guards it, and the count lets launches skip the
+// lock while the table is empty.
+struct RuntimeChoice {
+    int64_t M, N, K;
+    int epi, a_vec, bc_vec, config;
+};
+constexpr int kMaxRuntimeChoices = 64;
+RuntimeChoice g_choices[kMaxRuntimeChoices];
+std::atomic<int> g_num_choices{0};
+std::mutex g_choices_mu;
+
+int runtime_choice(const Request &r, bool av, bool bv)
+{
+    if (g_num_choices.load(std::memory_order_acquire) == 0) return -1;
+    std::lock_guard<std::mutex> lock(g_choices_mu);
+    const int n = g_num_choices.load(std::memory_order_relaxed);
+    for (int i = 0; i < n; ++i) {
+        const RuntimeChoice &c = g_choices[i];
+        if (c.M == r.M && c.N == r.N && c.K == r.K && c.epi == r.epi && c.a_vec == (int)av &&
+            c.bc_vec == (int)bv && config_fits(kConfigs[c.config], r))
+            return c.config;
+    }
+    return -1;
+}
+
 int choose(const Request &r)
 {
     const bool av = a_vector_ok(r), bv = bc_vector_ok(r);
+    const int installed = runtime_choice(r, av, bv);
+    if (installed >= 0) return installed;
     const int tuned = tuned_choice(r, av, bv);
     if (tuned >= 0) return tuned;
     constexpr int64_t kCUs = 256;
@@ -543,6 +575,48 @@ mi355gemm_status mi355gemm_attention(int64_t batch, int64_t heads, int64_t seq_q
     if (e != hipSuccess)
         return fail(MI355GEMM_EHIP, "launch of attention failed: %s", hipGetErrorString(e));
     return MI355GEMM_OK;
+}
+
+mi355gemm_status mi355gemm_set_choice(int64_t M, int64_t N, int64_t K, int epi, int a_vector,
+                                      int bc_vector, int config_id)
+{
+    g_last_error[0] = 0;
+    if (M < 0 || N < 0 || K < 0)
+        return fail(MI355GEMM_EINVAL, "negative size (M=%lld N=%lld K=%lld)", (long long)M,
+                    (long long)N, (long long)K);
+    if (epi < MI355GEMM_EPI_NONE || epi > MI355GEMM_EPI_BIAS_GELU)
+        return fail(MI355GEMM_EINVAL, "unknown epilogue %d", epi);
+    if ((a_vector != 0 && a_vector != 1) || (bc_vector != 0 && bc_vector != 1))
+        return fail(MI355GEMM_EINVAL, "alignment classes are 0 or 1 (got %d, %d)", a_vector,
+                    bc_vector);
+    if (config_id < 0 || config_id >= kNumConfigs)
+        return fail(MI355GEMM_EINVAL, "unknown config id %d", config_id);
+    const Config &c = kConfigs[config_id];
+    if ((c.a_vec && !a_vector) || (c.bc_vec && !bc_vector) || (c.narrow && N > c.bn))
+        return fail(MI355GEMM_EUNSUPPORTED, "config %s cannot serve this alignment class or N",
+                    c.name);
+    std::lock_guard<std::mutex> lock(g_choices_mu);
+    const int n = g_num_choices.load(std::memory_order_relaxed);
+    for (int i = 0; i < n; ++i) {
+        RuntimeChoice &e = g_choices[i];
+        if (e.M == M && e.N == N && e.K == K && e.epi == epi && e.a_vec == a_vector &&
+            e.bc_vec == bc_vector) {
+            e.config = config_id;
+            return MI355GEMM_OK;
+        }
+    }
+    if (n == kMaxRuntimeChoices)
+        return fail(MI355GEMM_EUNSUPPORTED, "the table of installed choices is full (%d)",
+                    kMaxRuntimeChoices);
+    g_choices[n] = RuntimeChoice{M, N, K, epi, a_vector, bc_vector, config_id};
+    g_num_choices.store(n + 1, std::memory_order_release);
+    return MI355GEMM_OK;
+}
+
+void mi355gemm_clear_choices(void)
+{
+    std::lock_guard<std::mutex> lock(g_choices_mu);
+    g_num_choices.store(0, std::memory_order_release);
 }
 
 int mi355gemm_num_configs(void) { return kNumConfigs; }

@@ -147,6 +147,77 @@ def tune(shapes, rounds=7, margin=0.03, log=print, ms=20.0):
     return results
 
 
+def calibrate(a, b, bias=None, epilogue="none", out=None, candidates=None, ms=20.0,
+              rounds=4, prewarm_ms=100.0):
+    """Time candidate configurations for one call on the current device and install the
+    fastest for its shape, epilogue and alignment class in this process
+    (``mi355gemm_set_choice``).  The same tile can run up to 25% slower on one MI355X machine
+    than on another, while a neighbouring tile does not, so the measured table and the
+    rules cannot know the best tile for every box.
+
+    ``candidates``: configuration names; by default the direct configurations with the
+    same block_m x block_n as the selector's choice (ring depths, k-groups and stage
+    depths of one tile size).  Each must give the selector's output within 5e-3 relative
+    Frobenius distance.  Timing as in ``tune``: ``prewarm_ms`` of calls first, then
+    ``rounds`` interleaved rounds in alternating order, medians compared.  Returns
+    ``(name, {name: median us})``; with a single candidate nothing is timed or installed.
+    """
+    import torch
+    if ROOT not in sys.path:
+        sys.path.insert(0, ROOT)
+    import dense_fp16_gemm_fp32_amd as g
+
+    M, K = a.shape
+    N = b.shape[1]
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.float16, device=a.device)
+    b_arg = bias if epilogue != "none" else None
+    rule = g.select(a, b, b_arg, epilogue, out=out)
+    if rule < 0:
+        raise g.GemmError(g.EINVAL, g.mi355gemm_last_error())
+    info = g.mi355gemm_config_info(rule)
+    if candidates is None:
+        candidates = [c["name"] for c in g.configs()
+                      if c["direct"] and c["block_m"] == info["block_m"] and c["block_n"] == info["block_n"]]
+        if not info["direct"]:
+            candidates = [g.mi355gemm_config_name(rule)]
+    ref = g.gemm(a, b, b_arg, epilogue).float()
+    ref_norm = max(float(ref.norm()), 1e-30)
+    ids = {}
+    for name in candidates:
+        cid = g.config_id(name)
+        try:
+            g.gemm(a, b, b_arg, epilogue, out=out, config=cid)
+        except g.GemmError:
+            continue                                       # cannot serve this call
+        torch.cuda.synchronize()
+        if float((out.float() - ref).norm()) / ref_norm <= 5e-3:
+            ids[name] = cid
+    if not ids:
+        raise g.GemmError(g.EUNSUPPORTED, "no candidate configuration serves this call")
+    if len(ids) == 1:
+        return next(iter(ids)), {}
+    flops = 2.0 * M * N * K
+    steps = max(3, min(20000, int(ms * 1e-3 / max(flops / 1e15, 1e-9))))
+    calls = {n: (lambda cid=cid: g.gemm(a, b, b_arg, epilogue, out=out, config=cid)) for n, cid in ids.items()}
+    warm_steps = max(1, int(steps * prewarm_ms / ms / len(calls)))
+    for fn in calls.values():
+        for _ in range(warm_steps):
+            fn()
+    torch.cuda.synchronize()
+    times = {n: [] for n in calls}
+    items = list(calls.items())
+    for rnd in range(rounds):
+        for n, fn in (items if rnd % 2 == 0 else items[::-1]):
+            fn()
+            times[n].append(_time(fn, steps))
+    med = {n: statistics.median(v) for n, v in times.items()}
+    best = min(med, key=med.get)
+    av, bv = alignment_class(a, b, out, b_arg, K, N)
+    g.set_choice(M, N, K, epilogue, av, bv, best)
+    return best, med
+
+
 def table_source(results, device: str) -> str:
     lines = [
         "// Measured selector table: written by dense_fp16_gemm_fp32_amd/tune.py, do not edit.",

@@ -122,6 +122,28 @@ int mi355gemm_select(int64_t M, int64_t N, int64_t K, int epi,
                      const void *A, const void *B, const void *C, const void *bias);
 
 /*
+ * Install a choice for this process: requests with exactly these sizes and epilogue, whose
+ * A rows are (a_vector = 1) or are not (0) 16-byte friendly and whose B, C and bias rows
+ * are (bc_vector = 1) or are not (0), take config_id in mi355gemm_gemm,
+ * mi355gemm_gemm_timed with config_id -1 and mi355gemm_select, ahead of the measured
+ * table and the rules.  "16-byte friendly" is as for the configurations' alignment needs:
+ * K % 8 == 0 and A 16-byte aligned; N % 8 == 0, B and C 16-byte aligned and the bias
+ * 8-byte aligned.  The tutorial's point that the best schedule depends on the machine
+ * and the shape (thecryptopost.io page, section 3) holds from one MI355X machine to the next
+ * too, so a caller may time the candidates on its device and install the winner.  An entry
+ * with the same key is replaced.  Host memory only, no HIP call; safe to call while other
+ * threads launch.  Returns MI355GEMM_EINVAL for negative sizes, an unknown epilogue or
+ * config id, or a class other than 0 or 1; MI355GEMM_EUNSUPPORTED when the configuration
+ * needs 16-byte rows the class does not promise, computes fewer than N columns (narrow),
+ * or when the table already holds 64 entries.
+ */
+mi355gemm_status mi355gemm_set_choice(int64_t M, int64_t N, int64_t K, int epi,
+                                      int a_vector, int bc_vector, int config_id);
+
+/* Remove every choice installed with mi355gemm_set_choice. */
+void mi355gemm_clear_choices(void);
+
+/*
  * c[i] = a[i] + b[i] for 0 <= i < n, all fp16, one round-to-nearest-even per element (the
  * correctly rounded sum), enqueued on `stream`.  The tutorial's first kernel: "Designing
  * High-Performance GPU Kernels with TileLang: ...", ainovat.com page, first paragraph (a

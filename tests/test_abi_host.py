@@ -30,7 +30,7 @@ def header_functions():
 
 def test_library_exports_every_declared_symbol():
     declared = header_functions()
-    assert len(declared) == 13
+    assert len(declared) == 15
     assert sorted(g.EXPORTS) == declared
     lib = g.library()
     for name in declared:
@@ -384,3 +384,65 @@ def test_forced_narrow_config_rejects_more_than_8_columns():
         if c["narrow"]:
             assert _status(64, 9, 64, config=c["id"]) == g.EUNSUPPORTED
             assert "at most 8 columns" in g.mi355gemm_last_error()
+
+
+# ---- choices installed at run time ----------------------------------------------------
+
+def test_installed_choice_overrides_the_selector_for_its_exact_key_only():
+    k32, k64 = g.config_id("d128x128x32_w2x2_s4"), g.config_id("d128x128x64_w2x2_s4")
+    g.clear_choices()
+    try:
+        assert _select(2048, 2048, 2048) == k64                      # the rules
+        g.set_choice(2048, 2048, 2048, "none", True, True, "d128x128x32_w2x2_s4")
+        assert _select(2048, 2048, 2048) == k32
+        assert _select(2048, 2048, 2048, epi=2) == k64                # other epilogue
+        assert _select(2048, 2048, 2056) == k64                       # other shape
+        assert _select(2048, 2048, 2048, A=P2) != k32                 # other A class
+        g.set_choice(2048, 2048, 2048, "none", True, True, k64)       # same key: replaced
+        assert _select(2048, 2048, 2048) == k64
+        # a class-0 entry (rows not 16-byte friendly) names a configuration without
+        # 16-byte row needs, as the measured table's entries do
+        staged = g.config_id("s64x64x64_w2x1_an_bn")
+        g.set_choice(1000, 3001, 777, "bias_gelu", False, False, staged)
+        assert _select(1000, 3001, 777, epi=2) == staged
+        assert _select(1000, 3000, 777, epi=2) == k32                 # class 1: the rules
+        g.clear_choices()
+        assert _select(2048, 2048, 2048) == k64
+        assert _select(1000, 3001, 777, epi=2) == k32
+    finally:
+        g.clear_choices()
+
+
+def test_set_choice_rejects_bad_arguments():
+    k64 = g.config_id("d128x128x64_w2x2_s4")
+    vec = [c["id"] for c in g.configs() if c["a_vector"]][0]
+    narrow = [c["id"] for c in g.configs() if c["narrow"]][0]
+    lib_status = g.mi355gemm_set_choice
+    g.clear_choices()
+    try:
+        assert lib_status(-1, 8, 8, 0, 1, 1, k64) == g.EINVAL
+        assert lib_status(8, 8, 8, 3, 1, 1, k64) == g.EINVAL
+        assert lib_status(8, 8, 8, 0, 2, 1, k64) == g.EINVAL
+        assert lib_status(8, 8, 8, 0, 1, 1, -1) == g.EINVAL
+        assert lib_status(8, 8, 8, 0, 1, 1, g.mi355gemm_num_configs()) == g.EINVAL
+        assert lib_status(8, 8, 8, 0, 0, 1, vec) == g.EUNSUPPORTED    # needs 16-byte A rows
+        assert lib_status(8, 8, 8, 0, 1, 0, k64) == g.EUNSUPPORTED    # needs 16-byte B/C rows
+        assert lib_status(8, 9, 8, 0, 1, 0, narrow) == g.EUNSUPPORTED # 9 > 8 columns
+        assert lib_status(8, 8, 8, 0, 1, 1, narrow) == g.OK
+        with pytest.raises(g.GemmError):
+            g.set_choice(8, 8, 8, "none", True, True, -5)
+    finally:
+        g.clear_choices()
+
+
+def test_set_choice_table_holds_64_entries():
+    k64 = g.config_id("d128x128x64_w2x2_s4")
+    g.clear_choices()
+    try:
+        for i in range(64):
+            assert g.mi355gemm_set_choice(128, 128, 64 * (i + 1), 0, 1, 1, k64) == g.OK
+        assert g.mi355gemm_set_choice(128, 128, 64 * 65, 0, 1, 1, k64) == g.EUNSUPPORTED
+        assert g.mi355gemm_set_choice(128, 128, 64, 0, 1, 1, k64) == g.OK   # replacing is fine
+        assert _select(128, 128, 64 * 64) == k64
+    finally:
+        g.clear_choices()

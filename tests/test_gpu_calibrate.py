@@ -1,0 +1,55 @@
+"""Choices installed at run time on the GPU: calibrate() times one tile size's
+configurations on the device and installs the fastest; mi355gemm_gemm then launches it."""
+import numpy as np
+import pytest
+import torch
+
+import dense_fp16_gemm_fp32_amd as g
+from dense_fp16_gemm_fp32_amd import tune
+import oracle
+import workloads
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(autouse=True)
+def _no_installed_choices():
+    g.clear_choices()
+    yield
+    g.clear_choices()
+
+
+@pytest.mark.parametrize("shape,epi", [((1000, 3000, 777), "bias_gelu"), ((2048, 2048, 512), "none")],
+                         ids=lambda v: "x".join(map(str, v)) if isinstance(v, tuple) else v)
+def test_calibrate_installs_a_family_member_and_the_call_uses_it(shape, epi):
+    M, N, K = shape
+    print("calibrate", shape, epi, flush=True)
+    A, B, bias = workloads.make_inputs(M, N, K, "uniform", with_bias=True, seed=11)
+    Ad, Bd, biasd = A.cuda(), B.cuda(), bias.cuda()
+    b_arg = biasd if epi != "none" else None
+    rule = g.select(Ad, Bd, b_arg, epi)
+    info = g.mi355gemm_config_info(rule)
+    best, med = tune.calibrate(Ad, Bd, b_arg, epi, ms=2.0, rounds=2, prewarm_ms=10.0)
+    family = {c["name"] for c in g.configs() if c["direct"] and c["block_m"] == info["block_m"]
+              and c["block_n"] == info["block_n"]}
+    assert best in family and set(med) <= family and len(med) >= 2
+    assert g.mi355gemm_config_name(g.select(Ad, Bd, b_arg, epi)) == best
+    got = g.gemm(Ad, Bd, b_arg, epi)
+    forced = g.gemm(Ad, Bd, b_arg, epi, config=g.config_id(best))
+    torch.cuda.synchronize()
+    assert torch.equal(got.view(torch.int16), forced.view(torch.int16))
+    ref = oracle.gemm(A, B, bias if epi != "none" else None, epi).view(np.float16).astype(np.float64)
+    out = got.cpu().numpy().astype(np.float64)
+    assert np.linalg.norm(out - ref) <= 5e-3 * np.linalg.norm(ref)
+    assert np.all(np.abs(out - ref) <= 1e-2 * (1 + np.abs(ref)))
+    g.clear_choices()
+    assert g.select(Ad, Bd, b_arg, epi) == rule
+
+
+def test_calibrate_with_one_candidate_installs_nothing():
+    A, B, _ = workloads.make_inputs(256, 256, 256, "normal", seed=2)
+    Ad, Bd = A.cuda(), B.cuda()
+    rule = g.select(Ad, Bd)
+    name, med = tune.calibrate(Ad, Bd, candidates=["d128x128x64_w2x2_s4"])
+    assert name == "d128x128x64_w2x2_s4" and med == {}
+    assert g.select(Ad, Bd) == rule
