@@ -60,3 +60,16 @@ def test_kernel_hash_ignores_comments_but_not_code():
     src = "int a = 1;  // one\n\n// a note\nint b = a + 2;\n"
     assert bench.code_text(src) == bench.code_text("int a = 1;\nint b = a + 2;  // two\n")
     assert bench.code_text(src) != bench.code_text("int a = 1;\nint b = a + 3;\n")
+
+
+def test_traffic_lookup_covers_the_calibration_family_only_for_the_measured_code():
+    import bench
+    h = bench.kernel_sources_hash()
+    for name in ("d128x128x64_w2x2_s4", "d128x128x32_w2x2_s4", "d128x128x64_w2x2k2_s4"):
+        got = bench.traffic_for(name)
+        measured = (bench.TRAFFIC["sources_sha256_16"] == h if name == bench.TRAFFIC["kernel_config"]
+                    else bench.TRAFFIC_OTHER["sources_sha256_16"] == h)
+        assert (got is not None) == measured
+        if got is not None:
+            assert 25165824 <= got < 4 * 25165824   # A, B and C once, up to 4x that
+    assert bench.traffic_for("d256x256x32_w2x2_s4") is None
