@@ -81,7 +81,7 @@ def traffic_for(kernel_config: str):
     return None
 
 
-def parse():
+def parse(argv=None):
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=500)
@@ -106,7 +106,7 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run a 256 MiB device copy (counter calibration for rocprofv3)")
-    return ap.parse_args()
+    return ap.parse_args(argv)
 
 
 # Untimed warm-up lasts at least this long by default.  After a pause the engine clock

@@ -73,3 +73,10 @@ def test_traffic_lookup_covers_the_calibration_family_only_for_the_measured_code
         if got is not None:
             assert 25165824 <= got < 4 * 25165824   # A, B and C once, up to 4x that
     assert bench.traffic_for("d256x256x32_w2x2_s4") is None
+
+
+def test_bench_calibrates_by_default():
+    import bench
+    assert bench.parse([]).calibrate is True
+    assert bench.parse(["--no-calibrate"]).calibrate is False
+    assert bench.parse(["--config", "d128x128x32_w2x2_s4"]).config == "d128x128x32_w2x2_s4"
