@@ -605,6 +605,7 @@ def main():
         "pct_of_peak": head["pct_of_peak"],
         "event_ms_per_step": head["event_us"] * 1e-3,
         "kernel_us": head["kernel_us"],
+        "calibration_us": head["calibration_us"],
         "kernel_median_us": head["kernel_median_us"],
         "kernel_min_us": head["kernel_min_us"],
         "call_event_pair_us": head["call_event_pair_us"],
