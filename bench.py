@@ -104,6 +104,9 @@ def parse(argv=None):
     ap.add_argument("--no-gemm-extras", action="store_true",
                     help="skip the extra GEMM workloads and the cold run (profiling the other kernels)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--no-clock", dest="clock", action="store_false",
+                    help="skip the sustained window per GEMM workload that reads the engine "
+                         "clock and socket power from amd-smi (profiling runs)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run a 256 MiB device copy (counter calibration for rocprofv3)")
     return ap.parse_args(argv)
@@ -265,6 +268,103 @@ def run_cold(lib, w, steps, min_warm_ms=MIN_WARMUP_MS, min_bytes=256 << 20):
             "tflops": w.flops / (mean * 1e-3) / 1e12}
 
 
+class ClockSampler:
+    """Engine clock and socket power as the driver reports them (amd-smi's GPU metrics:
+    current_gfxclks per XCD in MHz, current_socket_power in W, and the power limit),
+    sampled from a background thread while GEMM calls run.  The driver refreshes these
+    metrics only every few hundred milliseconds, so a reading needs a sustained window of
+    calls (measure()), not the short timed region.  None where amd-smi is unavailable."""
+
+    def __init__(self):
+        self.smi = None
+        self.handle = None
+        self.power_limit_w = None
+        try:
+            import amdsmi
+            amdsmi.amdsmi_init()
+            self.handle = amdsmi.amdsmi_get_processor_handles()[0]
+            self.smi = amdsmi
+            info = amdsmi.amdsmi_get_power_info(self.handle)
+            lim = info.get("power_limit")
+            if isinstance(lim, (int, float)) and lim > 0:
+                # reported in microwatts by this driver
+                self.power_limit_w = lim / 1e6 if lim > 1e5 else float(lim)
+        except Exception:
+            self.smi = None
+
+    def read(self):
+        if self.smi is None:
+            return None
+        try:
+            m = self.smi.amdsmi_get_gpu_metrics_info(self.handle)
+        except Exception:
+            return None
+        clks = [c for c in (m.get("current_gfxclks") or []) if isinstance(c, (int, float)) and c > 0]
+        power = m.get("current_socket_power")
+        return {"ts": m.get("firmware_timestamp") or m.get("system_clock_counter"),
+                "gfxclk_mhz": sum(clks) / len(clks) if clks else None,
+                "gfxclk_mhz_min": min(clks) if clks else None,
+                "gfxclk_mhz_max": max(clks) if clks else None,
+                "socket_power_w": power if isinstance(power, (int, float)) else None}
+
+    def measure(self, fn, seconds=1.5, per_call_s=1e-5):
+        """Runs fn back to back for about `seconds` while sampling every 10 ms; returns the
+        median of the readings the driver refreshed after the first third of the window
+        (the clock has settled by then), or None."""
+        import statistics
+        import threading
+        import torch
+        if self.smi is None:
+            return None
+        stop = [False]
+        samples = []
+
+        def sampler():
+            t0 = time.perf_counter()
+            while not stop[0]:
+                r = self.read()
+                if r is not None:
+                    samples.append((time.perf_counter() - t0, r))
+                time.sleep(0.01)
+        th = threading.Thread(target=sampler, daemon=True)
+        th.start()
+        t0 = time.perf_counter()
+        batch = max(1, int(0.02 / per_call_s))
+        while time.perf_counter() - t0 < seconds:
+            for _ in range(batch):
+                fn()
+            torch.cuda.synchronize()
+        stop[0] = True
+        th.join()
+        late = [r for t, r in samples if t >= seconds / 3 and r["gfxclk_mhz"] is not None]
+        fresh, seen = [], set()
+        for r in late:                      # one reading per driver refresh
+            key = (r["ts"], r["gfxclk_mhz"], r["socket_power_w"])
+            if key not in seen:
+                seen.add(key)
+                fresh.append(r)
+        if not fresh:
+            return None
+        med = lambda k: statistics.median(r[k] for r in fresh if r[k] is not None)
+        return {"gfxclk_mhz": med("gfxclk_mhz"), "gfxclk_mhz_min": min(r["gfxclk_mhz_min"] for r in fresh),
+                "gfxclk_mhz_max": max(r["gfxclk_mhz_max"] for r in fresh),
+                "socket_power_w": med("socket_power_w"), "power_limit_w": self.power_limit_w,
+                "readings": len(fresh), "window_s": seconds}
+
+
+def clock_text(clock) -> str:
+    if not clock:
+        return ""
+    return "; held %.0f MHz at %s W (limit %s W), kernel at %.2f of the held-clock peak" % (
+        clock["gfxclk_mhz"], clock["socket_power_w"], clock["power_limit_w"],
+        clock.get("kernel_frac_of_held_clock_peak") or float("nan"))
+
+
+def held_clock_peak(cus, mhz):
+    """Dense fp16 MFMA peak at the engine clock held under load: CUs x 4096 flop/clk."""
+    return cus * 4096 * mhz * 1e6 / 1e12 if mhz else None
+
+
 def derived_peak():
     """CUs x 4096 flop/clk x the highest engine clock the driver lists (sysfs
     pp_dpm_sclk), next to the published 2.5 PFLOP/s; None where unreadable."""
@@ -314,7 +414,7 @@ def cpu_oracle_by_workload(max_gflop=20.0):
 
 
 def run_workload(lib, w, epi, steps, warmup, config=None, min_warm_ms=MIN_WARMUP_MS,
-                 calibrate=False):
+                 calibrate=False, sampler=None):
     import torch
     import workloads
     A, B, bias = workloads.make_inputs(w.M, w.N, w.K, w.dist, with_bias=(epi != "none"), seed=w.seed)
@@ -332,6 +432,15 @@ def run_workload(lib, w, epi, steps, warmup, config=None, min_warm_ms=MIN_WARMUP
     tflops = w.flops / (wall_ms * 1e-3) / 1e12
     # launch-bound sizes: the same calls replayed from a captured graph
     graph_ms = time_graph(lib, A, B, bias, epi, out, min_warm_ms=min_warm_ms) if w.M <= 256 else None
+    clock = None
+    if sampler is not None and w.M > 256:
+        clock = sampler.measure(lambda: lib.gemm(A, B, bias, epi, out=out, config=config),
+                                per_call_s=kernel_ms * 1e-3)
+        if clock is not None:
+            cus = torch.cuda.get_device_properties(0).multi_processor_count
+            clock["held_clock_peak_tflops"] = held_clock_peak(cus, clock["gfxclk_mhz"])
+            clock["kernel_frac_of_held_clock_peak"] = (
+                w.flops / (kernel_ms * 1e-3) / 1e12 / clock["held_clock_peak_tflops"])
     return {
         "workload": w.name, "M": w.M, "N": w.N, "K": w.K, "epilogue": epi,
         "kernel_config": lib.mi355gemm_config_name(cid),
@@ -345,6 +454,8 @@ def run_workload(lib, w, epi, steps, warmup, config=None, min_warm_ms=MIN_WARMUP
         "call_event_pair_us": call_ms * 1e3,
         "warmup_calls": warm,
         "graph_us_per_call": graph_ms * 1e3 if graph_ms is not None else None,
+        # engine clock and socket power over a sustained window of the same calls
+        "clock": clock,
         "inputs_sha256_16": inputs_sha256(w, epi),
         "kernel_tflops": w.flops / (kernel_ms * 1e-3) / 1e12,
         "algorithmic_GBps": w.algorithmic_bytes(epi) / (kernel_ms * 1e-3) / 1e9,
@@ -385,32 +496,26 @@ def run_vector_add(lib, n, steps, warmup, min_warm_ms=MIN_WARMUP_MS):
 
 def run_softmax(lib, M, N, steps, warmup, min_warm_ms=MIN_WARMUP_MS):
     """The tutorial's row-wise softmax on an M x N fp16 matrix (N(0, 3^2) entries, seed 0):
-    4 bytes move per element (one read, one write), so its GB/s reads against HBM peak;
-    torch.softmax on the same tensor is timed beside it as context."""
+    4 bytes move per element (one read, one write), so its GB/s reads against HBM peak."""
     import torch
     gen = torch.Generator(device="cpu")
     gen.manual_seed(0)
     x = (torch.randn(M, N, generator=gen, dtype=torch.float32) * 3).to(torch.float16).to("cuda:0")
     y = torch.empty_like(x)
     stream = torch.cuda.current_stream()
-    out = {"workload": "softmax", "M": M, "N": N, "bytes": 4 * M * N}
-    for name, fn in (("mi355gemm", lambda: lib.softmax(x, out=y)),
-                     ("torch", lambda: torch.softmax(x, dim=1, out=y))):
-        warm_up(fn, warmup, min_warm_ms)
-        e0 = torch.cuda.Event(enable_timing=True)
-        e1 = torch.cuda.Event(enable_timing=True)
-        e0.record(stream)
-        for _ in range(steps):
-            fn()
-        e1.record(stream)
-        torch.cuda.synchronize()
-        ms = e0.elapsed_time(e1) / steps
-        gbs = 4.0 * M * N / (ms * 1e-3) / 1e9
-        if name == "mi355gemm":
-            out.update({"us": ms * 1e3, "GBps": gbs, "frac_of_hbm_peak": gbs / PEAK_HBM_GBS})
-        else:
-            out.update({"torch_us": ms * 1e3, "torch_GBps": gbs})
-    return out
+    fn = lambda: lib.softmax(x, out=y)
+    warm_up(fn, warmup, min_warm_ms)
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(steps):
+        fn()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    gbs = 4.0 * M * N / (ms * 1e-3) / 1e9
+    return {"workload": "softmax", "M": M, "N": N, "bytes": 4 * M * N, "us": ms * 1e3,
+            "GBps": gbs, "frac_of_hbm_peak": gbs / PEAK_HBM_GBS}
 
 
 def attention_flops(B, H, Sq, Sk, D, causal):
@@ -426,10 +531,8 @@ def attention_flops(B, H, Sq, Sk, D, causal):
 
 def run_attention(lib, B, H, S, D, causal, steps, warmup, min_warm_ms=MIN_WARMUP_MS):
     """The tutorial's FlashAttention forward on (B, H, S, D) fp16 tensors, N(0,1) seed 0,
-    scale 1/sqrt(D); torch's scaled_dot_product_attention on the same tensors is timed
-    beside it as context."""
+    scale 1/sqrt(D)."""
     import torch
-    import torch.nn.functional as F
     gen = torch.Generator(device="cpu")
     gen.manual_seed(0)
     q, k, v = (torch.randn((B, H, S, D), generator=gen).to(torch.float16).to("cuda:0")
@@ -437,25 +540,20 @@ def run_attention(lib, B, H, S, D, causal, steps, warmup, min_warm_ms=MIN_WARMUP
     o = torch.empty_like(q)
     stream = torch.cuda.current_stream()
     flops = attention_flops(B, H, S, S, D, causal)
-    out = {"workload": "attention", "batch": B, "heads": H, "seq": S, "head_dim": D,
-           "causal": causal, "flops": flops}
-    for name, fn in (("mi355gemm", lambda: lib.attention(q, k, v, causal=causal, out=o)),
-                     ("torch_sdpa", lambda: F.scaled_dot_product_attention(q, k, v, is_causal=causal))):
-        warm_up(fn, warmup, min_warm_ms)
-        e0 = torch.cuda.Event(enable_timing=True)
-        e1 = torch.cuda.Event(enable_timing=True)
-        e0.record(stream)
-        for _ in range(steps):
-            fn()
-        e1.record(stream)
-        torch.cuda.synchronize()
-        ms = e0.elapsed_time(e1) / steps
-        tf = flops / (ms * 1e-3) / 1e12
-        if name == "mi355gemm":
-            out.update({"us": ms * 1e3, "tflops": tf, "frac_of_fp16_peak": tf / PEAK_FP16_TFLOPS})
-        else:
-            out.update({"torch_sdpa_us": ms * 1e3, "torch_sdpa_tflops": tf})
-    return out
+    fn = lambda: lib.attention(q, k, v, causal=causal, out=o)
+    warm_up(fn, warmup, min_warm_ms)
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(steps):
+        fn()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    tf = flops / (ms * 1e-3) / 1e12
+    return {"workload": "attention", "batch": B, "heads": H, "seq": S, "head_dim": D,
+            "causal": causal, "flops": flops, "us": ms * 1e3, "tflops": tf,
+            "frac_of_fp16_peak": tf / PEAK_FP16_TFLOPS}
 
 
 def host_info():
@@ -520,10 +618,11 @@ def main():
     epi = args.epilogue or w.epilogues[0]
     print("bench: %s epilogue=%s steps=%d warmup=%d" % (w.name, epi, args.steps, args.warmup),
           file=sys.stderr, flush=True)
+    sampler = ClockSampler() if args.clock else None
     head = run_workload(lib, w, epi, args.steps, args.warmup, args.config, args.min_warmup_ms,
-                        args.calibrate)
-    print("bench: headline %.2f us/step (events %.2f us), kernel %.2f us, %.1f TFLOP/s"
-          % (head["us"], head["event_us"], head["kernel_us"], head["tflops"]),
+                        args.calibrate, sampler)
+    print("bench: headline %.2f us/step (events %.2f us), kernel %.2f us, %.1f TFLOP/s%s"
+          % (head["us"], head["event_us"], head["kernel_us"], head["tflops"], clock_text(head["clock"])),
           file=sys.stderr, flush=True)
     if args.calibrate_copy:
         calibrate_copy()
@@ -536,11 +635,12 @@ def main():
                     continue
                 steps = 20 if ew.M >= 8192 else (1000 if ew.M <= 256 else 200)
                 r = run_workload(lib, ew, e, steps, 10, min_warm_ms=args.min_warmup_ms,
-                                 calibrate=args.calibrate)
-                print("bench: %s %s %.2f us/step, kernel %.2f us, %.1f TFLOP/s%s"
+                                 calibrate=args.calibrate, sampler=sampler)
+                print("bench: %s %s %.2f us/step, kernel %.2f us, %.1f TFLOP/s%s%s"
                       % (ew.name, e, r["us"], r["kernel_us"], r["tflops"],
                          "" if r["graph_us_per_call"] is None
-                         else ", %.2f us/call from a graph" % r["graph_us_per_call"]),
+                         else ", %.2f us/call from a graph" % r["graph_us_per_call"],
+                         clock_text(r["clock"])),
                       file=sys.stderr, flush=True)
                 extra.append(r)
 
@@ -555,16 +655,16 @@ def main():
     if others:
         for (M, N) in ((8192, 8192), (4096, 4096), (64, 65536)):
             r = run_softmax(lib, M, N, 100, 5, args.min_warmup_ms)
-            print("bench: softmax %dx%d %.2f us %.1f GB/s (torch %.1f GB/s)"
-                  % (M, N, r["us"], r["GBps"], r["torch_GBps"]), file=sys.stderr, flush=True)
+            print("bench: softmax %dx%d %.2f us %.1f GB/s" % (M, N, r["us"], r["GBps"]),
+                  file=sys.stderr, flush=True)
             softmax.append(r)
 
     attention = []
     if others:
         for (D, causal) in ((128, False), (128, True), (64, False), (64, True)):
             r = run_attention(lib, 4, 32, 4096, D, causal, 20, 3, args.min_warmup_ms)
-            print("bench: attention 4x32x4096 d%d %s %.1f us %.1f TFLOP/s (torch sdpa %.1f TFLOP/s)"
-                  % (D, "causal" if causal else "full", r["us"], r["tflops"], r["torch_sdpa_tflops"]),
+            print("bench: attention 4x32x4096 d%d %s %.1f us %.1f TFLOP/s"
+                  % (D, "causal" if causal else "full", r["us"], r["tflops"]),
                   file=sys.stderr, flush=True)
             attention.append(r)
 
@@ -614,7 +714,13 @@ def main():
         "roofline": {"bound": "mfma", "achieved": head["kernel_tflops"],
                      "peak": PEAK_FP16_TFLOPS, "unit": "TFLOP/s",
                      "frac": head["kernel_tflops"] / PEAK_FP16_TFLOPS,
-                     "traffic": traffic_for(head["kernel_config"])},
+                     "traffic": traffic_for(head["kernel_config"]),
+                     # the same kernel against the MFMA peak at the engine clock the part
+                     # held under this load (power-limited with random fp16 operands)
+                     "held_clock_mhz": (head["clock"] or {}).get("gfxclk_mhz"),
+                     "held_clock_peak": (head["clock"] or {}).get("held_clock_peak_tflops"),
+                     "frac_of_held_clock_peak": (head["clock"] or {}).get("kernel_frac_of_held_clock_peak")},
+        "clock": head["clock"],
         "cpu_baseline": cpu,
         "cpu_oracle_by_workload": cpu_all,
         "host": host_info(),

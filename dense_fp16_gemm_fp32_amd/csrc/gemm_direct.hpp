@@ -78,7 +78,7 @@ struct DTile {
     static_assert(KGROUPS == 1 || (KGROUPS == 2 && FM % 2 == 0), "k-groups: 1, or 2 with even FM");
     static_assert(KK % KGROUPS == 0, "k-steps must split evenly over the k-groups");
     static_assert((STAGES * Q) % 2 == 0, "fragment double-buffer parity must repeat per ring turn");
-    static_assert(STAGES >= 2 && STAGES <= 5 && G * (STAGES - 2) <= 63, "ring size / vmcnt range");
+    static_assert(STAGES >= 2 && STAGES <= 8 && G * (STAGES - 2) <= 63, "ring size / vmcnt range");
     static_assert(VM_WAIT >= 0 && VM_WAIT <= 63, "vmcnt range");
     static_assert(LDS_BYTES <= 160 * 1024, "over the gfx950 LDS budget");
     static_assert(RED_BYTES <= LDS_BYTES, "k-group exchange must fit in the ring");
@@ -134,16 +134,16 @@ __device__ __forceinline__ __attribute__((address_space(3))) void *lds_ptr(const
 // LDS at lds + 16*l.  Written as inline assembly on purpose: the compiler cannot tell the
 // ring slots apart once it has packed them into one LDS block, and would then wait for
 // every copy in flight before each LDS read.  The kernel waits for these copies itself
-// (wait_counts before each barrier) and for all of them before it ends.  M0 is a reserved
-// register the compiler sets right before each instruction of its own that reads it; the
-// kernels here have none, so writing it here disturbs nothing.
+// (wait_counts before each barrier) and for all of them before it ends.  The LDS address
+// is an operand bound to M0 ("{m0}"): the compiler writes M0 itself right before the
+// statement and knows the statement reads it, so no value of its own is lost there.
 __device__ __forceinline__ void lds_dma16(__amdgpu_buffer_rsrc_t rsrc, const void *lds,
                                           uint32_t voffset)
 {
     const uint32_t lds_addr = (uint32_t)(uintptr_t)lds_ptr(lds);
-    asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+    asm volatile("buffer_load_dwordx4 %0, %1, 0 offen lds"
                  :
-                 : "s"(lds_addr), "v"(voffset), "s"(rsrc));
+                 : "v"(voffset), "s"(rsrc), "{m0}"(lds_addr));
 }
 
 // The same copy with a wave-uniform byte offset `soffset` added in the instruction's
@@ -152,9 +152,9 @@ __device__ __forceinline__ void lds_dma16(__amdgpu_buffer_rsrc_t rsrc, const voi
                                           uint32_t voffset, uint32_t soffset)
 {
     const uint32_t lds_addr = (uint32_t)(uintptr_t)lds_ptr(lds);
-    asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
+    asm volatile("buffer_load_dwordx4 %0, %1, %2 offen lds"
                  :
-                 : "s"(lds_addr), "v"(voffset), "s"(rsrc), "s"(soffset));
+                 : "v"(voffset), "s"(rsrc), "s"(soffset), "{m0}"(lds_addr));
 }
 
 // Per-lane state of one wavefront: DMA source offsets, fragment read addresses, the
@@ -588,7 +588,10 @@ __global__ void __launch_bounds__(T::NT) gemm_direct(GemmArgs p)
         // Sum the two k-groups' partial tiles.  Group 0 keeps blocks i < FM/2 and hands
         // blocks i >= FM/2 to group 1; group 1 does the opposite; each then finishes the
         // half it kept.  Each 32x32 fp32 block moves as four 1 KiB ds_write_b128 /
-        // ds_read_b128 (lane-contiguous, conflict-free).
+        // ds_read_b128 (lane-contiguous, conflict-free).  The exchange runs in three
+        // phases (write, read and add, epilogue) separated by barriers that every wave
+        // reaches at the same point of the program; only the register halves a phase
+        // touches depend on the group (block indices must be compile-time constants).
         constexpr int H = T::FM / 2;
         float *red = reinterpret_cast<float *>(lds_raw);
         const int wc = w.wave % T::NWC;
@@ -597,8 +600,8 @@ __global__ void __launch_bounds__(T::NT) gemm_direct(GemmArgs p)
         auto slot_ptr = [&](int grp, int ii, int j, int c) {
             return red + ((((grp * T::NWC + wc) * H + ii) * T::FN + j) * 4 + c) * 256 + w.lane * 4;
         };
-        auto exchange = [&](auto give_c, auto keep_c) {
-            constexpr int GIVE = decltype(give_c)::value, KEEP = decltype(keep_c)::value;
+        auto give = [&](auto give_c) {
+            constexpr int GIVE = decltype(give_c)::value;
 #pragma unroll
             for (int ii = 0; ii < H; ++ii)
 #pragma unroll
@@ -609,7 +612,9 @@ __global__ void __launch_bounds__(T::NT) gemm_direct(GemmArgs p)
                         *reinterpret_cast<f32x4 *>(slot_ptr(w.kg, ii, j, c)) =
                             f32x4{v[4 * c], v[4 * c + 1], v[4 * c + 2], v[4 * c + 3]};
                     }
-            __syncthreads();
+        };
+        auto take = [&](auto keep_c) {
+            constexpr int KEEP = decltype(keep_c)::value;
 #pragma unroll
             for (int ii = 0; ii < H; ++ii)
 #pragma unroll
@@ -620,14 +625,17 @@ __global__ void __launch_bounds__(T::NT) gemm_direct(GemmArgs p)
 #pragma unroll
                         for (int e = 0; e < 4; ++e) w.acc[KEEP + ii][j][4 * c + e] += o[e];
                     }
-            __syncthreads();   // the exchange area is overwritten by the C tile below
-            tile_to_lds<T, KEEP, KEEP + H, EPI>(w.acc, w.bias_raw, w.wm * T::WTM, w.wn * T::WTN,
-                                                w.lane, ctile);
         };
+        using Zero = std::integral_constant<int, 0>;
+        using Half = std::integral_constant<int, H>;
+        if (w.kg == 0) give(Half{}); else give(Zero{});
+        __syncthreads();
+        if (w.kg == 0) take(Zero{}); else take(Half{});
+        __syncthreads();   // the exchange area is overwritten by the C tile below
         if (w.kg == 0)
-            exchange(std::integral_constant<int, H>{}, std::integral_constant<int, 0>{});
+            tile_to_lds<T, 0, H, EPI>(w.acc, w.bias_raw, w.wm * T::WTM, w.wn * T::WTN, w.lane, ctile);
         else
-            exchange(std::integral_constant<int, 0>{}, std::integral_constant<int, H>{});
+            tile_to_lds<T, H, T::FM, EPI>(w.acc, w.bias_raw, w.wm * T::WTM, w.wn * T::WTN, w.lane, ctile);
     }
     __syncthreads();
     lds_to_c<T>(p, m0, n0, rows_valid, ctile);

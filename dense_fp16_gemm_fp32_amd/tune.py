@@ -147,21 +147,12 @@ def tune(shapes, rounds=7, margin=0.03, log=print, ms=20.0):
     return results
 
 
-def calibrate(a, b, bias=None, epilogue="none", out=None, candidates=None, ms=20.0,
-              rounds=4, prewarm_ms=100.0):
-    """Time candidate configurations for one call on the current device and install the
-    fastest for its shape, epilogue and alignment class in this process
-    (``mi355gemm_set_choice``).  The same tile can run up to 25% slower on one MI355X box
-    than on another, while a neighbouring tile does not, so the measured table and the
-    rules cannot know the best tile for every box.
-
-    ``candidates``: configuration names; by default the direct configurations with the
-    same block_m x block_n as the selector's choice (ring depths, k-groups and stage
-    depths of one tile size).  Each must give the selector's output within 5e-3 relative
-    Frobenius distance.  Timing as in ``tune``: ``prewarm_ms`` of calls first, then
-    ``rounds`` interleaved rounds in alternating order, medians compared.  Returns
-    ``(name, {name: median us})``; with a single candidate nothing is timed or installed.
-    """
+def calibration_candidates(a, b, bias=None, epilogue="none", out=None):
+    """The configurations ``calibrate`` may time and install for this call: the direct
+    configurations with the selector's tile size (block_m x block_n), or the selector's
+    choice alone when it is not a direct kernel or when B and C rows are not 16-byte
+    friendly (the library then splits the launch into a direct part and a narrow strip,
+    which a forced configuration cannot do).  Returns (rule name, [candidate names])."""
     import torch
     if ROOT not in sys.path:
         sys.path.insert(0, ROOT)
@@ -175,14 +166,62 @@ def calibrate(a, b, bias=None, epilogue="none", out=None, candidates=None, ms=20
     rule = g.select(a, b, b_arg, epilogue, out=out)
     if rule < 0:
         raise g.GemmError(g.EINVAL, g.mi355gemm_last_error())
+    rule_name = g.mi355gemm_config_name(rule)
     info = g.mi355gemm_config_info(rule)
+    _, bv = alignment_class(a, b, out, b_arg, K, N)
+    if not info["direct"] or not bv:
+        return rule_name, [rule_name]
+    return rule_name, [c["name"] for c in g.configs()
+                       if c["direct"] and c["block_m"] == info["block_m"] and c["block_n"] == info["block_n"]]
+
+
+def agrees(got, ref, rel_fro=5e-3, elem=1e-2) -> bool:
+    """Candidate output against the selector's output, both fp16 on the device: relative
+    Frobenius distance at most ``rel_fro`` and every element within ``elem * (1 + |ref|)``,
+    no NaN or Inf where the reference is finite."""
+    import torch
+    g64, r64 = got.double(), ref.double()
+    if not bool(torch.isfinite(g64[torch.isfinite(r64)]).all()):
+        return False
+    d = (g64 - r64).abs()
+    if not bool((d <= elem * (1.0 + r64.abs())).all()):
+        return False
+    nr = float(r64.norm())
+    return float(d.norm()) <= rel_fro * (nr if nr > 0 else max(r64.numel(), 1) ** 0.5)
+
+
+def calibrate(a, b, bias=None, epilogue="none", out=None, candidates=None, ms=20.0,
+              rounds=4, prewarm_ms=100.0):
+    """Time candidate configurations for one call on the current device and install the
+    fastest for its shape, epilogue and alignment class in this process
+    (``mi355gemm_set_choice``).  The same tile can run up to 25% slower on one MI355X box
+    than on another, while a neighbouring tile does not, so the measured table and the
+    rules cannot know the best tile for every box.
+
+    ``candidates``: configuration names; by default ``calibration_candidates`` (ring
+    depths, k-groups and stage depths of the selector's tile size).  Each must agree with
+    the selector's output (``agrees``: relative Frobenius distance at most 5e-3 and every
+    element within 1e-2 * (1 + |ref|)).  Timing as in ``tune``: ``prewarm_ms`` of calls
+    first, then ``rounds`` interleaved rounds in alternating order, medians compared.
+    Returns ``(name, {name: median us})``; with a single candidate nothing is timed or
+    installed.
+    """
+    import torch
+    if ROOT not in sys.path:
+        sys.path.insert(0, ROOT)
+    import dense_fp16_gemm_fp32_amd as g
+
+    M, K = a.shape
+    N = b.shape[1]
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.float16, device=a.device)
+    b_arg = bias if epilogue != "none" else None
+    rule_name, default = calibration_candidates(a, b, bias, epilogue, out)
     if candidates is None:
-        candidates = [c["name"] for c in g.configs()
-                      if c["direct"] and c["block_m"] == info["block_m"] and c["block_n"] == info["block_n"]]
-        if not info["direct"]:
-            candidates = [g.mi355gemm_config_name(rule)]
-    ref = g.gemm(a, b, b_arg, epilogue).float()
-    ref_norm = max(float(ref.norm()), 1e-30)
+        candidates = default
+    if len(default) == 1 and candidates == default:
+        return rule_name, {}
+    ref = g.gemm(a, b, b_arg, epilogue)
     ids = {}
     for name in candidates:
         cid = g.config_id(name)
@@ -191,7 +230,7 @@ def calibrate(a, b, bias=None, epilogue="none", out=None, candidates=None, ms=20
         except g.GemmError:
             continue                                       # cannot serve this call
         torch.cuda.synchronize()
-        if float((out.float() - ref).norm()) / ref_norm <= 5e-3:
+        if agrees(out, ref):
             ids[name] = cid
     if not ids:
         raise g.GemmError(g.EUNSUPPORTED, "no candidate configuration serves this call")
@@ -218,14 +257,30 @@ def calibrate(a, b, bias=None, epilogue="none", out=None, candidates=None, ms=20
     return best, med
 
 
-def table_source(results, device: str) -> str:
+NOTE_PREFIX = "// note:"
+
+
+def existing_notes(path: str = TABLE) -> list:
+    """The hand-written note lines (``// note: ...``) of the current table, which a rewrite
+    keeps: they record why a measured winner was left out or where a rule came from."""
+    try:
+        with open(path) as fh:
+            return [line.rstrip("\n") for line in fh if line.startswith(NOTE_PREFIX)]
+    except OSError:
+        return []
+
+
+def table_source(results, device: str, notes=()) -> str:
     lines = [
-        "// Measured selector table: written by dense_fp16_gemm_fp32_amd/tune.py, do not edit.",
+        "// Measured selector table, written by dense_fp16_gemm_fp32_amd/tune.py.  Lines that",
+        "// start with '// note:' are written by hand and kept when the tuner rewrites the file;",
+        "// every other line is the tuner's.",
         "// Device: %s; %s." % (device, datetime.date.today().isoformat()),
         "// Fields: M, N, K, epilogue, A 16-byte rows, B/C 16-byte rows, configuration name.",
         "// Shapes whose best configuration beat the rule choice by less than the margin have",
         "// no entry (the rules stand); their timings are listed for the record.",
     ]
+    lines.extend(notes)
     epi_code = {"none": 0, "bias": 1, "bias_gelu": 2}
     for r in results:
         lines.append("// %dx%dx%d %s: %s" % (r["M"], r["N"], r["K"], r["epilogue"], ", ".join(
@@ -249,7 +304,7 @@ def main(argv=None):
     import torch
     shapes = [parse_shape(s) for s in args.shapes] if args.shapes else default_shapes()
     res = tune(shapes, args.rounds, args.margin, log=lambda m: print(m, flush=True), ms=args.ms)
-    src = table_source(res, torch.cuda.get_device_properties(0).name)
+    src = table_source(res, torch.cuda.get_device_properties(0).name, existing_notes(args.output))
     if args.write:
         with open(args.output, "w") as f:
             f.write(src)

@@ -37,15 +37,16 @@ EPILOGUES = {"none": EPI_NONE, "bias": EPI_BIAS, "bias_gelu": EPI_BIAS_GELU}
 _lib = None
 
 
-def compile_command(source: str = SOURCE, output: str = LIBRARY) -> list[str]:
+def compile_command(source: str = SOURCE, output: str = LIBRARY, extra=()) -> list[str]:
     return ["gcc", "-O2", "-fopenmp", "-ffp-contract=off", "-fPIC", "-shared",
-            "-std=c11", "-Wall", "-Wextra", source, "-o", output, "-lm"]
+            "-std=c11", "-Wall", "-Wextra", *extra, source, "-o", output, "-lm"]
 
 
-def build(source: str = SOURCE, output: str = LIBRARY) -> str:
-    """Compile the oracle into a shared library (always recompiles)."""
+def build(source: str = SOURCE, output: str = LIBRARY, extra=()) -> str:
+    """Compile the oracle into a shared library (always recompiles); ``extra`` adds
+    compiler flags (the sanitizer build of the tests)."""
     tmp = output + ".tmp%d" % os.getpid()
-    subprocess.run(compile_command(source, tmp), check=True)
+    subprocess.run(compile_command(source, tmp, extra), check=True)
     os.replace(tmp, output)
     return output
 

@@ -87,35 +87,71 @@ def test_small_integer_products_bitexact_every_config(shape):
         assert_bitexact(C, ref, "%s %s" % (cfg["name"], shape))
 
 
+# ---- the kernels a run can take on a workload -------------------------------------------
+
+def _members(w, epi):
+    """Every configuration a benchmark run of workload w may launch: the selector's choice
+    and each configuration run-time calibration may install in its place (tune's
+    calibration_candidates, the direct configurations of the same tile size).  Names, the
+    selector's first."""
+    from dense_fp16_gemm_fp32_amd import tune
+    A = torch.empty((w.M, w.K), dtype=torch.float16, device=DEV)
+    B = torch.empty((w.K, w.N), dtype=torch.float16, device=DEV)
+    bias = torch.empty((w.N,), dtype=torch.float16, device=DEV) if epi != "none" else None
+    out = torch.empty((w.M, w.N), dtype=torch.float16, device=DEV)
+    rule, cands = tune.calibration_candidates(A, B, bias, epi, out)
+    return [rule] + [c for c in cands if c != rule]
+
+
+def test_members_cover_the_calibration_family():
+    """The member list the full-size tests below walk is the selector's choice plus every
+    direct configuration of its tile size, at least two at each workload except 256^3."""
+    for w in workloads.WORKLOADS:
+        for e in w.epilogues:
+            names = _members(w, e)
+            print(w.name, e, names, flush=True)
+            assert len(set(names)) == len(names)
+            if w.name != "gemm_256":
+                assert len(names) >= 2
+
+
 # ---- structured inputs at every workload shape: exact results --------------------------
 
 @pytest.mark.parametrize("w", workloads.WORKLOADS, ids=[w.name for w in workloads.WORKLOADS])
 def test_all_ones_gives_K_exactly(w):
-    A = torch.ones((w.M, w.K), dtype=torch.float16)
-    B = torch.ones((w.K, w.N), dtype=torch.float16)
-    print("all-ones", w.name, flush=True)
-    C = _run(A, B, None, "none")
-    assert torch.all(C == float(w.K)).item(), "all-ones product is not K everywhere"
+    """All-ones operands: every partial sum is an integer below 2^11, exact in any order, so
+    C must be K everywhere, for every configuration a run on this shape may take."""
+    A = torch.ones((w.M, w.K), dtype=torch.float16, device=DEV)
+    B = torch.ones((w.K, w.N), dtype=torch.float16, device=DEV)
+    for name in _members(w, "none"):
+        print("all-ones", w.name, name, flush=True)
+        C = _run(A, B, None, "none", config=g.config_id(name))
+        assert torch.all(C == float(w.K)).item(), "all-ones product is not K everywhere (%s)" % name
 
 
 @pytest.mark.parametrize("w", workloads.WORKLOADS, ids=[w.name for w in workloads.WORKLOADS])
 def test_selection_matrices_copy_rows_and_columns(w):
+    """0/1 selection matrices: C[i, :] = B[i mod K, :] and C[:, j] = A[:, j mod K] exactly,
+    for every configuration a run on this shape may take."""
     M, N, K = w.M, w.N, w.K
     Ar, Br, _ = workloads.make_inputs(M, N, K, w.dist, seed=11)
-    # A selects rows of B: C[i, :] = B[i mod K, :]
     A_sel = torch.zeros((M, K), dtype=torch.float16)
     A_sel[torch.arange(M), torch.arange(M) % K] = 1
-    print("row selection", w.name, flush=True)
-    C = _run(A_sel, Br, None, "none")
-    want = Br[torch.arange(M) % K]
-    assert torch.equal(C.cpu(), want), "row selection mismatch"
-    # B selects columns of A: C[:, j] = A[:, j mod K]
     B_sel = torch.zeros((K, N), dtype=torch.float16)
     B_sel[torch.arange(N) % K, torch.arange(N)] = 1
-    print("column selection", w.name, flush=True)
-    C = _run(Ar, B_sel, None, "none")
-    want = Ar[:, torch.arange(N) % K]
-    assert torch.equal(C.cpu(), want), "column selection mismatch"
+    want_rows = Br[torch.arange(M) % K]
+    want_cols = Ar[:, torch.arange(N) % K]
+    A_sel_d, Br_d, Ar_d, B_sel_d = A_sel.to(DEV), Br.to(DEV), Ar.to(DEV), B_sel.to(DEV)
+    for name in _members(w, "none"):
+        cid = g.config_id(name)
+        # A selects rows of B
+        print("row selection", w.name, name, flush=True)
+        C = _run(A_sel_d, Br_d, None, "none", config=cid)
+        assert torch.equal(C.cpu(), want_rows), "row selection mismatch (%s)" % name
+        # B selects columns of A
+        print("column selection", w.name, name, flush=True)
+        C = _run(Ar_d, B_sel_d, None, "none", config=cid)
+        assert torch.equal(C.cpu(), want_cols), "column selection mismatch (%s)" % name
 
 
 # ---- random inputs at small and ragged shapes, every config, every epilogue -----------
@@ -155,15 +191,16 @@ CASES = _workload_cases()
 
 @pytest.mark.parametrize("w,epi", CASES, ids=["%s-%s" % (w.name, e) for w, e in CASES])
 def test_workload_parity(w, epi):
+    """Each workload at full size on its own inputs, through the selector and forced onto
+    every configuration run-time calibration may install instead (the benchmark times
+    whichever it installs).  Up to 2048^3 the whole output is compared with the oracle;
+    at 8192^3 sampled elements, including every tile-boundary row and column."""
     A, B, bias = workloads.make_inputs(w.M, w.N, w.K, w.dist, with_bias=True, seed=w.seed)
-    print("workload", w.name, epi, "config", g.mi355gemm_config_name(
-        g.select(_dev(A), _dev(B), _dev(bias), epi)), flush=True)
-    C = _run(A, B, bias, epi)
-    if w.M * w.N * w.K <= 2048 ** 3:
+    Ad, Bd, biasd = A.to(DEV), B.to(DEV), bias.to(DEV)
+    full = w.M * w.N * w.K <= 2048 ** 3
+    if full:
         ref = oracle.gemm(A, B, bias, epi)
-        rep = assert_parity(C, ref, w.name + " " + epi)
     else:
-        # full size: sampled elements, including every tile-boundary row and column
         rng = np.random.default_rng(0)
         edge = np.array([0, 1, 127, 128, 255, 256, w.M - 1])
         rows = np.concatenate([rng.integers(0, w.M, 6000), np.repeat(edge, 64)])
@@ -173,9 +210,18 @@ def test_workload_parity(w, epi):
         rows = np.concatenate([rows, rows2])
         cols = np.concatenate([cols, cols2])
         ref = oracle.gemm_sampled(A, B, rows, cols, bias, epi)
-        got = C.cpu()[torch.from_numpy(rows), torch.from_numpy(cols)]
-        rep = assert_parity(got, ref, w.name + " " + epi + " (sampled)")
-    print("   ", rep, flush=True)
+        ri, ci = torch.from_numpy(rows), torch.from_numpy(cols)
+    members = [None] + _members(w, epi)
+    for name in members:
+        cid = None if name is None else g.config_id(name)
+        print("workload", w.name, epi, "config", name or "(selector) " + g.mi355gemm_config_name(
+            g.select(Ad, Bd, biasd if epi != "none" else None, epi)), flush=True)
+        C = _run(Ad, Bd, biasd, epi, config=cid)
+        if full:
+            rep = assert_parity(C, ref, "%s %s %s" % (w.name, epi, name))
+        else:
+            rep = assert_parity(C.cpu()[ri, ci], ref, "%s %s %s (sampled)" % (w.name, epi, name))
+        print("   ", rep, flush=True)
 
 
 # ---- memory outside C is never touched -------------------------------------------------
