@@ -307,10 +307,11 @@ class ClockSampler:
                 "gfxclk_mhz_max": max(clks) if clks else None,
                 "socket_power_w": power if isinstance(power, (int, float)) else None}
 
-    def measure(self, fn, seconds=1.5, per_call_s=1e-5):
+    def measure(self, fn, seconds=3.0, per_call_s=1e-5):
         """Runs fn back to back for about `seconds` while sampling every 10 ms; returns the
         median of the readings the driver refreshed after the first third of the window
-        (the clock has settled by then), or None."""
+        (the clock has settled by then; a reading still unchanged from before is dropped),
+        or None."""
         import statistics
         import threading
         import torch
@@ -336,12 +337,13 @@ class ClockSampler:
             torch.cuda.synchronize()
         stop[0] = True
         th.join()
+        key = lambda r: (r["ts"], r["gfxclk_mhz"], r["socket_power_w"])
+        early = {key(r) for t, r in samples if t < seconds / 3}
         late = [r for t, r in samples if t >= seconds / 3 and r["gfxclk_mhz"] is not None]
-        fresh, seen = [], set()
-        for r in late:                      # one reading per driver refresh
-            key = (r["ts"], r["gfxclk_mhz"], r["socket_power_w"])
-            if key not in seen:
-                seen.add(key)
+        fresh, seen = [], set(early)
+        for r in late:                      # one reading per driver refresh after settling
+            if key(r) not in seen:
+                seen.add(key(r))
                 fresh.append(r)
         if not fresh:
             return None

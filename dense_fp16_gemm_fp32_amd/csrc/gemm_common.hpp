@@ -83,29 +83,31 @@ __device__ __forceinline__ void tile_coords(int bid, int tiles_m, int tiles_n, i
 }
 
 // ---------------------------------------------------------------- epilogue ----------
-// GELU(x) = x * Phi(x) with Phi the standard normal CDF:
-//   Phi(x) = 1 - erfc(z)/2 for x >= 0 and erfc(z)/2 for x < 0, z = |x| / sqrt 2,
-// one erfc evaluation and no cancellation on the negative side.  erfc(z) for z >= 0 uses
-// the rational approximation of Abramowitz and Stegun, Handbook of Mathematical Functions,
-// formula 7.1.26 (after Hastings): erfc(z) = t (a1 + t (a2 + t (a3 + t (a4 + t a5))))
-// exp(-z^2) with t = 1 / (1 + p z), absolute error at most 1.5e-7.  The polynomial
-// approximates erfc(z) exp(z^2), so the relative error stays of that order in the
-// tail as well, far below the 2^-11 relative step of the fp16 result.  exp and the
-// reciprocal are the hardware v_exp_f32 / v_rcp_f32.
+// GELU(x) = x * Phi(x) with Phi the standard normal CDF.  With h = Phi(-|x|) = erfc(z)/2,
+// z = |x| / sqrt 2, Phi(x) is 1 - h for x >= 0 and h for x < 0, so
+//   GELU(x) = max(x, 0) - |x| h
+// for both signs: one erfc evaluation, no cancellation on the negative side, and no
+// select.  erfc(z) for z >= 0 uses the rational approximation of Abramowitz and Stegun,
+// Handbook of Mathematical Functions, formula 7.1.26 (after Hastings):
+// erfc(z) = t (a1 + t (a2 + t (a3 + t (a4 + t a5)))) exp(-z^2) with t = 1 / (1 + p z),
+// absolute error at most 1.5e-7.  The polynomial approximates erfc(z) exp(z^2), so the
+// relative error stays of that order in the tail as well, far below the 2^-11 relative
+// step of the fp16 result.  exp and the reciprocal are the hardware v_exp_f32 / v_rcp_f32.
 __device__ __forceinline__ float gelu_erf(float x)
 {
-    // erfc(z) ~ t (a1 + a2 t + ... + a5 t^4) exp(-z^2), t = 1 / (1 + p z), z = |x| / sqrt(2);
     // the coefficients below are a1..a5 halved (exact in binary), so the polynomial times
     // exp(-z^2) is h = erfc(z) / 2 = Phi(-|x|) directly, and p is premultiplied by 1/sqrt(2).
     constexpr float p = 0.3275911f * 0.70710678118654752f;
     constexpr float a1 = 0.5f * 0.254829592f, a2 = 0.5f * -0.284496736f, a3 = 0.5f * 1.421413741f,
                     a4 = 0.5f * -1.453152027f, a5 = 0.5f * 1.061405429f;
     constexpr float kHalfLog2e = 0.72134752044448170f;   // log2(e) / 2: exp(-z^2) = 2^(-x^2 log2(e) / 2)
-    const float t = __builtin_amdgcn_rcpf(fmaf(p, fabsf(x), 1.0f));
+    // |x| clamped to the largest finite float: for x = +inf the last step then gives
+    // inf - 3.4e38 * 0 = inf (unclamped it would be inf * 0 = NaN); finite x are unchanged
+    const float ax = fminf(fabsf(x), 3.4028234663852886e38f);
+    const float t = __builtin_amdgcn_rcpf(fmaf(p, ax, 1.0f));
     const float poly = t * fmaf(t, fmaf(t, fmaf(t, fmaf(t, a5, a4), a3), a2), a1);
     const float h = poly * __builtin_amdgcn_exp2f(-(x * x) * kHalfLog2e);   // Phi(-|x|)
-    // Phi(x) = 1 - Phi(-x) for x >= 0; for x < 0 it is h itself, with no cancellation
-    return x * ((x >= 0.0f) ? 1.0f - h : h);
+    return fmaf(-ax, h, fmaxf(x, 0.0f));
 }
 
 template <int EPI>

@@ -39,11 +39,15 @@
 
 namespace mi355 {
 
-template <int BM_, int BN_, int BK_, int WAVES_M_, int WAVES_N_, int KGROUPS_, int STAGES_>
+// PF: k-steps the LDS fragment reads run ahead of the MFMAs that consume them (1: the next
+// k-step's fragments are read during the current one, 2 fragment buffers; 2 or 3: 4
+// buffers, so each read has one or two whole k-steps of MFMAs to complete in).
+template <int BM_, int BN_, int BK_, int WAVES_M_, int WAVES_N_, int KGROUPS_, int STAGES_,
+          int PF_ = 1>
 struct DTile {
     static constexpr int BM = BM_, BN = BN_, BK = BK_;
     static constexpr int WAVES_M = WAVES_M_, WAVES_N = WAVES_N_;
-    static constexpr int KGROUPS = KGROUPS_, STAGES = STAGES_;
+    static constexpr int KGROUPS = KGROUPS_, STAGES = STAGES_, PF = PF_;
     static constexpr int NWC = WAVES_M * WAVES_N;    // waves of one k-group
     static constexpr int NW = NWC * KGROUPS;
     static constexpr int NT = 64 * NW;
@@ -60,24 +64,31 @@ struct DTile {
     static constexpr int GA = A_BYTES / (1024 * NW);   // 1 KiB LDS-DMA loads per wave
     static constexpr int GB = B_BYTES / (1024 * NW);
     static constexpr int G = GA + GB;
-    // Copies of a stage issued in its first k-step, before the end-of-stage wait: all of
-    // them with a ring of 2 stages (the next stage's copy must land before that wait) or
-    // one k-step per stage; else half, and the rest after the barrier.  VM_WAIT: the
-    // copies younger than the next stage's when the wait is reached.
-    static constexpr int G_EARLY = (STAGES >= 3 && KK / KGROUPS >= 2) ? G / 2 : G;
-    static constexpr int VM_WAIT = G * (STAGES - 3) + G_EARLY;
+    static constexpr int NBUF = PF == 1 ? 2 : 4;      // fragment buffers
+    // k-step of a stage that waits for the next stage's copy and crosses the barrier: from
+    // there on the reads run into the next stage
+    static constexpr int QB = Q - PF;
+    // Copies of a stage issued in its first k-step: all of them with a ring of 2 stages
+    // (the next stage's copy must land before the end-of-stage wait) or one k-step per
+    // stage; else half, and the rest after the barrier.  VM_WAIT: the copies younger than
+    // the next stage's when the wait is reached (the first k-step's copies come after the
+    // barrier when the barrier is in that k-step, QB == 0, with more than one k-step).
+    static constexpr int G_EARLY = (STAGES >= 3 && Q >= 2) ? G / 2 : G;
+    static constexpr int VM_WAIT = G * (STAGES - 3) + ((QB > 0 || Q == 1) ? G_EARLY : 0);
     static constexpr int LDS_BYTES = STAGES * STAGE_BYTES;
     // k-group exchange at the end: every wave hands half of its 32x32 fp32 blocks (4 KiB
     // each) to its partner in the other group
     static constexpr int RED_BYTES = KGROUPS > 1 ? NW * (NMFMA / 2) * 4096 : 0;
     static_assert(WTM % 32 == 0 && WTN % 32 == 0, "wave tile must be whole 32x32 blocks");
     static_assert(BK == 32 || BK == 64, "A swizzle assumes 4 or 8 chunks per row");
-    static_assert(CB >= 16, "B swizzle assumes rows of at least 256 bytes");
+    static_assert(CB % 16 == 0, "B swizzle assumes rows of a multiple of 256 bytes");
     static_assert(A_BYTES % (1024 * NW) == 0 && B_BYTES % (1024 * NW) == 0,
                   "stage must split into whole 1 KiB loads per wave");
     static_assert(KGROUPS == 1 || (KGROUPS == 2 && FM % 2 == 0), "k-groups: 1, or 2 with even FM");
     static_assert(KK % KGROUPS == 0, "k-steps must split evenly over the k-groups");
-    static_assert((STAGES * Q) % 2 == 0, "fragment double-buffer parity must repeat per ring turn");
+    static_assert(PF >= 1 && PF <= Q && PF <= 3, "reads run at most one stage and 3 k-steps ahead");
+    static_assert(PF == 1 || STAGES >= 3, "prefetch beyond one k-step needs a ring of 3 or more");
+    static_assert((STAGES * Q) % NBUF == 0, "fragment buffer cycle must repeat per ring turn");
     static_assert(STAGES >= 2 && STAGES <= 8 && G * (STAGES - 2) <= 63, "ring size / vmcnt range");
     static_assert(VM_WAIT >= 0 && VM_WAIT <= 63, "vmcnt range");
     static_assert(LDS_BYTES <= 160 * 1024, "over the gfx950 LDS budget");
@@ -180,8 +191,8 @@ struct DirectWave {
     uint32_t tail_mask;       // bit g: piece g of the last stage straddles K
     u32x2 bias_raw[T::FN][4]; // bias of this lane's accumulator columns (bias epilogues)
     f32x16 acc[T::FM][T::FN];
-    f16x8 af[2][T::FM];
-    s16x4 bl[2][T::FN], bh[2][T::FN];
+    f16x8 af[T::NBUF][T::FM];
+    s16x4 bl[T::NBUF][T::FN], bh[T::NBUF][T::FN];
 
     __device__ __forceinline__ void init(const GemmArgs &p, int m0, int n0_, int rows_valid,
                                          int cols_valid)
@@ -388,11 +399,14 @@ struct DirectWave {
 // stores to HBM are whole rows: 16 bytes per lane, consecutive lanes on consecutive
 // columns, every 128-byte line written by one instruction.  LDS layout: row-major
 // BM x BN fp16, 16-byte chunk c of row r stored at chunk c ^ (r % CW) (CW = chunks per
-// row), so the column-wise writes from the accumulator layout spread over the banks.
+// row, a power of two), so the column-wise writes from the accumulator layout spread over
+// the banks.
 template <class T>
-__device__ __forceinline__ int c_chunk_swz(int r)
+__device__ __forceinline__ int c_phys(int c, int r)
 {
-    return r % (T::BN / 8);
+    constexpr int CW = T::BN / 8;
+    static_assert((CW & (CW - 1)) == 0, "C tile rows of a power-of-two number of chunks");
+    return c ^ (r % CW);
 }
 
 // Bias, GELU and fp16 rounding of accumulator block rows I0 <= i < I1 of this wave,
@@ -428,12 +442,19 @@ __device__ __forceinline__ void tile_to_lds(const f32x16 (&acc)[T::FM][T::FN],
                     const f16 h = (f16)epilogue_op<EPI>(acc[i][j][4 * g + e], bv[e]);
                     hb[e] = __builtin_bit_cast(uint16_t, h);
                 }
-                char *dst = ctile + (r * T::BN + 8 * (c ^ c_chunk_swz<T>(r)) + 4 * half) * 2;
+                char *dst = ctile + (r * T::BN + 8 * c_phys<T>(c, r) + 4 * half) * 2;
                 *reinterpret_cast<u32x2 *>(dst) = u32x2{hb[0] | (hb[1] << 16), hb[2] | (hb[3] << 16)};
             }
         }
     }
 }
+
+// Cache policy of the C stores: sc0 | sc1 (system scope), so the lines are written through
+// L2 as the epilogue produces them instead of staying dirty until the write-back at the
+// end of the kernel.  Measured on MI355X: 1000x3000x777 + bias + GELU 11.76 us against
+// 12.38 us with the default policy, 2048^3 + bias + GELU 20.42 against 20.62, 2048^3 and
+// 8192^3 unchanged (interleaved on one box); the non-temporal hint alone did not help.
+constexpr int kStoreWriteThrough = 1 | 16;
 
 // All threads: copy the LDS tile to C, 16 bytes per lane.  Rows past M fall outside the
 // C descriptor's range, 8-column chunks past N are pushed out of range (N % 8 == 0 here,
@@ -452,9 +473,9 @@ __device__ __forceinline__ void lds_to_c(const GemmArgs &p, int m0, int n0, int 
     for (int k = 0; k < PER; ++k) {
         const int q = threadIdx.x + k * T::NT;
         const int r = q / CW, c = q % CW;
-        const u32x4 v = *reinterpret_cast<const u32x4 *>(ctile + (r * T::BN + 8 * (c ^ c_chunk_swz<T>(r))) * 2);
+        const u32x4 v = *reinterpret_cast<const u32x4 *>(ctile + (r * T::BN + 8 * c_phys<T>(c, r)) * 2);
         const uint32_t off = masked_offset((uint32_t)(r * p.ldc + 8 * c) * 2u, 8 * c < cols_valid);
-        __builtin_amdgcn_raw_buffer_store_b128(v, c_rs, off, 0, 0);
+        __builtin_amdgcn_raw_buffer_store_b128(v, c_rs, off, 0, kStoreWriteThrough);
     }
 }
 
@@ -493,11 +514,11 @@ __global__ void __launch_bounds__(T::NT) gemm_direct(GemmArgs p)
 
     // One stage J of a ring turn (stage kt).  The wave runs its Q k-steps; each k-step
     // issues its MFMAs one by one, and after each MFMA a share of the LDS reads for the
-    // wave's next k-step and, in the first k-step, a share of the HBM -> LDS copy of stage
-    // kt+STAGES-1 into the slot freed by stage kt-1.  The last k-step first waits for
-    // stage kt+1's copy and crosses the barrier, then reads the next stage's fragments
-    // while its MFMAs run.  The body has no branches on data; near the end of K it copies
-    // zeros for the stages past the end and reads fragments it never uses.
+    // k-step PF ahead and, in the first k-step, a share of the HBM -> LDS copy of stage
+    // kt+STAGES-1 into the slot freed by stage kt-1.  k-step QB first waits for stage
+    // kt+1's copy and crosses the barrier: from there on the reads run into stage kt+1, and
+    // the rest of the copies follow.  The body has no branches on data; near the end of K
+    // it copies zeros for the stages past the end and reads fragments it never uses.
     auto stage = [&](auto Jc, int kt, auto full_c) {
         constexpr int J = decltype(Jc)::value;
         constexpr bool FULL = decltype(full_c)::value;   // the stage copied here is below K
@@ -506,15 +527,17 @@ __global__ void __launch_bounds__(T::NT) gemm_direct(GemmArgs p)
         St &dst = ring[(J + T::STAGES - 1) % T::STAGES];
         static_for<T::Q>([&](auto qc) {
             constexpr int q = decltype(qc)::value;
-            constexpr int buf = (J * T::Q + q) & 1;
-            constexpr bool last = (q == T::Q - 1);
+            constexpr int buf = (J * T::Q + q) % T::NBUF;
+            constexpr int rbuf = (J * T::Q + q + T::PF) % T::NBUF;   // buffer the reads fill
+            constexpr bool ahead = q + T::PF >= T::Q;                // reads from stage kt+1
+            constexpr int rq = (q + T::PF) % T::Q;                   // their k-step there
             if constexpr (T::Q == 1) {
                 w.template issue_stage<FULL>(dst, kt + T::STAGES - 1);
             }
-            if constexpr (last) {
+            if constexpr (q == T::QB) {
                 // stage kt+1 has landed once at most the copies issued after it are in
                 // flight (stages kt+2 .. kt+STAGES-2 and the early part of kt+STAGES-1);
-                // this wave's reads of stage kt were issued before the barrier
+                // this wave's reads of stage kt-1 were issued before the barrier
                 wait_counts<T::VM_WAIT, 15>();
                 if (k_tail && kt + 1 == nk - 1) w.patch_tail(nxt);
                 workgroup_barrier();
@@ -526,10 +549,10 @@ __global__ void __launch_bounds__(T::NT) gemm_direct(GemmArgs p)
                 constexpr int r1 = (m + 1) * T::NREAD / T::NMFMA;
 #pragma unroll
                 for (int r = r0; r < r1; ++r) {
-                    if constexpr (last)
-                        w.read_one(nxt, 0, buf ^ 1, r);
+                    if constexpr (ahead)
+                        w.read_one(nxt, rq, rbuf, r);
                     else
-                        w.read_one(cur, q + 1, buf ^ 1, r);
+                        w.read_one(cur, rq, rbuf, r);
                 }
                 if constexpr (q == 0 && T::Q > 1) {
                     constexpr int g0 = m * T::G_EARLY / T::NMFMA;
@@ -537,9 +560,9 @@ __global__ void __launch_bounds__(T::NT) gemm_direct(GemmArgs p)
 #pragma unroll
                     for (int g = g0; g < g1; ++g) w.template issue_piece<FULL>(dst, kt + T::STAGES - 1, g);
                 }
-                if constexpr (last && T::Q > 1 && T::G_EARLY < T::G) {
+                if constexpr (q == T::QB && T::Q > 1 && T::G_EARLY < T::G) {
                     // the rest after the barrier: slot dst held stage kt-1, which no wave
-                    // has read since the previous barrier
+                    // has read since the barrier of stage kt-1
                     constexpr int g0 = T::G_EARLY + m * (T::G - T::G_EARLY) / T::NMFMA;
                     constexpr int g1 = T::G_EARLY + (m + 1) * (T::G - T::G_EARLY) / T::NMFMA;
 #pragma unroll
@@ -557,7 +580,10 @@ __global__ void __launch_bounds__(T::NT) gemm_direct(GemmArgs p)
         wait_counts<T::G * (T::STAGES - 2), 15>();
         if (k_tail && nk == 1) w.patch_tail(ring[0]);
         workgroup_barrier();
-        w.read_all(ring[0], 0, 0);
+        static_for<T::PF>([&](auto qc) {   // the first PF k-steps of stage 0
+            constexpr int q = decltype(qc)::value;
+            w.read_all(ring[0], q, q);
+        });
 
         // ---- main loop, unrolled over the ring so every slot address is a constant.
         // The last ring turn stops at the end of K (a branch on a workgroup-uniform

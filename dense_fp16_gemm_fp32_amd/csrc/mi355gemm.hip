@@ -18,6 +18,7 @@
 #include "attention.hpp"
 #include "gemm_direct.hpp"
 #include "gemm_narrow.hpp"
+#include "gemm_pingpong.hpp"
 #include "gemm_staged.hpp"
 #include "softmax.hpp"
 #include "vector_add.hpp"
@@ -31,6 +32,8 @@ using D128 = DTile<128, 128, 64, 2, 2, 2, 4>;       // 2 x 4 waves of 64x64, 128
 using D128w4 = DTile<128, 128, 64, 2, 2, 1, 4>;     // 4 waves of 64x64, 128 KiB
 using D256w4 = DTile<256, 256, 32, 2, 2, 1, 4>;     // 4 waves of 128x128, 128 KiB
 using D128k32 = DTile<128, 128, 32, 2, 2, 1, 4>;    // 4 waves of 64x64, 64 KiB
+// ping-pong tile: BM, BN, BK, waves of a group (M x N), stages
+using P256 = PTile<256, 256, 32, 1, 4, 4>;          // 2 groups x 4 waves of 128x64, 128 KiB
 // attention: head dim, keys per block, waves (32 query rows each), LDS stages
 using A128 = ATile<128, 128, 8, 2>;  // 256 query rows, 128-key blocks, 128 KiB LDS
 using A64 = ATile<64, 64, 8, 3>;     // 256 query rows, 64-key blocks, 48 KiB LDS
@@ -56,6 +59,12 @@ MI355_DIRECT(D128w4)
 MI355_DIRECT(D256w4)
 MI355_DIRECT(D128k32)
 #undef MI355_DIRECT
+#define MI355_PINGPONG(T)                                     \
+    template __global__ void gemm_pingpong<T, 0>(GemmArgs);   \
+    template __global__ void gemm_pingpong<T, 1>(GemmArgs);   \
+    template __global__ void gemm_pingpong<T, 2>(GemmArgs);
+MI355_PINGPONG(P256)
+#undef MI355_PINGPONG
 #define MI355_NARROW(KS)                                   \
     template __global__ void gemm_narrow<0, KS>(GemmArgs); \
     template __global__ void gemm_narrow<1, KS>(GemmArgs); \
@@ -90,6 +99,8 @@ struct Config {
     int group_m;
     KernelFn fn[2][3];   // [K % 8 != 0][epilogue]
     bool narrow;      // vector-ALU kernel for at most bn (8) columns
+    bool k_mult8;     // needs K % 8 == 0 (no kernel for the K-tail case)
+    bool pingpong;    // two wave groups taking turns
 };
 
 template <class T, bool AV, bool BV>
@@ -99,7 +110,7 @@ Config staged_config(const char *name, int group_m)
                   T::LDS_BYTES, AV, BV, group_m,
                   {{gemm_staged<T, AV, BV, 0>, gemm_staged<T, AV, BV, 1>, gemm_staged<T, AV, BV, 2>},
                    {gemm_staged<T, AV, BV, 0>, gemm_staged<T, AV, BV, 1>, gemm_staged<T, AV, BV, 2>}},
-                  false};
+                  false, false, false};
 }
 
 template <class T>
@@ -110,7 +121,18 @@ Config direct_config(const char *name, int group_m)
                   T::LDS_BYTES, false, true, group_m,
                   {{gemm_direct<T, 0, false>, gemm_direct<T, 1, false>, gemm_direct<T, 2, false>},
                    {gemm_direct<T, 0, true>, gemm_direct<T, 1, true>, gemm_direct<T, 2, true>}},
-                  false};
+                  false, false, false};
+}
+
+// Two groups of four waves taking turns; K % 8 == 0 only (no K-tail patch)
+template <class T>
+Config pingpong_config(const char *name, int group_m)
+{
+    return Config{name, true, T::BM, T::BN, T::BK, T::STAGES, 2 * T::WM, T::WN, 1,
+                  T::NT, T::LDS_BYTES, false, true, group_m,
+                  {{gemm_pingpong<T, 0>, gemm_pingpong<T, 1>, gemm_pingpong<T, 2>},
+                   {nullptr, nullptr, nullptr}},
+                  false, true, true};
 }
 
 // Up to 8 columns; 4 waves per workgroup, KS of them splitting K for each 8-row group
@@ -122,7 +144,7 @@ Config narrow_config(const char *name)
                   KS > 1 ? (int)(T::NW * 64 * sizeof(float)) : 0, false, false, 1,
                   {{gemm_narrow<0, KS>, gemm_narrow<1, KS>, gemm_narrow<2, KS>},
                    {gemm_narrow<0, KS>, gemm_narrow<1, KS>, gemm_narrow<2, KS>}},
-                  true};
+                  true, false, false};
 }
 
 const Config kConfigs[] = {
@@ -133,6 +155,7 @@ const Config kConfigs[] = {
     direct_config<D128w4>("d128x128x64_w2x2_s4", 8),
     direct_config<D256w4>("d256x256x32_w2x2_s4", 4),
     direct_config<D128k32>("d128x128x32_w2x2_s4", 8),
+    pingpong_config<P256>("p256x256x32_w2x4_s4", 4),
     staged_config<T256, true, true>("s256x256x64_w2x2_av_bv", 8),
     staged_config<T128, true, true>("s128x128x64_w2x2_av_bv", 8),
     staged_config<T128, true, false>("s128x128x64_w2x2_av_bn", 8),
@@ -221,11 +244,18 @@ int find_staged(int bm, int bn, bool av, bool bv)
     return -1;
 }
 
+int find_pingpong(int bm, int bn)
+{
+    for (int i = 0; i < kNumConfigs; ++i)
+        if (kConfigs[i].pingpong && kConfigs[i].bm == bm && kConfigs[i].bn == bn) return i;
+    return -1;
+}
+
 int find_direct(int bm, int bn, int bk, int waves, int k_groups)
 {
     for (int i = 0; i < kNumConfigs; ++i) {
         const Config &c = kConfigs[i];
-        if (c.direct && c.bm == bm && c.bn == bn && c.bk == bk &&
+        if (c.direct && !c.pingpong && c.bm == bm && c.bn == bn && c.bk == bk &&
             c.waves_m * c.waves_n * c.k_groups == waves && c.k_groups == k_groups)
             return i;
     }
@@ -236,7 +266,7 @@ int find_direct(int bm, int bn, int bk, int waves, int k_groups)
 bool config_fits(const Config &c, const Request &r)
 {
     return c.lds_bytes <= kLdsBudget && (!c.a_vec || a_vector_ok(r)) && (!c.bc_vec || bc_vector_ok(r)) &&
-           (!c.narrow || r.N <= c.bn);
+           (!c.narrow || r.N <= c.bn) && (!c.k_mult8 || r.K % 8 == 0);
 }
 
 // Measured winners for exact shapes, written by the package's tune.py (an interleaved
@@ -268,8 +298,11 @@ int tuned_choice(const Request &r, bool av, bool bv)
 // Shape-keyed choice (host only), from interleaved timings of the candidates on several
 // MI355X boxes.  A launch should cover the 256 compute units; among the tiles that do,
 // the largest wins (fewer bytes per flop from L2 into LDS).  With every CU busy the part
-// runs at its power limit: 256x256x32 tiles on 4 waves of 128x128 from four full waves
-// of them, 256x256x64 tiles (8 waves, 2 stages) from one, else 256x128 tiles with two
+// runs at its power limit.  From one full wave of 256x256 tiles on, the ping-pong kernel
+// (two groups of 4 waves taking turns) leads the other 256x256 tiles by 0-1.5% (8192^3
+// with and without bias + GELU, 4096^3); it needs K % 8 == 0.  Otherwise: 256x256x32
+// tiles on 4 waves of 128x128 from four full waves of them, 256x256x64 tiles (8 waves, 2
+// stages) from one, else 256x128 tiles with two
 // k-groups when they fill the chip, else 128x128 tiles: 4 waves when they fill the chip
 // with K below 4096, two k-groups for long K or with part of the chip idle (two waves per
 // SIMD hide each other's LDS reads and barrier waits).  The 4-wave tiles took over
@@ -323,6 +356,9 @@ int choose(const Request &r)
     if (bv || r.N >= 64) {
         // measured with the interleaved tuner on MI355X (the table file records the runs)
         const int64_t t256 = tiles(r, 256, 256), t256x128 = tiles(r, 256, 128), t128 = tiles(r, 128, 128);
+        // one wave of 256x256 tiles or more: the ping-pong kernel when K % 8 == 0 and the
+        // rows of B and C are 16-byte friendly (no split launch)
+        if (bv && t256 >= kCUs && r.K % 8 == 0) return find_pingpong(256, 256);
         if (t256 >= 4 * kCUs) return find_direct(256, 256, 32, 4, 1);   // several waves of big tiles
         if (t256 >= kCUs) return find_direct(256, 256, 64, 8, 1);        // about one wave of them
         if (t256x128 >= kCUs) return find_direct(256, 128, 64, 8, 2);    // e.g. one GPU's share of 8192^3
@@ -355,6 +391,9 @@ mi355gemm_status check_config(const Config &c, const Request &r)
     if (c.narrow && r.N > c.bn)
         return fail(MI355GEMM_EUNSUPPORTED, "config %s computes at most %d columns (N=%lld)", c.name,
                     c.bn, (long long)r.N);
+    if (c.k_mult8 && r.K % 8 != 0)
+        return fail(MI355GEMM_EUNSUPPORTED, "config %s needs K %% 8 == 0 (K=%lld)", c.name,
+                    (long long)r.K);
     return MI355GEMM_OK;
 }
 
@@ -381,6 +420,8 @@ mi355gemm_status launch(const Config &c, const Request &r, int64_t n_begin, int6
     if (grid >= ((int64_t)1 << 31))
         return fail(MI355GEMM_EUNSUPPORTED, "too many tiles (%lld)", (long long)grid);
     const KernelFn fn = c.fn[(r.K & 7) != 0][r.epi];
+    if (fn == nullptr)
+        return fail(MI355GEMM_EUNSUPPORTED, "config %s has no kernel for K %% 8 != 0", c.name);
     if (ev_start != nullptr || ev_stop != nullptr)
         hipExtLaunchKernelGGL(fn, dim3((unsigned)grid), dim3(c.threads), 0, stream, ev_start,
                               ev_stop, 0, a);
@@ -592,7 +633,8 @@ mi355gemm_status mi355gemm_set_choice(int64_t M, int64_t N, int64_t K, int epi, 
     if (config_id < 0 || config_id >= kNumConfigs)
         return fail(MI355GEMM_EINVAL, "unknown config id %d", config_id);
     const Config &c = kConfigs[config_id];
-    if ((c.a_vec && !a_vector) || (c.bc_vec && !bc_vector) || (c.narrow && N > c.bn))
+    if ((c.a_vec && !a_vector) || (c.bc_vec && !bc_vector) || (c.narrow && N > c.bn) ||
+        (c.k_mult8 && K % 8 != 0))
         return fail(MI355GEMM_EUNSUPPORTED, "config %s cannot serve this alignment class or N",
                     c.name);
     std::lock_guard<std::mutex> lock(g_choices_mu);
@@ -646,6 +688,8 @@ mi355gemm_status mi355gemm_config_info(int config_id, mi355gemm_config_desc *out
     out->group_m = c.group_m;
     out->direct = c.direct;
     out->narrow = c.narrow;
+    out->k_mult8 = c.k_mult8;
+    out->pingpong = c.pingpong;
     return MI355GEMM_OK;
 }
 

@@ -149,7 +149,8 @@ def tune(shapes, rounds=7, margin=0.03, log=print, ms=20.0):
 
 def calibration_candidates(a, b, bias=None, epilogue="none", out=None):
     """The configurations ``calibrate`` may time and install for this call: the direct
-    configurations with the selector's tile size (block_m x block_n), or the selector's
+    configurations with the selector's tile size (block_m x block_n) that serve its K
+    (the ping-pong ones need K % 8 == 0), or the selector's
     choice alone when it is not a direct kernel or when B and C rows are not 16-byte
     friendly (the library then splits the launch into a direct part and a narrow strip,
     which a forced configuration cannot do).  Returns (rule name, [candidate names])."""
@@ -172,7 +173,8 @@ def calibration_candidates(a, b, bias=None, epilogue="none", out=None):
     if not info["direct"] or not bv:
         return rule_name, [rule_name]
     return rule_name, [c["name"] for c in g.configs()
-                       if c["direct"] and c["block_m"] == info["block_m"] and c["block_n"] == info["block_n"]]
+                       if c["direct"] and c["block_m"] == info["block_m"] and c["block_n"] == info["block_n"]
+                       and not (c["k_mult8"] and K % 8)]
 
 
 def agrees(got, ref, rel_fro=5e-3, elem=1e-2) -> bool:

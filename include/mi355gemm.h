@@ -240,23 +240,34 @@ typedef struct {
     int narrow;                     /* 1: vector-ALU kernel for at most block_n (8) columns:
                                        block_m rows per workgroup, k_groups waves on
                                        interleaved block_k-wide k-blocks, no LDS tiles */
+    int k_mult8;                    /* 1: needs K % 8 == 0 (A at any 2-byte alignment) */
+    int pingpong;                   /* 1: two groups of four waves take turns, one
+                                       multiplying while the other loads its next operands
+                                       (k_groups 2: the groups take alternate K stages and
+                                       sum at the end; 1: each group owns half the rows) */
 } mi355gemm_config_desc;
 
 /* Number of compiled configurations (ids 0 .. n-1). Host-only. */
 int mi355gemm_num_configs(void);
 
 /* Static name of a configuration, or NULL for an unknown id.  Host-only.  Names read
- * <d|s|n><BM>x<BN>x<BK>_w<waves_m>x<waves_n>[k<k_groups>]_...: d = direct HBM -> LDS kernel
- * (suffix s<stages>), s = register-staged kernel (suffix av/an: A in 16-byte / 2-byte
- * loads, bv/bn: B and C likewise), n = narrow vector-ALU kernel for N <= 8 (any
- * alignment), e.g. "d128x128x64_w2x2_s4", "s64x64x64_w2x1_av_bv", "n8x8x512_w1x1k4". */
+ * <d|p|s|n><BM>x<BN>x<BK>_w<waves_m>x<waves_n>[k<k_groups>]_...: d = direct HBM -> LDS kernel
+ * (suffix s<stages>), p = the same loader and tiles with two wave groups taking turns
+ * (ping-pong; suffix s<stages>), s = register-staged kernel (suffix av/an: A in 16-byte /
+ * 2-byte loads, bv/bn: B and C likewise), n = narrow vector-ALU kernel for N <= 8 (any
+ * alignment), e.g. "d128x128x64_w2x2_s4", "p256x256x32_w2x4_s4", "s64x64x64_w2x1_av_bv",
+ * "n8x8x512_w1x1k4".  The tag mirrors the candidate tag of the tutorial's schedule sweep
+ * (thecryptopost.io page, section 3: block_M x block_N x block_K with stages and threads). */
 const char *mi355gemm_config_name(int config_id);
 
 /* Fill *out for config_id; EINVAL for an unknown id or NULL out. Host-only. */
 mi355gemm_status mi355gemm_config_info(int config_id, mi355gemm_config_desc *out);
 
 /* LDS bytes one workgroup may use on gfx950 (the budget every configuration is checked
- * against; 160 KiB). Host-only. */
+ * against; 160 KiB). Host-only.  The counterpart of the tutorial's shared-memory budget
+ * check, which skips schedules whose (block_M*block_K + block_K*block_N) * 2 * stages bytes
+ * exceed the device's capacity (thecryptopost.io page, sections 2 and 3, smem_bytes and
+ * SMEM_CAP). */
 int mi355gemm_lds_budget(void);
 
 /* Message for the last non-OK status returned on this thread ("" if none). The string

@@ -77,6 +77,10 @@ def test_config_table_is_consistent():
         assert c["k_groups"] in (1, 2) and (c["direct"] or c["k_groups"] == 1)
         assert c["block_m"] % (32 * c["waves_m"]) == 0 and c["block_n"] % (32 * c["waves_n"]) == 0
         assert c["block_k"] % 16 == 0
+        # ping-pong: the direct loader with two groups of 4 waves, K % 8 == 0 only
+        assert c["k_mult8"] == c["pingpong"]
+        if c["pingpong"]:
+            assert c["direct"] == 1 and c["threads"] == 512 and c["name"].startswith("p")
     assert g.mi355gemm_config_name(-1) is None
     assert g.mi355gemm_config_name(len(cfgs)) is None
     with pytest.raises(g.GemmError):
@@ -322,11 +326,13 @@ def test_attention_argument_checks(args, want):
 
 
 @pytest.mark.parametrize("shape,want", [
-    ((8192, 8192, 8192), "d256x256x32_w2x2_s4"),      # four waves of 256 x 256 tiles
-    ((16384, 8192, 4096), "d256x256x32_w2x2_s4"),
-    ((4096, 4096, 4096), "d256x256x64_w2x4_s2"),      # one wave of them
-    ((16384, 2048, 1024), "d256x256x64_w2x4_s2"),
-    ((2048, 8192, 4096), "d256x256x64_w2x4_s2"),
+    ((8192, 8192, 8192), "p256x256x32_w2x4_s4"),      # four waves of 256 x 256 tiles: ping-pong
+    ((16384, 8192, 4096), "p256x256x32_w2x4_s4"),
+    ((4096, 4096, 4096), "p256x256x32_w2x4_s4"),      # one wave of them
+    ((16384, 2048, 1024), "p256x256x32_w2x4_s4"),
+    ((2048, 8192, 4096), "p256x256x32_w2x4_s4"),
+    ((8192, 8192, 8190), "d256x256x32_w2x2_s4"),      # K % 8 != 0: no ping-pong kernel
+    ((4096, 4096, 4095), "d256x256x64_w2x4_s2"),
     ((8192, 1024, 8192), "d256x128x64_w2x2k2_s3"),    # one GPU's N share of 8192^3
     ((1024, 8192, 8192), "d256x128x64_w2x2k2_s3"),    # its M share
     ((2048, 2048, 8192), "d128x128x64_w2x2k2_s4"),    # 256 tiles, long K

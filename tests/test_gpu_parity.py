@@ -40,6 +40,8 @@ def _compatible(cfg, M, N, K):
         return False
     if cfg["bc_vector"] and N % 8:
         return False
+    if cfg["k_mult8"] and K % 8:
+        return False
     return True
 
 
@@ -316,9 +318,13 @@ def test_direct_kernel_full_turn_boundary_bitexact():
     for cfg in all_configs():
         if not cfg["direct"]:
             continue
-        kb = (2 * cfg["stages"] - 1) * cfg["block_k"]
+        # the row-split ping-pong kernel copies one stage further ahead per turn
+        rows_pp = cfg["pingpong"] and cfg["k_groups"] == 1
+        kb = (2 * cfg["stages"] - (0 if rows_pp else 1)) * cfg["block_k"]
         M, N = cfg["block_m"] + 3, cfg["block_n"] + 8
         for K in (kb - 8, kb, kb + 3, kb + 8, kb + cfg["stages"] * cfg["block_k"]):
+            if cfg["k_mult8"] and K % 8:
+                continue
             print("turn boundary", cfg["name"], (M, N, K), flush=True)
             A, B = _small_int_inputs(M, N, K)
             C = _run(A, B, None, "none", config=cfg["id"])
@@ -362,19 +368,21 @@ def test_gelu_epilogue_every_finite_fp16_input():
 # ---- the direct kernel on A with any alignment and any K --------------------------------
 
 @pytest.mark.parametrize("shape", [(300, 264, 777), (1000, 3000, 777), (130, 136, 9), (64, 128, 5),
-                                   (257, 384, 1027), (128, 128, 65)],
+                                   (257, 384, 1027), (128, 128, 65), (300, 264, 776),
+                                   (1000, 3000, 784), (257, 520, 8), (600, 768, 1032)],
                          ids=lambda s: "%dx%dx%d" % s)
 def test_direct_kernel_k_tail_and_misaligned_a(shape):
     """K % 8 != 0 (the chunk of each A row that holds K is patched in LDS) and an A that is
-    only 2-byte aligned, on every direct configuration, against the oracle; C sits between
-    NaN guard bands."""
+    only 2-byte aligned, on every direct configuration that serves the K (the ping-pong
+    ones need K % 8 == 0: the shapes with such K run them too), against the oracle; C sits
+    between NaN guard bands."""
     M, N, K = shape
     A, B, bias = workloads.make_inputs(M, N, K, "uniform", with_bias=True, seed=K)
     refs = {e: oracle.gemm(A, B, bias, e) for e in ("none", "bias_gelu")}
     Ab = torch.zeros(M * K + 1, dtype=torch.float16, device=DEV)
     Ab[1:] = A.reshape(-1).to(DEV)
     for cfg in all_configs():
-        if not cfg["direct"]:
+        if not cfg["direct"] or (cfg["k_mult8"] and K % 8):
             continue
         for a_dev, how in ((A.to(DEV), "aligned"), (Ab[1:].view(M, K), "A+2 bytes")):
             for e in ("none", "bias_gelu"):
