@@ -91,6 +91,9 @@ def parse(argv=None):
                          "have passed (0: exactly --warmup calls)")
     ap.add_argument("--workload", default=HEADLINE)
     ap.add_argument("--epilogue", default=None, help="override the workload's epilogue")
+    ap.add_argument("--dist", default=None,
+                    help="override the headline workload's operand distribution (e.g. zeros, to "
+                         "show what the operand values cost under the power limit)")
     ap.add_argument("--config", default=None, help="force a kernel configuration by name")
     ap.add_argument("--no-calibrate", dest="calibrate", action="store_false",
                     help="time the selector's own choice; by default each GEMM workload first "
@@ -268,6 +271,10 @@ def run_cold(lib, w, steps, min_warm_ms=MIN_WARMUP_MS, min_bytes=256 << 20):
             "tflops": w.flops / (mean * 1e-3) / 1e12}
 
 
+RESIDENCY_KEYS = ("accumulation_counter", "ppt_residency_acc", "socket_thm_residency_acc",
+                  "vr_thm_residency_acc", "hbm_thm_residency_acc", "prochot_residency_acc")
+
+
 class ClockSampler:
     """Engine clock and socket power as the driver reports them (amd-smi's GPU metrics:
     current_gfxclks per XCD in MHz, current_socket_power in W, and the power limit),
@@ -301,11 +308,15 @@ class ClockSampler:
             return None
         clks = [c for c in (m.get("current_gfxclks") or []) if isinstance(c, (int, float)) and c > 0]
         power = m.get("current_socket_power")
+        num = lambda v: v if isinstance(v, (int, float)) else None
         return {"ts": m.get("firmware_timestamp") or m.get("system_clock_counter"),
                 "gfxclk_mhz": sum(clks) / len(clks) if clks else None,
                 "gfxclk_mhz_min": min(clks) if clks else None,
                 "gfxclk_mhz_max": max(clks) if clks else None,
-                "socket_power_w": power if isinstance(power, (int, float)) else None}
+                "socket_power_w": num(power),
+                # cumulative counters: time in power-limit (PPT) and thermal throttling,
+                # on the firmware's accumulation time base
+                "acc": {k: num(m.get(k)) for k in RESIDENCY_KEYS}}
 
     def measure(self, fn, seconds=3.0, per_call_s=1e-5):
         """Runs fn back to back for about `seconds` while sampling every 10 ms; returns the
@@ -348,9 +359,22 @@ class ClockSampler:
         if not fresh:
             return None
         med = lambda k: statistics.median(r[k] for r in fresh if r[k] is not None)
+        # fraction of the settled part of the window spent throttled, by cause: the
+        # residency counters' increase over the accumulation counter's
+        residency = None
+        first = next((r for t, r in samples if t >= seconds / 3), None)
+        last = samples[-1][1] if samples else None
+        if first is not None and last is not None:
+            a0, a1 = first["acc"], last["acc"]
+            span = (a1["accumulation_counter"] or 0) - (a0["accumulation_counter"] or 0)
+            if span > 0:
+                residency = {k.replace("_residency_acc", ""): (a1[k] - a0[k]) / span
+                             for k in RESIDENCY_KEYS[1:]
+                             if a0[k] is not None and a1[k] is not None}
         return {"gfxclk_mhz": med("gfxclk_mhz"), "gfxclk_mhz_min": min(r["gfxclk_mhz_min"] for r in fresh),
                 "gfxclk_mhz_max": max(r["gfxclk_mhz_max"] for r in fresh),
                 "socket_power_w": med("socket_power_w"), "power_limit_w": self.power_limit_w,
+                "throttle_residency": residency,
                 "readings": len(fresh), "window_s": seconds}
 
 
@@ -617,6 +641,9 @@ def main():
 
     lib.library()  # fails loudly if the HIP library is not built
     w = workloads.BY_NAME[args.workload]
+    if args.dist:
+        import dataclasses
+        w = dataclasses.replace(w, dist=args.dist)
     epi = args.epilogue or w.epilogues[0]
     print("bench: %s epilogue=%s steps=%d warmup=%d" % (w.name, epi, args.steps, args.warmup),
           file=sys.stderr, flush=True)

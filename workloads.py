@@ -14,6 +14,7 @@ the bias (only when the workload has an epilogue), each in fp32, then cast to fp
 * ``"uniform"``     U(-1, 1)              (``torch.rand * 2 - 1``)
 * ``"normal_rsqrtk"`` N(0, 1) / sqrt(K)   both A and B divided by sqrt(K) in fp32
   before the cast, which keeps |C| near K**-0.5 at large K.
+* ``"zeros"``       all zeros (no draw); only for the benchmark's power measurement.
 
 The bias is always N(0, 1), length N.
 """
@@ -72,6 +73,10 @@ def _draw(shape, dist: str, K: int, gen: torch.Generator) -> torch.Tensor:
         x = torch.rand(shape, generator=gen, dtype=torch.float32) * 2.0 - 1.0
     elif dist == "normal_rsqrtk":
         x = torch.randn(shape, generator=gen, dtype=torch.float32) / math.sqrt(K)
+    elif dist == "zeros":
+        # all-zero operands: the same work with no switching in the multipliers, to show
+        # how much of the clock the operand values cost under the power limit
+        x = torch.zeros(shape, dtype=torch.float32)
     else:
         raise ValueError("unknown distribution %r" % dist)
     return x.to(torch.float16)
