@@ -97,7 +97,7 @@ def parse(argv=None):
     ap.add_argument("--config", default=None, help="force a kernel configuration by name")
     ap.add_argument("--no-calibrate", dest="calibrate", action="store_false",
                     help="time the selector's own choice; by default each GEMM workload first "
-                         "times its tile size's configurations on this device and installs the "
+                         "times the configurations of its tile area on this device and installs the "
                          "fastest (tune.calibrate), since some tiles run up to 25%% slower on "
                          "some MI355X boxes")
     ap.add_argument("--no-cpu-baseline", action="store_true")

@@ -32,6 +32,9 @@ using D128 = DTile<128, 128, 64, 2, 2, 2, 4>;       // 2 x 4 waves of 64x64, 128
 using D128w4 = DTile<128, 128, 64, 2, 2, 1, 4>;     // 4 waves of 64x64, 128 KiB
 using D256w4 = DTile<256, 256, 32, 2, 2, 1, 4>;     // 4 waves of 128x128, 128 KiB
 using D128k32 = DTile<128, 128, 32, 2, 2, 1, 4>;    // 4 waves of 64x64, 64 KiB
+using D128w8 = DTile<128, 128, 64, 2, 4, 1, 4>;     // 8 waves of 64x32, 128 KiB
+using D64x256 = DTile<64, 256, 32, 1, 4, 1, 4>;     // 4 waves of 64x64, 80 KiB
+using D64x128 = DTile<64, 128, 32, 1, 4, 1, 4>;     // 4 waves of 64x32, 40 KiB
 // ping-pong tile: BM, BN, BK, waves of a group (M x N), stages
 using P256 = PTile<256, 256, 32, 1, 4, 4>;          // 2 groups x 4 waves of 128x64, 128 KiB
 // attention: head dim, keys per block, waves (32 query rows each), LDS stages
@@ -58,6 +61,9 @@ MI355_DIRECT(D128)
 MI355_DIRECT(D128w4)
 MI355_DIRECT(D256w4)
 MI355_DIRECT(D128k32)
+MI355_DIRECT(D128w8)
+MI355_DIRECT(D64x256)
+MI355_DIRECT(D64x128)
 #undef MI355_DIRECT
 #define MI355_PINGPONG(T)                                     \
     template __global__ void gemm_pingpong<T, 0>(GemmArgs);   \
@@ -155,6 +161,9 @@ const Config kConfigs[] = {
     direct_config<D128w4>("d128x128x64_w2x2_s4", 8),
     direct_config<D256w4>("d256x256x32_w2x2_s4", 4),
     direct_config<D128k32>("d128x128x32_w2x2_s4", 8),
+    direct_config<D128w8>("d128x128x64_w2x4_s4", 8),
+    direct_config<D64x256>("d64x256x32_w1x4_s4", 8),
+    direct_config<D64x128>("d64x128x32_w1x4_s4", 8),
     pingpong_config<P256>("p256x256x32_w2x4_s4", 4),
     staged_config<T256, true, true>("s256x256x64_w2x2_av_bv", 8),
     staged_config<T128, true, true>("s128x128x64_w2x2_av_bv", 8),
@@ -303,7 +312,9 @@ int tuned_choice(const Request &r, bool av, bool bv)
 // with and without bias + GELU, 4096^3); it needs K % 8 == 0.  Otherwise: 256x256x32
 // tiles on 4 waves of 128x128 from four full waves of them, 256x256x64 tiles (8 waves, 2
 // stages) from one, else 256x128 tiles with two
-// k-groups when they fill the chip, else 128x128 tiles: 4 waves when they fill the chip
+// k-groups when they fill the chip; where at most one wave of 128x128 tiles remains,
+// 64-row tiles (64x256 for short K, 64x128 where 128x128 tiles would idle half the chip),
+// else 128x128 tiles: 4 waves when they fill the chip
 // with K below 4096, two k-groups for long K or with part of the chip idle (two waves per
 // SIMD hide each other's LDS reads and barrier waits).  The 4-wave tiles took over
 // (256x256 at 8192^3) or kept (128x128 at 2048^3) their shapes once the copies lost their
@@ -362,6 +373,18 @@ int choose(const Request &r)
         if (t256 >= 4 * kCUs) return find_direct(256, 256, 32, 4, 1);   // several waves of big tiles
         if (t256 >= kCUs) return find_direct(256, 256, 64, 8, 1);        // about one wave of them
         if (t256x128 >= kCUs) return find_direct(256, 128, 64, 8, 2);    // e.g. one GPU's share of 8192^3
+        // at most one wave of 128x128 tiles with short K (1000x3000x777: 192 tiles either
+        // way): 64x256 tiles, 11.6 us against 12.2 with 128x128x32 (3000x1000x777: 11.6
+        // against 13.2; 2048x2048x777: 11.1-11.3 against 11.2-11.8)
+        const int64_t t64x256 = tiles(r, 64, 256), t64x128 = tiles(r, 64, 128);
+        if (r.K < 1024 && r.N >= 256 && t128 <= kCUs && t64x256 <= kCUs && t64x256 >= kCUs / 2)
+            return find_direct(64, 256, 32, 4, 1);
+        // 128x128 tiles would leave half the chip or more idle: 64x128 tiles, twice as
+        // many, while they still fit in one wave (1024^3: 6.3 us against 8.4 with the
+        // k-group 128x128 tile; 512x4096x1024 7.3 against 8.7; 768^3 6.6 against 8.5);
+        // from K = 4096 the k-group tile wins again (1024x1024x4096: 25.3 against 26.7)
+        if (r.N >= 128 && t128 <= kCUs / 2 && t64x128 <= kCUs && t64x128 >= kCUs / 8 && r.K <= 2048)
+            return find_direct(64, 128, 32, 4, 1);
         // short K: 32-deep stages, so the ring fills and the last stage drains sooner
         if (t128 >= kCUs / 4 && r.K < 1024) return find_direct(128, 128, 32, 4, 1);
         if (t128 >= kCUs) return r.K >= 4096 ? find_direct(128, 128, 64, 8, 2)   // long K: k-groups

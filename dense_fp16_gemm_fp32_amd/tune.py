@@ -149,8 +149,9 @@ def tune(shapes, rounds=7, margin=0.03, log=print, ms=20.0):
 
 def calibration_candidates(a, b, bias=None, epilogue="none", out=None):
     """The configurations ``calibrate`` may time and install for this call: the direct
-    configurations with the selector's tile size (block_m x block_n) that serve its K
-    (the ping-pong ones need K % 8 == 0), or the selector's
+    configurations whose tile area (block_m x block_n) equals the selector's choice's --
+    about the same number of tiles, so the same share of the chip -- and that serve its K (the
+    ping-pong ones need K % 8 == 0), or the selector's
     choice alone when it is not a direct kernel or when B and C rows are not 16-byte
     friendly (the library then splits the launch into a direct part and a narrow strip,
     which a forced configuration cannot do).  Returns (rule name, [candidate names])."""
@@ -173,7 +174,7 @@ def calibration_candidates(a, b, bias=None, epilogue="none", out=None):
     if not info["direct"] or not bv:
         return rule_name, [rule_name]
     return rule_name, [c["name"] for c in g.configs()
-                       if c["direct"] and c["block_m"] == info["block_m"] and c["block_n"] == info["block_n"]
+                       if c["direct"] and c["block_m"] * c["block_n"] == info["block_m"] * info["block_n"]
                        and not (c["k_mult8"] and K % 8)]
 
 
@@ -200,8 +201,8 @@ def calibrate(a, b, bias=None, epilogue="none", out=None, candidates=None, ms=20
     than on another, while a neighbouring tile does not, so the measured table and the
     rules cannot know the best tile for every box.
 
-    ``candidates``: configuration names; by default ``calibration_candidates`` (ring
-    depths, k-groups and stage depths of the selector's tile size).  Each must agree with
+    ``candidates``: configuration names; by default ``calibration_candidates`` (the tile
+    shapes, wave layouts, k-groups and ring depths of the selector's tile area).  Each must agree with
     the selector's output (``agrees``: relative Frobenius distance at most 5e-3 and every
     element within 1e-2 * (1 + |ref|)).  Timing as in ``tune``: ``prewarm_ms`` of calls
     first, then ``rounds`` interleaved rounds in alternating order, medians compared.

@@ -196,14 +196,18 @@ def test_select_routes_misaligned_pointers_to_narrow_loads():
     assert c["direct"] == 1
     c = _cfg(_select(1000, 3000, 777))                # the ragged workload: direct, K tail patched
     assert c["direct"] == 1
-    c = _cfg(_select(512, 512, 512, B=P2))
+    # a handful of tiles (no direct launch to split): the register-staged kernel with
+    # narrow B / C accesses
+    c = _cfg(_select(256, 256, 256, B=P2))
     assert c["bc_vector"] == 0
-    c = _cfg(_select(512, 512, 512, C=P2))
+    c = _cfg(_select(256, 256, 256, C=P2))
     assert c["bc_vector"] == 0
-    c = _cfg(_select(512, 512, 512, epi=2, bias=P16 + 4))  # bias only 4-byte aligned
+    c = _cfg(_select(256, 256, 256, epi=2, bias=P16 + 4))  # bias only 4-byte aligned
     assert c["bc_vector"] == 0
-    c = _cfg(_select(512, 500, 512))                      # N % 8 != 0
+    c = _cfg(_select(256, 250, 256))                      # N % 8 != 0
     assert c["bc_vector"] == 0
+    c = _cfg(_select(512, 512, 512, B=P2))                # enough tiles: direct, split launch
+    assert c["direct"] == 1
 
 
 def test_select_rejects_invalid_and_empty():
@@ -338,12 +342,17 @@ def test_attention_argument_checks(args, want):
     ((2048, 2048, 8192), "d128x128x64_w2x2k2_s4"),    # 256 tiles, long K
     ((2048, 2048, 2048), "d128x128x64_w2x2_s4"),      # 256 tiles, K = 2048
     ((2048, 2048, 1024), "d128x128x64_w2x2_s4"),      # 256 tiles, K = 1024
-    ((2048, 2048, 768), "d128x128x32_w2x2_s4"),       # 256 tiles, K < 1024
-    ((2048, 2048, 512), "d128x128x32_w2x2_s4"),
-    ((1024, 1024, 1024), "d128x128x64_w2x2k2_s4"),    # 64 tiles
+    ((2048, 2048, 768), "d64x256x32_w1x4_s4"),        # one wave of 128x128 tiles, K < 1024
+    ((2048, 2048, 512), "d64x256x32_w1x4_s4"),
+    ((3072, 2048, 512), "d128x128x32_w2x2_s4"),       # 1.5 waves of them, K < 1024
+    ((1024, 1024, 1024), "d64x128x32_w1x4_s4"),       # 64 tiles of 128x128, 128 of 64x128
+    ((512, 4096, 1024), "d64x128x32_w1x4_s4"),
+    ((768, 768, 768), "d64x128x32_w1x4_s4"),
+    ((1024, 1024, 4096), "d128x128x64_w2x2k2_s4"),    # 64 tiles, long K
+    ((1536, 1536, 1536), "d128x128x64_w2x2k2_s4"),    # 144 tiles (288 of 64x128)
     ((1000, 3000, 1024), "d128x128x64_w2x2k2_s4"),    # 192 tiles, K = 1024
-    ((1000, 3000, 777), "d128x128x32_w2x2_s4"),       # 192 tiles, K < 1024
-    ((3000, 1000, 777), "d128x128x32_w2x2_s4"),
+    ((1000, 3000, 777), "d64x256x32_w1x4_s4"),        # 192 tiles, K < 1024
+    ((3000, 1000, 777), "d64x256x32_w1x4_s4"),
     ((256, 256, 256), "s64x64x64_w2x1_av_bv"),        # a handful of tiles
 ])
 def test_selector_rules_pick_the_measured_winners(shape, want):
@@ -356,10 +365,11 @@ def test_selector_rules_pick_the_measured_winners(shape, want):
 @pytest.mark.parametrize("shape,ptr_off,want", [
     ((2048, 2047, 2048), 0, "d128x128x64_w2x2_s4"),   # odd N: direct on the first 2040 columns
     ((8192, 8191, 8192), 0, "d256x256x32_w2x2_s4"),
-    ((1000, 3001, 777), 0, "d128x128x32_w2x2_s4"),
+    ((1000, 3001, 777), 0, "d64x256x32_w1x4_s4"),
     ((2048, 2048, 2048), 2, "d128x128x64_w2x2_s4"),   # B and C only 2-byte aligned
     ((8192, 63, 8192), 0, "s64x64x64_w2x1_av_bn"),    # N < 64: no direct launch to split
-    ((512, 1031, 64), 0, "s64x64x64_w2x1_av_bn"),     # too few tiles
+    ((128, 1031, 64), 0, "s64x64x64_w2x1_av_bn"),     # too few tiles
+    ((512, 1031, 64), 0, "d64x128x32_w1x4_s4"),       # 72 tiles of 64x128
 ])
 def test_selector_splits_unfriendly_rows(shape, ptr_off, want):
     """Rows of B and C that are not 16-byte friendly keep the direct kernel from N >= 64
@@ -411,10 +421,11 @@ def test_installed_choice_overrides_the_selector_for_its_exact_key_only():
         staged = g.config_id("s64x64x64_w2x1_an_bn")
         g.set_choice(1000, 3001, 777, "bias_gelu", False, False, staged)
         assert _select(1000, 3001, 777, epi=2) == staged
-        assert _select(1000, 3000, 777, epi=2) == k32                 # class 1: the rules
+        ragged = g.config_id("d64x256x32_w1x4_s4")
+        assert _select(1000, 3000, 777, epi=2) == ragged              # class 1: the rules
         g.clear_choices()
         assert _select(2048, 2048, 2048) == k64
-        assert _select(1000, 3001, 777, epi=2) == k32
+        assert _select(1000, 3001, 777, epi=2) == ragged
     finally:
         g.clear_choices()
 

@@ -94,7 +94,7 @@ def test_small_integer_products_bitexact_every_config(shape):
 def _members(w, epi):
     """Every configuration a benchmark run of workload w may launch: the selector's choice
     and each configuration run-time calibration may install in its place (tune's
-    calibration_candidates, the direct configurations of the same tile size).  Names, the
+    calibration_candidates, the direct configurations of the same tile area).  Names, the
     selector's first."""
     from dense_fp16_gemm_fp32_amd import tune
     A = torch.empty((w.M, w.K), dtype=torch.float16, device=DEV)
@@ -107,7 +107,7 @@ def _members(w, epi):
 
 def test_members_cover_the_calibration_family():
     """The member list the full-size tests below walk is the selector's choice plus every
-    direct configuration of its tile size, at least two at each workload except 256^3."""
+    direct configuration of its tile area, at least two at each workload except 256^3."""
     for w in workloads.WORKLOADS:
         for e in w.epilogues:
             names = _members(w, e)
