@@ -40,13 +40,13 @@ HEADLINE = "gemm_2048"
 # each scaled by what the same counter reads for a plain copy of known size (the
 # --calibrate-copy run).  Reported only while the kernel sources hash to the version the
 # counters were taken on (profiles/ holds the summary); otherwise null.
-TRAFFIC = {"kernel_config": "d128x128x64_w2x2_s4", "sources_sha256_16": "682a06ce35342b31",
-           "bytes": 58915136}
+TRAFFIC = {"kernel_config": "d128x128x64_w2x2_s4", "sources_sha256_16": "88f4d3f42ba68837",
+           "bytes": 58914251}
 
 
 # The files whose text defines the GEMM kernels (the configuration name fixes the template
 # arguments); the counters above stand only while their code is unchanged.
-GEMM_KERNEL_SOURCES = ("gemm_common.hpp", "gemm_direct.hpp", "gemm_staged.hpp")
+GEMM_KERNEL_SOURCES = ("gemm_common.hpp", "gemm_direct.hpp", "gemm_staged.hpp", "gemm_pingpong.hpp")
 
 
 def code_text(source: str) -> str:
@@ -66,10 +66,11 @@ def kernel_sources_hash() -> str:
     return h.hexdigest()[:16]
 
 
-# The same counters for the other 128x128 tiles a calibrated run may take at 2048^3 (each
-# forced with --config; profiles/ holds the summary).
-TRAFFIC_OTHER = {"sources_sha256_16": "682a06ce35342b31",
-                 "bytes": {"d128x128x32_w2x2_s4": 58854803, "d128x128x64_w2x2k2_s4": 58846591}}
+# The same counters for the other tiles of the same area a calibrated run may take at
+# 2048^3 (each forced with --config; profiles/ holds the summary).
+TRAFFIC_OTHER = {"sources_sha256_16": "88f4d3f42ba68837",
+                 "bytes": {"d128x128x64_w2x2k2_s4": 58850705, "d128x128x32_w2x2_s4": 58854740,
+                           "d128x128x64_w2x4_s4": 58822716, "d64x256x32_w1x4_s4": 58849647}}
 
 
 def traffic_for(kernel_config: str):
@@ -148,14 +149,17 @@ def time_gemm(lib, A, B, bias, epi, out, steps, warmup, config=None, min_warm_ms
     """Three timed passes of `steps` calls each, after `warmup` untimed calls (and more,
     up to `min_warm_ms` milliseconds of them, see warm_up).
 
-    Pass 1 (the step time): wall clock between synchronisations around the back-to-back
-    calls, and device events at both ends of the same region on the launch stream.
-    Pass 2 (the kernel time): every launch records its own pair of HIP events from the
-    kernel dispatch (mi355gemm_gemm_timed), as the kernel starts and as it ends; the mean
-    pair time is the kernel's average duration, which the roofline uses.  It is the
-    figure a rocprofv3 kernel trace reports.
+    Pass 1 (the step and kernel time): wall clock between synchronisations around the
+    back-to-back calls, and HIP events at both ends of the same region on the stream the
+    kernels are launched on; the event time per call is the kernel's average launch
+    duration, which the roofline uses (a rocprofv3 kernel trace of the same back-to-back
+    calls reads within a few percent of it).
+    Pass 2: every launch records its own pair of HIP events from the kernel dispatch
+    (mi355gemm_gemm_timed), as the kernel starts and as it ends.  Kept for reference
+    only: the per-launch signalling it adds has read from 1% to 17% above the
+    back-to-back time from run to run, and over 60% above it under a profiler.
     Pass 3: an event pair recorded on the stream around every call; it also counts the
-    dispatch latency of each launch, about 1.6 us more than the kernel time at 2048^3.
+    dispatch latency of each launch.
     Returns (ms per step by wall clock, ms per step by events, mean, median and minimum
     ms per launch from pass 2, mean ms per call from pass 3, warm-up calls made)."""
     import torch
@@ -239,7 +243,7 @@ def inputs_sha256(w, epi) -> dict:
 def run_cold(lib, w, steps, min_warm_ms=MIN_WARMUP_MS, min_bytes=256 << 20):
     """The workload with cold caches: enough copies of A and B (more than min_bytes in
     all, past the L2s and the Infinity Cache) that each call reads operands the previous
-    calls did not touch; kernel time from the dispatch's own events, mean and median."""
+    calls did not touch; kernel time per launch from HIP events around back-to-back calls."""
     import torch
     import workloads
     A, B, _ = workloads.make_inputs(w.M, w.N, w.K, w.dist, with_bias=False, seed=w.seed)
@@ -255,20 +259,16 @@ def run_cold(lib, w, steps, min_warm_ms=MIN_WARMUP_MS, min_bytes=256 << 20):
         lib.gemm(As[turn[0] % n], Bs[turn[0] % n], out=out)
         turn[0] += 1
     warm_up(call, n, min_warm_ms)
-    pairs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-             for _ in range(steps)]
-    for a, b in pairs:              # creates the HIP events the launches re-record
-        a.record(stream)
-        b.record(stream)
+    start = torch.cuda.Event(enable_timing=True)
+    stop = torch.cuda.Event(enable_timing=True)
+    start.record(stream)
+    for _ in range(steps):
+        call()
+    stop.record(stream)
     torch.cuda.synchronize()
-    for i, (a, b) in enumerate(pairs):
-        lib.gemm(As[i % n], Bs[i % n], out=out, events=(a, b))
-    torch.cuda.synchronize()
-    per = sorted(a.elapsed_time(b) for a, b in pairs)
-    mean = sum(per) / len(per)
+    mean = start.elapsed_time(stop) / steps
     return {"workload": w.name + "_cold", "copies": n, "bytes_rotated": n * per_copy,
-            "kernel_us": mean * 1e3, "kernel_median_us": per[len(per) // 2] * 1e3,
-            "tflops": w.flops / (mean * 1e-3) / 1e12}
+            "kernel_us": mean * 1e3, "tflops": w.flops / (mean * 1e-3) / 1e12}
 
 
 RESIDENCY_KEYS = ("accumulation_counter", "ppt_residency_acc", "socket_thm_residency_acc",
@@ -453,8 +453,9 @@ def run_workload(lib, w, epi, steps, warmup, config=None, min_warm_ms=MIN_WARMUP
         from dense_fp16_gemm_fp32_amd import tune
         calibration = tune.calibrate(A, B, bias, epi, out=out)[1]
     cid = lib.select(A, B, bias, epi, out=out) if config is None else lib.config_id(config)
-    wall_ms, event_ms, kernel_ms, kernel_med, kernel_min, call_ms, warm = time_gemm(
+    wall_ms, event_ms, disp_ms, disp_med, disp_min, call_ms, warm = time_gemm(
         lib, A, B, bias, epi, out, steps, warmup, config, min_warm_ms)
+    kernel_ms = event_ms   # the back-to-back event time per launch
     tflops = w.flops / (wall_ms * 1e-3) / 1e12
     # launch-bound sizes: the same calls replayed from a captured graph
     graph_ms = time_graph(lib, A, B, bias, epi, out, min_warm_ms=min_warm_ms) if w.M <= 256 else None
@@ -475,8 +476,9 @@ def run_workload(lib, w, epi, steps, warmup, config=None, min_warm_ms=MIN_WARMUP
         "pct_of_peak": 100.0 * tflops / PEAK_FP16_TFLOPS,
         "event_us": event_ms * 1e3,
         "kernel_us": kernel_ms * 1e3,
-        "kernel_median_us": kernel_med * 1e3,
-        "kernel_min_us": kernel_min * 1e3,
+        "dispatch_event_us": disp_ms * 1e3,
+        "dispatch_event_median_us": disp_med * 1e3,
+        "dispatch_event_min_us": disp_min * 1e3,
         "call_event_pair_us": call_ms * 1e3,
         "warmup_calls": warm,
         "graph_us_per_call": graph_ms * 1e3 if graph_ms is not None else None,
@@ -650,8 +652,10 @@ def main():
     sampler = ClockSampler() if args.clock else None
     head = run_workload(lib, w, epi, args.steps, args.warmup, args.config, args.min_warmup_ms,
                         args.calibrate, sampler)
-    print("bench: headline %.2f us/step (events %.2f us), kernel %.2f us, %.1f TFLOP/s%s"
-          % (head["us"], head["event_us"], head["kernel_us"], head["tflops"], clock_text(head["clock"])),
+    print("bench: headline %.2f us/step (events %.2f us per launch), %.1f TFLOP/s; per-launch "
+          "dispatch events %.2f us%s"
+          % (head["us"], head["event_us"], head["tflops"], head["dispatch_event_us"],
+             clock_text(head["clock"])),
           file=sys.stderr, flush=True)
     if args.calibrate_copy:
         calibrate_copy()
@@ -735,11 +739,12 @@ def main():
         "event_ms_per_step": head["event_us"] * 1e-3,
         "kernel_us": head["kernel_us"],
         "calibration_us": head["calibration_us"],
-        "kernel_median_us": head["kernel_median_us"],
-        "kernel_min_us": head["kernel_min_us"],
+        "dispatch_event_us": head["dispatch_event_us"],
+        "dispatch_event_median_us": head["dispatch_event_median_us"],
+        "dispatch_event_min_us": head["dispatch_event_min_us"],
         "call_event_pair_us": head["call_event_pair_us"],
-        # the dominant (only) kernel: 2*M*N*K flops per launch over its mean duration from
-        # the events each launch records as its kernel starts and ends
+        # the dominant (only) kernel: 2*M*N*K flops per launch over its average launch
+        # duration, HIP events around the timed back-to-back launches on their stream
         "roofline": {"bound": "mfma", "achieved": head["kernel_tflops"],
                      "peak": PEAK_FP16_TFLOPS, "unit": "TFLOP/s",
                      "frac": head["kernel_tflops"] / PEAK_FP16_TFLOPS,

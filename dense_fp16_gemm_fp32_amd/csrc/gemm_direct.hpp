@@ -492,9 +492,33 @@ __device__ __forceinline__ void static_for(F &&f)
 }
 
 // KTAIL = false: the variant for K % 8 == 0, without the K-tail patch.
+// Phase clock (diagnostic build only, MI355_PHASE_CLOCK=1): thread 0 of each workgroup
+// records s_memrealtime (100 MHz) and s_memtime (shader clock cycles) at the kernel's phase
+// boundaries -- 0 entry, 1 first stage landed, 2 K loop done, 3 epilogue in LDS, 4 after
+// the barrier, 5 C stores issued, 6 C stores complete -- into g_phase_clock[tile][slot]
+// (realtime) and [tile][8 + slot] (cycles), for the first kPhaseClockTiles workgroups.
+// The regular build compiles the calls to nothing.
+#ifndef MI355_PHASE_CLOCK
+#define MI355_PHASE_CLOCK 0
+#endif
+constexpr int kPhaseClockTiles = 8192;
+#if MI355_PHASE_CLOCK
+__device__ unsigned long long g_phase_clock[kPhaseClockTiles * 16];
+__device__ __forceinline__ void phase_stamp(int slot)
+{
+    if (threadIdx.x == 0 && blockIdx.x < kPhaseClockTiles) {
+        g_phase_clock[blockIdx.x * 16 + slot] = __builtin_amdgcn_s_memrealtime();
+        g_phase_clock[blockIdx.x * 16 + 8 + slot] = __builtin_amdgcn_s_memtime();
+    }
+}
+#else
+__device__ __forceinline__ void phase_stamp(int) {}
+#endif
+
 template <class T, int EPI, bool KTAIL>
 __global__ void __launch_bounds__(T::NT) gemm_direct(GemmArgs p)
 {
+    phase_stamp(0);
     using St = Stage<T>;
     __shared__ __attribute__((aligned(16))) char lds_raw[T::LDS_BYTES];
 
@@ -580,6 +604,7 @@ __global__ void __launch_bounds__(T::NT) gemm_direct(GemmArgs p)
         wait_counts<T::G * (T::STAGES - 2), 15>();
         if (k_tail && nk == 1) w.patch_tail(ring[0]);
         workgroup_barrier();
+        phase_stamp(1);
         static_for<T::PF>([&](auto qc) {   // the first PF k-steps of stage 0
             constexpr int q = decltype(qc)::value;
             w.read_all(ring[0], q, q);
@@ -600,6 +625,7 @@ __global__ void __launch_bounds__(T::NT) gemm_direct(GemmArgs p)
                 if (k < nk) stage(jc, k, std::false_type{});
             });
         }
+        phase_stamp(2);
         // the copies past the end of K are still landing; none may outlive the kernel
         // (and with k-groups the ring is reused below)
         wait_counts<0, 0>();
@@ -663,8 +689,15 @@ __global__ void __launch_bounds__(T::NT) gemm_direct(GemmArgs p)
         else
             tile_to_lds<T, H, T::FM, EPI>(w.acc, w.bias_raw, w.wm * T::WTM, w.wn * T::WTN, w.lane, ctile);
     }
+    phase_stamp(3);
     __syncthreads();
+    phase_stamp(4);
     lds_to_c<T>(p, m0, n0, rows_valid, ctile);
+    if constexpr (MI355_PHASE_CLOCK != 0) {
+        phase_stamp(5);
+        if (threadIdx.x == 0) wait_counts<0, 0>();   // this thread's C stores complete
+        phase_stamp(6);
+    }
 }
 
 }  // namespace mi355

@@ -722,4 +722,28 @@ const char *mi355gemm_last_error(void) { return g_last_error; }
 
 const char *mi355gemm_version(void) { return "mi355gemm 0.1.0 (gfx950)"; }
 
+#if MI355_PHASE_CLOCK
+// Diagnostic build only (no header declares these): copy out or clear the direct kernel's
+// phase clock, kPhaseClockTiles x 16 values (see gemm_direct.hpp).  `n` values at most.
+int mi355gemm_phase_clock_read(unsigned long long *host, int n)
+{
+    if (host == nullptr || n < 0 || n > kPhaseClockTiles * 16)
+        return fail(MI355GEMM_EINVAL, "phase clock: NULL buffer or n=%d outside 0..%d", n,
+                    kPhaseClockTiles * 16);
+    if (hipMemcpyFromSymbol(host, HIP_SYMBOL(g_phase_clock), sizeof(unsigned long long) * n, 0,
+                            hipMemcpyDeviceToHost) != hipSuccess)
+        return fail(MI355GEMM_EHIP, "phase clock: copy from the device failed");
+    return MI355GEMM_OK;
+}
+
+int mi355gemm_phase_clock_clear(void)
+{
+    void *dev = nullptr;
+    if (hipGetSymbolAddress(&dev, HIP_SYMBOL(g_phase_clock)) != hipSuccess ||
+        hipMemset(dev, 0, sizeof(unsigned long long) * kPhaseClockTiles * 16) != hipSuccess)
+        return fail(MI355GEMM_EHIP, "phase clock: clearing the device array failed");
+    return MI355GEMM_OK;
+}
+#endif
+
 }  // extern "C"
