@@ -311,8 +311,9 @@ int tuned_choice(const Request &r, bool av, bool bv)
 // (two groups of 4 waves taking turns) leads the other 256x256 tiles by 0-1.5% (8192^3
 // with and without bias + GELU, 4096^3); it needs K % 8 == 0.  Otherwise: 256x256x32
 // tiles on 4 waves of 128x128 from four full waves of them, 256x256x64 tiles (8 waves, 2
-// stages) from one, else 256x128 tiles with two
-// k-groups when they fill the chip; where at most one wave of 128x128 tiles remains,
+// stages) from one, 256x256x32 tiles on 8 waves where 256x128 tiles would need more than
+// one round, 256x128 tiles with two k-groups where they fill exactly one;
+// where at most one wave of 128x128 tiles remains,
 // 64-row tiles (64x256 for short K, 64x128 where 128x128 tiles would idle half the chip),
 // else 128x128 tiles: 4 waves when they fill the chip
 // with K below 4096, two k-groups for long K or with part of the chip idle (two waves per
@@ -372,7 +373,12 @@ int choose(const Request &r)
         if (bv && t256 >= kCUs && r.K % 8 == 0) return find_pingpong(256, 256);
         if (t256 >= 4 * kCUs) return find_direct(256, 256, 32, 4, 1);   // several waves of big tiles
         if (t256 >= kCUs) return find_direct(256, 256, 64, 8, 1);        // about one wave of them
-        if (t256x128 >= kCUs) return find_direct(256, 128, 64, 8, 2);    // e.g. one GPU's share of 8192^3
+        // more 256x128 tiles than CUs, fewer 256x256 ones: one round of the larger tiles
+        // beats a second, partly idle round of the smaller ones (3072^3: 144 tiles of
+        // 256x256 in 58.5 us against 85.0 for 288 of 256x128; 3072x3072x2048 41.9 against
+        // 60.0; 6144x2048x2048, 1.5 rounds of 256x128, 50.6 against 63.3)
+        if (t256x128 > kCUs) return find_direct(256, 256, 32, 8, 1);
+        if (t256x128 == kCUs) return find_direct(256, 128, 64, 8, 2);    // e.g. one GPU's share of 8192^3
         // at most one wave of 128x128 tiles with short K (1000x3000x777: 192 tiles either
         // way): 64x256 tiles, 11.6 us against 12.2 with 128x128x32 (3000x1000x777: 11.6
         // against 13.2; 2048x2048x777: 11.1-11.3 against 11.2-11.8)

@@ -342,14 +342,17 @@ def test_attention_argument_checks(args, want):
     ((2048, 2048, 8192), "d128x128x64_w2x2k2_s4"),    # 256 tiles, long K
     ((2048, 2048, 2048), "d128x128x64_w2x2_s4"),      # 256 tiles, K = 2048
     ((2048, 2048, 1024), "d128x128x64_w2x2_s4"),      # 256 tiles, K = 1024
-    ((2048, 2048, 768), "d64x256x32_w1x4_s4"),        # one wave of 128x128 tiles, K < 1024
+    ((2048, 2048, 777), "d64x256x32_w1x4_s4"),        # one wave of 128x128 tiles, K < 1024
     ((2048, 2048, 512), "d64x256x32_w1x4_s4"),
     ((3072, 2048, 512), "d128x128x32_w2x2_s4"),       # 1.5 waves of them, K < 1024
     ((1024, 1024, 1024), "d64x128x32_w1x4_s4"),       # 64 tiles of 128x128, 128 of 64x128
     ((512, 4096, 1024), "d64x128x32_w1x4_s4"),
     ((768, 768, 768), "d64x128x32_w1x4_s4"),
     ((1024, 1024, 4096), "d128x128x64_w2x2k2_s4"),    # 64 tiles, long K
-    ((1536, 1536, 1536), "d128x128x64_w2x2k2_s4"),    # 144 tiles (288 of 64x128)
+    ((1536, 1536, 1024), "d128x128x64_w2x2k2_s4"),    # 144 tiles (288 of 64x128)
+    ((3072, 3072, 2048), "d256x256x32_w2x4_s4"),      # 144 of 256x256 in one round, not
+    ((4096, 2304, 4096), "d256x256x32_w2x4_s4"),      # 288 of 256x128 in two
+    ((6144, 2048, 2048), "d256x256x32_w2x4_s4"),      # 192 of 256x256, not 384 of 256x128
     ((1000, 3000, 1024), "d128x128x64_w2x2k2_s4"),    # 192 tiles, K = 1024
     ((1000, 3000, 777), "d64x256x32_w1x4_s4"),        # 192 tiles, K < 1024
     ((3000, 1000, 777), "d64x256x32_w1x4_s4"),
