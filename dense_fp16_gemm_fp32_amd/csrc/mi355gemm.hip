@@ -312,7 +312,8 @@ int tuned_choice(const Request &r, bool av, bool bv)
 // with and without bias + GELU, 4096^3); it needs K % 8 == 0.  Otherwise: 256x256x32
 // tiles on 4 waves of 128x128 from four full waves of them, 256x256x64 tiles (8 waves, 2
 // stages) from one, 256x256x32 tiles on 8 waves where 256x128 tiles would need more than
-// one round, 256x128 tiles with two k-groups where they fill exactly one;
+// one round, 256x128 tiles with two k-groups where they fill exactly one or where 128x128
+// tiles would need a partial second round;
 // where at most one wave of 128x128 tiles remains,
 // 64-row tiles (64x256 for short K, 64x128 where 128x128 tiles would idle half the chip),
 // else 128x128 tiles: 4 waves when they fill the chip
@@ -378,7 +379,11 @@ int choose(const Request &r)
         // 256x256 in 58.5 us against 85.0 for 288 of 256x128; 3072x3072x2048 41.9 against
         // 60.0; 6144x2048x2048, 1.5 rounds of 256x128, 50.6 against 63.3)
         if (t256x128 > kCUs) return find_direct(256, 256, 32, 8, 1);
-        if (t256x128 == kCUs) return find_direct(256, 128, 64, 8, 2);    // e.g. one GPU's share of 8192^3
+        // one full round of 256x128 tiles (e.g. one GPU's share of 8192^3), or 128x128 tiles
+        // that would need a second, partial round while 256x128 ones fit in one (2304^3
+        // 32.4 us against 36.6; 2560^3 38.7 against 42.2; 3072x2048x2048 31.0 against
+        // 34.0; measured from K = 1024 up)
+        if (t256x128 == kCUs || (t128 > kCUs && r.K >= 1024)) return find_direct(256, 128, 64, 8, 2);
         // at most one wave of 128x128 tiles with short K (1000x3000x777: 192 tiles either
         // way): 64x256 tiles, 11.6 us against 12.2 with 128x128x32 (3000x1000x777: 11.6
         // against 13.2; 2048x2048x777: 11.1-11.3 against 11.2-11.8)

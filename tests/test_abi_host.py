@@ -353,6 +353,8 @@ def test_attention_argument_checks(args, want):
     ((3072, 3072, 2048), "d256x256x32_w2x4_s4"),      # 144 of 256x256 in one round, not
     ((4096, 2304, 4096), "d256x256x32_w2x4_s4"),      # 288 of 256x128 in two
     ((6144, 2048, 2048), "d256x256x32_w2x4_s4"),      # 192 of 256x256, not 384 of 256x128
+    ((2304, 2304, 2304), "d256x128x64_w2x2k2_s3"),    # 162 of 256x128, not 324 of 128x128
+    ((3072, 2048, 2048), "d256x128x64_w2x2k2_s3"),    # 192 of 256x128, not 384 of 128x128
     ((1000, 3000, 1024), "d128x128x64_w2x2k2_s4"),    # 192 tiles, K = 1024
     ((1000, 3000, 777), "d64x256x32_w1x4_s4"),        # 192 tiles, K < 1024
     ((3000, 1000, 777), "d64x256x32_w1x4_s4"),
