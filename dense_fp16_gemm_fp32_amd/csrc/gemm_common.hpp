@@ -101,9 +101,11 @@ __device__ __forceinline__ float gelu_erf(float x)
     constexpr float a1 = 0.5f * 0.254829592f, a2 = 0.5f * -0.284496736f, a3 = 0.5f * 1.421413741f,
                     a4 = 0.5f * -1.453152027f, a5 = 0.5f * 1.061405429f;
     constexpr float kHalfLog2e = 0.72134752044448170f;   // log2(e) / 2: exp(-z^2) = 2^(-x^2 log2(e) / 2)
-    // |x| clamped to the largest finite float: for x = +inf the last step then gives
-    // inf - 3.4e38 * 0 = inf (unclamped it would be inf * 0 = NaN); finite x are unchanged
-    const float ax = fminf(fabsf(x), 3.4028234663852886e38f);
+    // x capped at the largest finite float before taking |x|: for x = +inf the last step
+    // then gives inf - 3.4e38 * 0 = inf (uncapped, inf * 0 = NaN); x = -inf keeps |x| =
+    // inf, so -inf * 0 = NaN, as x * Phi(x) evaluates in IEEE arithmetic; a NaN x reaches
+    // the result through h; finite x are unchanged
+    const float ax = fabsf(fminf(x, 3.4028234663852886e38f));
     const float t = __builtin_amdgcn_rcpf(fmaf(p, ax, 1.0f));
     const float poly = t * fmaf(t, fmaf(t, fmaf(t, fmaf(t, a5, a4), a3), a2), a1);
     const float h = poly * __builtin_amdgcn_exp2f(-(x * x) * kHalfLog2e);   // Phi(-|x|)

@@ -365,6 +365,30 @@ def test_gelu_epilogue_every_finite_fp16_input():
         assert (d == 0).mean() >= 0.99, "%s: only %.4f exact" % (cfg["name"], (d == 0).mean())
 
 
+def test_gelu_epilogue_non_finite_inputs():
+    """+inf, -inf and NaN in the bias reach the epilogue as GELU's input (A = 0): the result
+    is what x * Phi(x) gives in IEEE arithmetic, as the oracle evaluates it -- +inf for
+    +inf, NaN for -inf (-inf * 0) and for NaN -- and the finite columns beside them are
+    unaffected, on every configuration."""
+    M, N, K = 8, 64, 16
+    vals = [float("inf"), float("-inf"), float("nan"), 65504.0, -65504.0, 0.0, -0.0, 1.0]
+    bias = torch.tensor((vals * (N // len(vals)))[:N], dtype=torch.float16)
+    A = torch.zeros((M, K), dtype=torch.float16)
+    _, B, _ = workloads.make_inputs(M, N, K, "normal", seed=6)
+    ref = oracle.gemm(A, B, bias, "bias_gelu").view(np.float16).astype(np.float64)
+    assert np.isposinf(ref[0, 0]) and np.isnan(ref[0, 1]) and np.isnan(ref[0, 2])
+    for cfg in all_configs():
+        if not _compatible(cfg, M, N, K):
+            continue
+        print("gelu non-finite", cfg["name"], flush=True)
+        got = _run(A, B, bias, "bias_gelu", config=cfg["id"]).cpu().numpy().astype(np.float64)
+        assert np.array_equal(np.isnan(got), np.isnan(ref)), cfg["name"]
+        assert np.array_equal(np.isposinf(got), np.isposinf(ref)), cfg["name"]
+        assert np.array_equal(np.isneginf(got), np.isneginf(ref)), cfg["name"]
+        fin = np.isfinite(ref)
+        assert np.all(np.abs(got[fin] - ref[fin]) <= 1e-2 * (1 + np.abs(ref[fin]))), cfg["name"]
+
+
 # ---- the direct kernel on A with any alignment and any K --------------------------------
 
 @pytest.mark.parametrize("shape", [(300, 264, 777), (1000, 3000, 777), (130, 136, 9), (64, 128, 5),
