@@ -53,3 +53,26 @@ def test_calibrate_with_one_candidate_installs_nothing():
     name, med = tune.calibrate(Ad, Bd, candidates=["d128x128x64_w2x2_s4"])
     assert name == "d128x128x64_w2x2_s4" and med == {}
     assert g.select(Ad, Bd) == rule
+
+
+@pytest.mark.parametrize("shape", [(2048, 2047, 2048), (1000, 3001, 777)],
+                         ids=lambda v: "x".join(map(str, v)))
+def test_calibrate_on_rows_that_are_not_16_byte_friendly_installs_nothing(shape):
+    """Odd N: the library splits the call into a direct launch and a narrow strip, which a
+    forced configuration cannot do, so calibration has the selector's choice as its only
+    candidate, times nothing and installs nothing; the call itself still serves the shape
+    and matches the oracle."""
+    M, N, K = shape
+    print("calibrate odd N", shape, flush=True)
+    A, B, bias = workloads.make_inputs(M, N, K, "uniform", with_bias=True, seed=12)
+    Ad, Bd, biasd = A.cuda(), B.cuda(), bias.cuda()
+    rule = g.select(Ad, Bd, biasd, "bias_gelu")
+    name, med = tune.calibrate(Ad, Bd, biasd, "bias_gelu", ms=2.0, rounds=2, prewarm_ms=10.0)
+    assert name == g.mi355gemm_config_name(rule) and med == {}
+    assert g.select(Ad, Bd, biasd, "bias_gelu") == rule
+    got = g.gemm(Ad, Bd, biasd, "bias_gelu")
+    torch.cuda.synchronize()
+    ref = oracle.gemm(A, B, bias, "bias_gelu").view(np.float16).astype(np.float64)
+    out = got.cpu().numpy().astype(np.float64)
+    assert np.linalg.norm(out - ref) <= 5e-3 * np.linalg.norm(ref)
+    assert np.all(np.abs(out - ref) <= 1e-2 * (1 + np.abs(ref)))
