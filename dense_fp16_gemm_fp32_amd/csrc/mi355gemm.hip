@@ -392,9 +392,11 @@ int choose(const Request &r)
             return find_direct(64, 256, 32, 4, 1);
         // 128x128 tiles would leave half the chip or more idle: 64x128 tiles, twice as
         // many, while they still fit in one wave (1024^3: 6.3 us against 8.4 with the
-        // k-group 128x128 tile; 512x4096x1024 7.3 against 8.7; 768^3 6.6 against 8.5);
-        // from K = 4096 the k-group tile wins again (1024x1024x4096: 25.3 against 26.7)
-        if (r.N >= 128 && t128 <= kCUs / 2 && t64x128 <= kCUs && t64x128 >= kCUs / 8 && r.K <= 2048)
+        // k-group 128x128 tile; 512x4096x1024 7.3 against 8.7; 768^3 6.6 against 8.5;
+        // 256^3, 8 tiles: 4.1 us per kernel against 4.5-4.8 for the register-staged
+        // 64x64 tile); from K = 4096 the k-group tile wins again (1024x1024x4096: 25.3
+        // against 26.7)
+        if (r.N >= 128 && t128 <= kCUs / 2 && t64x128 <= kCUs && t64x128 >= kCUs / 32 && r.K <= 2048)
             return find_direct(64, 128, 32, 4, 1);
         // short K: 32-deep stages, so the ring fills and the last stage drains sooner
         if (t128 >= kCUs / 4 && r.K < 1024) return find_direct(128, 128, 32, 4, 1);

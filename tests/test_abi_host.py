@@ -177,8 +177,8 @@ def test_select_for_the_workload_shapes():
             if w.K % 8 != 0:
                 assert c["a_vector"] == 0, w.name     # ragged K: A may not need 16-byte rows
             assert c["bc_vector"] == (1 if w.N % 8 == 0 else 0), w.name
-            # every workload but the tiny one fills the chip with the direct kernel
-            assert c["direct"] == (0 if w.M * w.N < 128 * 128 * 128 else 1), w.name
+            # every workload takes the direct kernel (256^3 its 64x128 tile, 8 of them)
+            assert c["direct"] == 1, w.name
     # large square problems take the widest tile; 2048^3 must still fill 256 CUs
     big = _cfg(_select(8192, 8192, 8192))
     assert (big["block_m"], big["block_n"]) == (256, 256)
@@ -198,13 +198,13 @@ def test_select_routes_misaligned_pointers_to_narrow_loads():
     assert c["direct"] == 1
     # a handful of tiles (no direct launch to split): the register-staged kernel with
     # narrow B / C accesses
-    c = _cfg(_select(256, 256, 256, B=P2))
+    c = _cfg(_select(128, 256, 256, B=P2))
     assert c["bc_vector"] == 0
-    c = _cfg(_select(256, 256, 256, C=P2))
+    c = _cfg(_select(128, 256, 256, C=P2))
     assert c["bc_vector"] == 0
-    c = _cfg(_select(256, 256, 256, epi=2, bias=P16 + 4))  # bias only 4-byte aligned
+    c = _cfg(_select(128, 256, 256, epi=2, bias=P16 + 4))  # bias only 4-byte aligned
     assert c["bc_vector"] == 0
-    c = _cfg(_select(256, 250, 256))                      # N % 8 != 0
+    c = _cfg(_select(128, 250, 256))                      # N % 8 != 0
     assert c["bc_vector"] == 0
     c = _cfg(_select(512, 512, 512, B=P2))                # enough tiles: direct, split launch
     assert c["direct"] == 1
@@ -358,7 +358,8 @@ def test_attention_argument_checks(args, want):
     ((1000, 3000, 1024), "d128x128x64_w2x2k2_s4"),    # 192 tiles, K = 1024
     ((1000, 3000, 777), "d64x256x32_w1x4_s4"),        # 192 tiles, K < 1024
     ((3000, 1000, 777), "d64x256x32_w1x4_s4"),
-    ((256, 256, 256), "s64x64x64_w2x1_av_bv"),        # a handful of tiles
+    ((256, 256, 256), "d64x128x32_w1x4_s4"),          # 8 tiles of 64x128
+    ((128, 256, 256), "s64x64x64_w2x1_av_bv"),        # a handful of tiles
 ])
 def test_selector_rules_pick_the_measured_winners(shape, want):
     """The rules' choice for shapes the interleaved tuner measured (they have no table
@@ -373,7 +374,7 @@ def test_selector_rules_pick_the_measured_winners(shape, want):
     ((1000, 3001, 777), 0, "d64x256x32_w1x4_s4"),
     ((2048, 2048, 2048), 2, "d128x128x64_w2x2_s4"),   # B and C only 2-byte aligned
     ((8192, 63, 8192), 0, "s64x64x64_w2x1_av_bn"),    # N < 64: no direct launch to split
-    ((128, 1031, 64), 0, "s64x64x64_w2x1_av_bn"),     # too few tiles
+    ((64, 775, 64), 0, "s64x64x64_w2x1_av_bn"),       # too few tiles (7 of 64x128)
     ((512, 1031, 64), 0, "d64x128x32_w1x4_s4"),       # 72 tiles of 64x128
 ])
 def test_selector_splits_unfriendly_rows(shape, ptr_off, want):

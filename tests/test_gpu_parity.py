@@ -265,7 +265,8 @@ def test_empty_and_zero_k():
 
 
 def test_misaligned_operands_use_narrow_loads():
-    M, N, K = 200, 136, 96
+    # few enough tiles (4 of 64x128) that the register-staged kernel serves the call
+    M, N, K = 100, 136, 96
     A, B, bias = workloads.make_inputs(M, N, K, "normal", with_bias=True, seed=6)
     # views one element into larger buffers: 2-byte aligned only
     Ab = torch.zeros(M * K + 1, dtype=torch.float16, device=DEV)
