@@ -185,12 +185,16 @@ def config_id(name: str) -> int:
     return _config_ids[name]
 
 
+_F16 = torch.float16
+
+
 def _check_tensor(t, name, ndim):
+    # the cheap attribute reads first: this runs three times per call on the launch path
     if not isinstance(t, torch.Tensor):
         raise TypeError("%s must be a torch.Tensor" % name)
-    if t.dtype != torch.float16:
+    if t.dtype is not _F16:
         raise TypeError("%s must be float16, got %s" % (name, t.dtype))
-    if t.device.type != "cuda":
+    if not t.is_cuda:
         raise ValueError("%s must be on a GPU device" % name)
     if t.dim() != ndim or not t.is_contiguous():
         raise ValueError("%s must be a contiguous %d-D tensor" % (name, ndim))
@@ -209,6 +213,11 @@ try:   # the raw handle of the current stream without building a Stream object
 except AttributeError:  # pragma: no cover - older torch
     def _raw_stream(index):
         return torch.cuda.current_stream(index).cuda_stream
+
+try:   # the current device index, without torch.cuda's Python-level checks
+    _current_device = torch._C._cuda_getDevice
+except AttributeError:  # pragma: no cover - older torch
+    _current_device = torch.cuda.current_device
 
 
 def gemm(a: torch.Tensor, b: torch.Tensor, bias: torch.Tensor | None = None,
@@ -244,9 +253,16 @@ def gemm(a: torch.Tensor, b: torch.Tensor, bias: torch.Tensor | None = None,
         if tuple(out.shape) != (M, N) or out.device != dev:
             raise ValueError("out must be (%d, %d) on %s" % (M, N, dev))
     lib = _lib if _lib is not None else library()
-    idx = dev.index if dev.index is not None else torch.cuda.current_device()
+    cur = _current_device()
+    idx = dev.index if dev.index is not None else cur
     sptr = stream.cuda_stream if stream is not None else _raw_stream(idx)
     args = (M, N, K, a.data_ptr(), b.data_ptr(), out.data_ptr(), bptr, epi, sptr)
+    if config is None and events is None and idx == cur:
+        # the common call: the selector's choice on the current device
+        st = lib.mi355gemm_gemm(*args)
+        if st != OK:
+            raise GemmError(st, mi355gemm_last_error())
+        return out
     # config None: the selector's choice; any given id goes to the library, which rejects
     # ids out of range (the timed entry reads -1 as the selector's choice, so a negative
     # id given here is rejected before it)
@@ -264,7 +280,7 @@ def gemm(a: torch.Tensor, b: torch.Tensor, bias: torch.Tensor | None = None,
             return lib.mi355gemm_gemm_timed(*args, -1 if cid is None else cid, ev[0], ev[1])
         return lib.mi355gemm_gemm(*args) if cid is None else lib.mi355gemm_gemm_config(*args, cid)
     # the library launches on the calling thread's current HIP device
-    if idx == torch.cuda.current_device():
+    if idx == cur:
         st = call()
     else:
         with torch.cuda.device(idx):
