@@ -81,7 +81,7 @@ struct DTile {
     static constexpr int RED_BYTES = KGROUPS > 1 ? NW * (NMFMA / 2) * 4096 : 0;
     static_assert(WTM % 32 == 0 && WTN % 32 == 0, "wave tile must be whole 32x32 blocks");
     static_assert(BK == 32 || BK == 64, "A swizzle assumes 4 or 8 chunks per row");
-    static_assert(CB % 16 == 0, "B swizzle assumes rows of a multiple of 256 bytes");
+    static_assert(CB % 8 == 0, "B swizzle assumes rows of a multiple of 128 bytes");
     static_assert(A_BYTES % (1024 * NW) == 0 && B_BYTES % (1024 * NW) == 0,
                   "stage must split into whole 1 KiB loads per wave");
     static_assert(KGROUPS == 1 || (KGROUPS == 2 && FM % 2 == 0), "k-groups: 1, or 2 with even FM");
@@ -111,9 +111,19 @@ __device__ __forceinline__ int swz_a(int row)
     return (row / RP) % T::CA;
 }
 
-// B chunk swizzle: a transposing read touches 4 consecutive k-rows x 4 chunks; XOR bits 2-3
-// of the chunk with k % 4 so those 16 chunks fall in distinct 16-byte bank groups.
-__device__ __forceinline__ int swz_b(int k) { return 4 * (k & 3); }
+// B chunk swizzle: a transposing read touches 4 consecutive k-rows (k % 4 = 0..3) x 4
+// chunks (the first a multiple of 4), and those 16 chunks must fall in distinct 16-byte
+// bank groups (16 groups of 4 banks).  Rows of CB chunks start CB % 16 groups apart:
+//   CB % 16 == 0 -- every row starts at group 0: XOR bits 2-3 of the chunk with k % 4;
+//   CB % 16 == 8 -- rows alternate between groups 0 and 8, so only rows k and k + 2
+//                   collide: XOR bit 2 of the chunk with bit 1 of k.  The chunk stays in
+//                   its aligned group of 8, which a row of CB chunks holds whole.
+template <int CB = 16>
+__device__ __forceinline__ int swz_b(int k)
+{
+    static_assert(CB % 8 == 0, "B rows of a multiple of 128 bytes");
+    return CB % 16 == 0 ? 4 * (k & 3) : 4 * ((k >> 1) & 1);
+}
 
 // s_waitcnt immediates for gfx9: vmcnt bits [3:0] and [15:14], expcnt [6:4], lgkmcnt [11:8].
 template <int VM, int LGKM>
@@ -225,7 +235,7 @@ struct DirectWave {
         for (int g = 0; g < T::GB; ++g) {
             const int s = (g * T::NW + wave) * 64 + lane;
             const int row = s / T::CB;
-            const int c = (s % T::CB) ^ swz_b(row);
+            const int c = (s % T::CB) ^ swz_b<T::CB>(row);
             b_off[g] = masked_offset((uint32_t)(row * ldb + 8 * c) * 2u, 8 * c < cols_valid);
         }
         // A fragment: row wm*WTM + i*32 + r32, logical chunk 2*kk + h -> physical chunk
@@ -247,7 +257,7 @@ struct DirectWave {
         // of its group's 4-row band and columns 4*(i%4) .. +3 of its 16-column half; lane j
         // then receives B[band + 0..3][half + j].  Band = 16*kk + 8*h + 4*t, t = 0 or 1.
         const int i16 = lane & 15;
-        const int sb = swz_b(i16 >> 2);
+        const int sb = swz_b<T::CB>(i16 >> 2);
 #pragma unroll
         for (int j = 0; j < T::FN; ++j) {
             const int n = wn * T::WTN + j * 32 + 16 * ((lane >> 4) & 1) + 4 * (i16 & 3);
@@ -398,15 +408,24 @@ struct DirectWave {
 // The C tile is staged in LDS (the ring is free once the K loop is done) so that the
 // stores to HBM are whole rows: 16 bytes per lane, consecutive lanes on consecutive
 // columns, every 128-byte line written by one instruction.  LDS layout: row-major
-// BM x BN fp16, 16-byte chunk c of row r stored at chunk c ^ (r % CW) (CW = chunks per
-// row, a power of two), so the column-wise writes from the accumulator layout spread over
-// the banks.
+// BM x BN fp16 with the 16-byte chunks of each row permuted, so that the column-wise
+// writes from the accumulator layout (one chunk in each of 32 consecutive rows) spread
+// over the 16 bank groups, two rows per group:
+//   CW (chunks per row) a power of two -- chunk c of row r at c ^ (r % CW);
+//   CW % 16 == 8 -- rows start alternately at bank groups 0 and 8, so chunk c of row r
+//                   goes to c ^ ((r / 2) % 8): over 16 rows, (r % 2, (r / 2) % 8) takes
+//                   every value once.  The chunk stays in its aligned group of 8, so the
+//                   row-wise reads of lds_to_c touch the same banks as without it.
 template <class T>
 __device__ __forceinline__ int c_phys(int c, int r)
 {
     constexpr int CW = T::BN / 8;
-    static_assert((CW & (CW - 1)) == 0, "C tile rows of a power-of-two number of chunks");
-    return c ^ (r % CW);
+    if constexpr ((CW & (CW - 1)) == 0) {
+        return c ^ (r % CW);
+    } else {
+        static_assert(CW % 16 == 8, "C tile rows of a power-of-two number of chunks, or 8 past a multiple of 16");
+        return c ^ ((r >> 1) & 7);
+    }
 }
 
 // Bias, GELU and fp16 rounding of accumulator block rows I0 <= i < I1 of this wave,

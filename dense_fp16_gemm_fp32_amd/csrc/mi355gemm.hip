@@ -35,6 +35,7 @@ using D128k32 = DTile<128, 128, 32, 2, 2, 1, 4>;    // 4 waves of 64x64, 64 KiB
 using D128w8 = DTile<128, 128, 64, 2, 4, 1, 4>;     // 8 waves of 64x32, 128 KiB
 using D64x256 = DTile<64, 256, 32, 1, 4, 1, 4>;     // 4 waves of 64x64, 80 KiB
 using D64x128 = DTile<64, 128, 32, 1, 4, 1, 4>;     // 4 waves of 64x32, 40 KiB
+using D64x192 = DTile<64, 192, 32, 2, 2, 1, 4>;     // 4 waves of 32x96, 64 KiB
 // ping-pong tile: BM, BN, BK, waves of a group (M x N), stages
 using P256 = PTile<256, 256, 32, 1, 4, 4>;          // 2 groups x 4 waves of 128x64, 128 KiB
 // attention: head dim, keys per block, waves (32 query rows each), LDS stages
@@ -64,6 +65,7 @@ MI355_DIRECT(D128k32)
 MI355_DIRECT(D128w8)
 MI355_DIRECT(D64x256)
 MI355_DIRECT(D64x128)
+MI355_DIRECT(D64x192)
 #undef MI355_DIRECT
 #define MI355_PINGPONG(T)                                     \
     template __global__ void gemm_pingpong<T, 0>(GemmArgs);   \
@@ -164,6 +166,7 @@ const Config kConfigs[] = {
     direct_config<D128w8>("d128x128x64_w2x4_s4", 8),
     direct_config<D64x256>("d64x256x32_w1x4_s4", 8),
     direct_config<D64x128>("d64x128x32_w1x4_s4", 8),
+    direct_config<D64x192>("d64x192x32_w2x2_s4", 8),
     pingpong_config<P256>("p256x256x32_w2x4_s4", 4),
     staged_config<T256, true, true>("s256x256x64_w2x2_av_bv", 8),
     staged_config<T128, true, true>("s128x128x64_w2x2_av_bv", 8),
@@ -315,7 +318,8 @@ int tuned_choice(const Request &r, bool av, bool bv)
 // one round, 256x128 tiles with two k-groups where they fill exactly one or where 128x128
 // tiles would need a partial second round;
 // where at most one wave of 128x128 tiles remains,
-// 64-row tiles (64x256 for short K, 64x128 where 128x128 tiles would idle half the chip),
+// 64-row tiles (64x192 where a full wave of them fills the chip with K up to 1024, 64x256
+// for short K, 64x128 where 128x128 tiles would idle half the chip),
 // else 128x128 tiles: 4 waves when they fill the chip
 // with K below 4096, two k-groups for long K or with part of the chip idle (two waves per
 // SIMD hide each other's LDS reads and barrier waits).  The 4-wave tiles took over
@@ -384,10 +388,23 @@ int choose(const Request &r)
         // 32.4 us against 36.6; 2560^3 38.7 against 42.2; 3072x2048x2048 31.0 against
         // 34.0; measured from K = 1024 up)
         if (t256x128 == kCUs || (t128 > kCUs && r.K >= 1024)) return find_direct(256, 128, 64, 8, 2);
-        // at most one wave of 128x128 tiles with short K (1000x3000x777: 192 tiles either
-        // way): 64x256 tiles, 11.6 us against 12.2 with 128x128x32 (3000x1000x777: 11.6
-        // against 13.2; 2048x2048x777: 11.1-11.3 against 11.2-11.8)
-        const int64_t t64x256 = tiles(r, 64, 256), t64x128 = tiles(r, 64, 128);
+        const int64_t t64x256 = tiles(r, 64, 256), t64x128 = tiles(r, 64, 128),
+                      t64x192 = tiles(r, 64, 192);
+        // K up to 1024 and a full wave of 64x192 tiles (at most 1/32 of the CUs idle) where
+        // the 128x128, 64x256 and 64x128 tiles fill less of the chip or need a second
+        // round: 1000x3000x777 + bias + GELU 256 tiles, 10.2 us against 10.9 for 192 of
+        // 64x256; 2048x1536x512 5.8 against 6.3; 1024x3072x768 + bias + GELU 8.7 against
+        // 9.4 with 128x128x32; 4096x768x1024 8.5 against 8.9 with the k-group 128x128
+        // tile.  From K = 2048 the k-group 128x128 tile leads (1000x3000x2048 + bias +
+        // GELU 19.2 against 20.2), and 240 tiles were not enough (1280x2304x1024: 9.45
+        // against 9.35).
+        if (r.K <= 1024 && t128 <= kCUs && t64x192 <= kCUs && t64x192 >= kCUs - kCUs / 32 &&
+            t64x192 > t64x256 && t64x192 < t64x128)
+            return find_direct(64, 192, 32, 4, 1);
+        // at most one wave of 128x128 tiles with short K: 64x256 tiles (3000x1000x777: 11.6
+        // us against 13.2 with 128x128x32; 2048x2048x777: 11.1-11.3 against 11.2-11.8; the
+        // ragged 1000x3000x777, 192 tiles of either, 11.6 against 12.2 before the 64x192
+        // tile took it)
         if (r.K < 1024 && r.N >= 256 && t128 <= kCUs && t64x256 <= kCUs && t64x256 >= kCUs / 2)
             return find_direct(64, 256, 32, 4, 1);
         // 128x128 tiles would leave half the chip or more idle: 64x128 tiles, twice as

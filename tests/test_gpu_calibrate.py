@@ -19,7 +19,7 @@ def _no_installed_choices():
     g.clear_choices()
 
 
-@pytest.mark.parametrize("shape,epi", [((1000, 3000, 777), "bias_gelu"), ((2048, 2048, 512), "none")],
+@pytest.mark.parametrize("shape,epi", [((3000, 1000, 777), "bias_gelu"), ((2048, 2048, 512), "none")],
                          ids=lambda v: "x".join(map(str, v)) if isinstance(v, tuple) else v)
 def test_calibrate_installs_a_family_member_and_the_call_uses_it(shape, epi):
     M, N, K = shape
@@ -44,6 +44,26 @@ def test_calibrate_installs_a_family_member_and_the_call_uses_it(shape, epi):
     assert np.all(np.abs(out - ref) <= 1e-2 * (1 + np.abs(ref)))
     g.clear_choices()
     assert g.select(Ad, Bd, b_arg, epi) == rule
+
+
+def test_calibrate_with_a_one_member_tile_area_installs_nothing():
+    """1000x3000x777 takes the 64x192 tile, the only configuration of its tile area: the
+    calibration has nothing to time, installs nothing, and the call still matches the
+    oracle."""
+    M, N, K = 1000, 3000, 777
+    A, B, bias = workloads.make_inputs(M, N, K, "uniform", with_bias=True, seed=13)
+    Ad, Bd, biasd = A.cuda(), B.cuda(), bias.cuda()
+    rule = g.select(Ad, Bd, biasd, "bias_gelu")
+    assert g.mi355gemm_config_name(rule) == "d64x192x32_w2x2_s4"
+    name, med = tune.calibrate(Ad, Bd, biasd, "bias_gelu", ms=2.0, rounds=2, prewarm_ms=10.0)
+    assert name == "d64x192x32_w2x2_s4" and med == {}
+    assert g.select(Ad, Bd, biasd, "bias_gelu") == rule
+    got = g.gemm(Ad, Bd, biasd, "bias_gelu")
+    torch.cuda.synchronize()
+    ref = oracle.gemm(A, B, bias, "bias_gelu").view(np.float16).astype(np.float64)
+    out = got.cpu().numpy().astype(np.float64)
+    assert np.linalg.norm(out - ref) <= 5e-3 * np.linalg.norm(ref)
+    assert np.all(np.abs(out - ref) <= 1e-2 * (1 + np.abs(ref)))
 
 
 def test_calibrate_with_one_candidate_installs_nothing():

@@ -107,13 +107,21 @@ def _members(w, epi):
 
 def test_members_cover_the_calibration_family():
     """The member list the full-size tests below walk is the selector's choice plus every
-    direct configuration of its tile area, at least two at each workload except 256^3."""
+    direct configuration of its tile area (every workload's K is a multiple of 8, so the
+    ping-pong kernel counts): several at 2048^3 and 8192^3, one where the area has a
+    single configuration (256^3 on 64x128, the ragged shape on 64x192)."""
+    areas = {}
+    for c in g.configs():
+        if c["direct"]:
+            areas.setdefault(c["block_m"] * c["block_n"], set()).add(c["name"])
     for w in workloads.WORKLOADS:
         for e in w.epilogues:
             names = _members(w, e)
             print(w.name, e, names, flush=True)
             assert len(set(names)) == len(names)
-            if w.name != "gemm_256":
+            info = g.mi355gemm_config_info(g.config_id(names[0]))
+            assert set(names) == areas[info["block_m"] * info["block_n"]]
+            if w.M >= 2048:
                 assert len(names) >= 2
 
 
