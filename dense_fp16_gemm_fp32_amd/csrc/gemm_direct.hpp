@@ -42,15 +42,22 @@ namespace mi355 {
 // PF: k-steps the LDS fragment reads run ahead of the MFMAs that consume them (1: the next
 // k-step's fragments are read during the current one, 2 fragment buffers; 2 or 3: 4
 // buffers, so each read has one or two whole k-steps of MFMAs to complete in).
+//
+// LOADERS: 0, or the number of extra wavefronts that issue every HBM -> LDS copy while the
+// NW multiplying waves only read LDS and issue MFMAs (the loader waves share the SIMDs
+// with them, one more wave per SIMD for LOADERS = 4).
 template <int BM_, int BN_, int BK_, int WAVES_M_, int WAVES_N_, int KGROUPS_, int STAGES_,
-          int PF_ = 1>
+          int PF_ = 1, int LOADERS_ = 0>
 struct DTile {
     static constexpr int BM = BM_, BN = BN_, BK = BK_;
     static constexpr int WAVES_M = WAVES_M_, WAVES_N = WAVES_N_;
     static constexpr int KGROUPS = KGROUPS_, STAGES = STAGES_, PF = PF_;
     static constexpr int NWC = WAVES_M * WAVES_N;    // waves of one k-group
-    static constexpr int NW = NWC * KGROUPS;
-    static constexpr int NT = 64 * NW;
+    static constexpr int NW = NWC * KGROUPS;         // multiplying waves
+    static constexpr int NL = LOADERS_;              // loader waves (waves NW .. NW+NL-1)
+    static constexpr int NI = NL > 0 ? NL : NW;      // waves that issue the copies
+    static constexpr int NTC = 64 * NW;              // threads of the multiplying waves
+    static constexpr int NT = 64 * (NW + NL);
     static constexpr int WTM = BM / WAVES_M, WTN = BN / WAVES_N;
     static constexpr int FM = WTM / 32, FN = WTN / 32;
     static constexpr int NMFMA = FM * FN;            // MFMAs per k-step per wave
@@ -61,8 +68,8 @@ struct DTile {
     static constexpr int CB = BN / 8;                // 16-byte chunks per B row
     static constexpr int A_BYTES = BM * BK * 2, B_BYTES = BK * BN * 2;
     static constexpr int STAGE_BYTES = A_BYTES + B_BYTES;
-    static constexpr int GA = A_BYTES / (1024 * NW);   // 1 KiB LDS-DMA loads per wave
-    static constexpr int GB = B_BYTES / (1024 * NW);
+    static constexpr int GA = A_BYTES / (1024 * NI);   // 1 KiB LDS-DMA loads per issuing wave
+    static constexpr int GB = B_BYTES / (1024 * NI);
     static constexpr int G = GA + GB;
     static constexpr int NBUF = PF == 1 ? 2 : 4;      // fragment buffers
     // k-step of a stage that waits for the next stage's copy and crosses the barrier: from
@@ -75,6 +82,8 @@ struct DTile {
     // barrier when the barrier is in that k-step, QB == 0, with more than one k-step).
     static constexpr int G_EARLY = (STAGES >= 3 && Q >= 2) ? G / 2 : G;
     static constexpr int VM_WAIT = G * (STAGES - 3) + ((QB > 0 || Q == 1) ? G_EARLY : 0);
+    // loader waves: the copies of the stages after the next one, in flight at each barrier
+    static constexpr int VM_WAIT_L = G * (STAGES - 2);
     static constexpr int LDS_BYTES = STAGES * STAGE_BYTES;
     // k-group exchange at the end: every wave hands half of its 32x32 fp32 blocks (4 KiB
     // each) to its partner in the other group
@@ -82,8 +91,9 @@ struct DTile {
     static_assert(WTM % 32 == 0 && WTN % 32 == 0, "wave tile must be whole 32x32 blocks");
     static_assert(BK == 32 || BK == 64, "A swizzle assumes 4 or 8 chunks per row");
     static_assert(CB % 8 == 0, "B swizzle assumes rows of a multiple of 128 bytes");
-    static_assert(A_BYTES % (1024 * NW) == 0 && B_BYTES % (1024 * NW) == 0,
+    static_assert(A_BYTES % (1024 * NI) == 0 && B_BYTES % (1024 * NI) == 0,
                   "stage must split into whole 1 KiB loads per wave");
+    static_assert(NL == 0 || (KGROUPS == 1 && NW + NL <= 16), "loader waves: one k-group, 16 waves at most");
     static_assert(KGROUPS == 1 || (KGROUPS == 2 && FM % 2 == 0), "k-groups: 1, or 2 with even FM");
     static_assert(KK % KGROUPS == 0, "k-steps must split evenly over the k-groups");
     static_assert(PF >= 1 && PF <= Q && PF <= 3, "reads run at most one stage and 3 k-steps ahead");
@@ -184,6 +194,7 @@ template <class T>
 struct DirectWave {
     using St = Stage<T>;
     int lane, wave, kg, wm, wn;
+    int issuer;               // index among the waves that issue copies (< 0: none)
     int K, N, ldb, n0;
     const f16 *B;
     __amdgpu_buffer_rsrc_t a_rs;
@@ -211,6 +222,7 @@ struct DirectWave {
         lane = tid & 63;
         wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform: LDS-DMA base
         kg = wave / T::NWC;
+        issuer = T::NL > 0 ? wave - T::NW : wave;
         const int wc = wave % T::NWC;
         wm = wc / T::WAVES_N;
         wn = wc % T::WAVES_N;
@@ -224,7 +236,7 @@ struct DirectWave {
         a_rs = make_rsrc(p.A + (int64_t)m0 * K, (uint32_t)(rows_valid * K) * 2u);
 #pragma unroll
         for (int g = 0; g < T::GA; ++g) {
-            const int s = (g * T::NW + wave) * 64 + lane;
+            const int s = (g * T::NI + issuer) * 64 + lane;
             const int row = s / T::CA;
             const int c = (s % T::CA) ^ swz_a<T>(row);
             a_kc[g] = 8 * c;
@@ -233,7 +245,7 @@ struct DirectWave {
         // B: slot s holds k-row s / CB, physical chunk s % CB = logical chunk ^ swz_b(row).
 #pragma unroll
         for (int g = 0; g < T::GB; ++g) {
-            const int s = (g * T::NW + wave) * 64 + lane;
+            const int s = (g * T::NI + issuer) * 64 + lane;
             const int row = s / T::CB;
             const int c = (s % T::CB) ^ swz_b<T::CB>(row);
             b_off[g] = masked_offset((uint32_t)(row * ldb + 8 * c) * 2u, 8 * c < cols_valid);
@@ -315,7 +327,7 @@ struct DirectWave {
 #pragma unroll
         for (int g = 0; g < T::GA; ++g) {
             if (tail_mask & (1u << g)) {
-                char *q = reinterpret_cast<char *>(dst.a) + ((g * T::NW + wave) * 64 + lane) * 16;
+                char *q = reinterpret_cast<char *>(dst.a) + ((g * T::NI + issuer) * 64 + lane) * 16;
                 uint32_t t[8];
 #pragma unroll
                 for (int e = 0; e < 8; ++e) {
@@ -344,10 +356,10 @@ struct DirectWave {
         const int k0 = kt * T::BK;
         if (g < T::GA) {
             if constexpr (FULL) {
-                lds_dma16(a_rs, dst.a + (g * T::NW + wave) * 512, a_off[g], (uint32_t)k0 * 2u);
+                lds_dma16(a_rs, dst.a + (g * T::NI + issuer) * 512, a_off[g], (uint32_t)k0 * 2u);
             } else {
                 const uint32_t off = masked_offset(a_off[g] + (uint32_t)k0 * 2u, k0 + a_kc[g] < K);
-                lds_dma16(a_rs, dst.a + (g * T::NW + wave) * 512, off);
+                lds_dma16(a_rs, dst.a + (g * T::NI + issuer) * 512, off);
             }
         } else {
             const int gb = g - T::GA;
@@ -355,7 +367,7 @@ struct DirectWave {
             const int rows_k = FULL ? T::BK : min(T::BK, K - k0);
             const __amdgpu_buffer_rsrc_t b_rs =
                 make_rsrc(B + (int64_t)(FULL ? k0 : min(k0, K)) * ldb + n0, span_bytes(rows_k, ldb, N - n0));
-            lds_dma16(b_rs, dst.b + (gb * T::NW + wave) * 512, b_off[gb]);
+            lds_dma16(b_rs, dst.b + (gb * T::NI + issuer) * 512, b_off[gb]);
         }
     }
 
@@ -483,14 +495,15 @@ __device__ __forceinline__ void lds_to_c(const GemmArgs &p, int m0, int n0, int 
                                          const char *ctile)
 {
     constexpr int CW = T::BN / 8;
-    constexpr int PER = T::BM * CW / T::NT;
-    static_assert(T::BM * CW % T::NT == 0, "tile must split evenly over the threads");
+    constexpr int PER = T::BM * CW / T::NTC;
+    static_assert(T::BM * CW % T::NTC == 0, "tile must split evenly over the threads");
+    if (T::NL > 0 && (int)threadIdx.x >= T::NTC) return;   // loader waves store nothing
     const int cols_valid = p.N - n0;
     const __amdgpu_buffer_rsrc_t c_rs =
         make_rsrc(p.C + (int64_t)m0 * p.ldc + n0, span_bytes(rows_valid, p.ldc, cols_valid));
 #pragma unroll
     for (int k = 0; k < PER; ++k) {
-        const int q = threadIdx.x + k * T::NT;
+        const int q = threadIdx.x + k * T::NTC;
         const int r = q / CW, c = q % CW;
         const u32x4 v = *reinterpret_cast<const u32x4 *>(ctile + (r * T::BN + 8 * c_phys<T>(c, r)) * 2);
         const uint32_t off = masked_offset((uint32_t)(r * p.ldc + 8 * c) * 2u, 8 * c < cols_valid);
@@ -549,9 +562,13 @@ __global__ void __launch_bounds__(T::NT) gemm_direct(GemmArgs p)
 
     DirectWave<T> w;
     w.init(p, m0, n0, rows_valid, p.N - n0);
-    if constexpr (EPI != 0) w.load_bias(p);
+    // the multiplying waves (all of them without loader waves); wave-uniform
+    const bool mult = T::NL == 0 || w.wave < T::NW;
+    if constexpr (EPI != 0) {
+        if (mult) w.load_bias(p);
+    }
     const bool k_tail = KTAIL && (p.K & 7) != 0;
-    if (k_tail && nk > 0) w.load_tail(nk);
+    if (k_tail && nk > 0 && (T::NL == 0 || w.issuer >= 0)) w.load_tail(nk);
 
     St *const ring = reinterpret_cast<St *>(lds_raw);
 
@@ -616,7 +633,83 @@ __global__ void __launch_bounds__(T::NT) gemm_direct(GemmArgs p)
         });
     };
 
-    if (nk > 0) {
+    // With loader waves: the multiplying waves run the stages below without copies or
+    // copy waits, and the loader waves run their own loop, which crosses the same
+    // barriers in the same order (the prologue's, then one per stage).  Before the
+    // barrier of stage kt's k-step QB (the one after which stage kt+1 is read) a loader
+    // wave waits for its copies of stage kt+1; after it, it issues the copy of stage
+    // kt+STAGES into the slot of stage kt, whose reads were all issued before that
+    // barrier -- the order the multiplying waves keep themselves without loader waves.
+    auto mult_stage = [&](auto Jc, int kt) {
+        constexpr int J = decltype(Jc)::value;
+        St &cur = ring[J];
+        St &nxt = ring[(J + 1) % T::STAGES];
+        static_for<T::Q>([&](auto qc) {
+            constexpr int q = decltype(qc)::value;
+            constexpr int buf = (J * T::Q + q) % T::NBUF;
+            constexpr int rbuf = (J * T::Q + q + T::PF) % T::NBUF;
+            constexpr bool ahead = q + T::PF >= T::Q;
+            constexpr int rq = (q + T::PF) % T::Q;
+            if constexpr (q == T::QB) workgroup_barrier();   // stage kt+1 has landed
+            static_for<T::NMFMA>([&](auto mc) {
+                constexpr int m = decltype(mc)::value;
+                w.mfma_one(buf, m);
+                constexpr int r0 = m * T::NREAD / T::NMFMA;
+                constexpr int r1 = (m + 1) * T::NREAD / T::NMFMA;
+#pragma unroll
+                for (int r = r0; r < r1; ++r) {
+                    if constexpr (ahead)
+                        w.read_one(nxt, rq, rbuf, r);
+                    else
+                        w.read_one(cur, rq, rbuf, r);
+                }
+                __builtin_amdgcn_sched_barrier(0);
+            });
+        });
+        (void)kt;
+    };
+
+    if constexpr (T::NL > 0) {
+        if (nk > 0 && mult) {
+            workgroup_barrier();   // stage 0 has landed
+            phase_stamp(1);
+            static_for<T::PF>([&](auto qc) {
+                constexpr int q = decltype(qc)::value;
+                w.read_all(ring[0], q, q);
+            });
+            int kt = 0;
+            for (; kt + T::STAGES <= nk; kt += T::STAGES)
+                static_for<T::STAGES>([&](auto jc) { mult_stage(jc, kt + decltype(jc)::value); });
+            if (kt < nk) {
+                static_for<T::STAGES>([&](auto jc) {
+                    const int k = kt + decltype(jc)::value;
+                    if (k < nk) mult_stage(jc, k);
+                });
+            }
+            phase_stamp(2);
+            wait_counts<0, 0>();   // the bias loads
+        } else if (nk > 0) {
+            // loader wave: stages 0 .. STAGES-2 in flight, wait for stage 0
+#pragma unroll
+            for (int s = 0; s < T::STAGES - 1; ++s) w.issue_stage(ring[s], s);
+            wait_counts<T::VM_WAIT_L, 15>();
+            if (k_tail && nk == 1) w.patch_tail(ring[0]);
+            workgroup_barrier();
+            for (int kt = 0; kt < nk; ++kt) {
+                // the slot of stage kt-1 (stage kt+STAGES-1's), free since the last barrier
+                const int ks = kt + T::STAGES - 1;
+                St &dst = ring[ks % T::STAGES];
+                if ((ks + 1) * T::BK <= p.K)
+                    w.template issue_stage<true>(dst, ks);
+                else
+                    w.template issue_stage<false>(dst, ks);
+                wait_counts<T::VM_WAIT_L, 15>();   // stage kt+1 has landed
+                if (k_tail && kt + 1 == nk - 1) w.patch_tail(ring[(kt + 1) % T::STAGES]);
+                workgroup_barrier();
+            }
+            wait_counts<0, 0>();   // no copy outlives the kernel
+        }
+    } else if (nk > 0) {
         // ---- prologue: stages 0 .. STAGES-2 in flight, wait for stage 0 ----
 #pragma unroll
         for (int s = 0; s < T::STAGES - 1; ++s) w.issue_stage(ring[s], s);
@@ -654,7 +747,8 @@ __global__ void __launch_bounds__(T::NT) gemm_direct(GemmArgs p)
     workgroup_barrier();
     char *ctile = lds_raw;
     if constexpr (T::KGROUPS == 1) {
-        tile_to_lds<T, 0, T::FM, EPI>(w.acc, w.bias_raw, w.wm * T::WTM, w.wn * T::WTN, w.lane, ctile);
+        if (mult)
+            tile_to_lds<T, 0, T::FM, EPI>(w.acc, w.bias_raw, w.wm * T::WTM, w.wn * T::WTN, w.lane, ctile);
     } else {
         // Sum the two k-groups' partial tiles.  Group 0 keeps blocks i < FM/2 and hands
         // blocks i >= FM/2 to group 1; group 1 does the opposite; each then finishes the

@@ -42,6 +42,7 @@ struct PTile {
     static constexpr int WM = WM_, WN = WN_;         // waves of one group in M and N
     static constexpr int STAGES = STAGES_;
     static constexpr int NW = 8, NT = 512, NWG = 4;  // waves, threads, waves per group
+    static constexpr int NL = 0, NTC = NT;           // no loader waves: every thread stores C
     static constexpr int ROWS_G = BM / 2;            // rows one group computes
     static constexpr int WTM = ROWS_G / WM, WTN = BN / WN;
     static constexpr int FM = WTM / 32, FN = WTN / 32;

@@ -36,6 +36,8 @@ using D128w8 = DTile<128, 128, 64, 2, 4, 1, 4>;     // 8 waves of 64x32, 128 KiB
 using D64x256 = DTile<64, 256, 32, 1, 4, 1, 4>;     // 4 waves of 64x64, 80 KiB
 using D64x128 = DTile<64, 128, 32, 1, 4, 1, 4>;     // 4 waves of 64x32, 40 KiB
 using D64x192 = DTile<64, 192, 32, 2, 2, 1, 4>;     // 4 waves of 32x96, 64 KiB
+using D128L4 = DTile<128, 128, 64, 2, 2, 1, 4, 1, 4>;   // 4 waves of 64x64 + 4 loader waves
+using D64x192L4 = DTile<64, 192, 32, 2, 2, 1, 4, 1, 4>; // 4 waves of 32x96 + 4 loader waves
 // ping-pong tile: BM, BN, BK, waves of a group (M x N), stages
 using P256 = PTile<256, 256, 32, 1, 4, 4>;          // 2 groups x 4 waves of 128x64, 128 KiB
 // attention: head dim, keys per block, waves (32 query rows each), LDS stages
@@ -66,6 +68,8 @@ MI355_DIRECT(D128w8)
 MI355_DIRECT(D64x256)
 MI355_DIRECT(D64x128)
 MI355_DIRECT(D64x192)
+MI355_DIRECT(D128L4)
+MI355_DIRECT(D64x192L4)
 #undef MI355_DIRECT
 #define MI355_PINGPONG(T)                                     \
     template __global__ void gemm_pingpong<T, 0>(GemmArgs);   \
@@ -109,6 +113,7 @@ struct Config {
     bool narrow;      // vector-ALU kernel for at most bn (8) columns
     bool k_mult8;     // needs K % 8 == 0 (no kernel for the K-tail case)
     bool pingpong;    // two wave groups taking turns
+    int loaders;      // extra waves issuing every HBM -> LDS copy (direct kernel), else 0
 };
 
 template <class T, bool AV, bool BV>
@@ -118,7 +123,7 @@ Config staged_config(const char *name, int group_m)
                   T::LDS_BYTES, AV, BV, group_m,
                   {{gemm_staged<T, AV, BV, 0>, gemm_staged<T, AV, BV, 1>, gemm_staged<T, AV, BV, 2>},
                    {gemm_staged<T, AV, BV, 0>, gemm_staged<T, AV, BV, 1>, gemm_staged<T, AV, BV, 2>}},
-                  false, false, false};
+                  false, false, false, 0};
 }
 
 template <class T>
@@ -129,7 +134,7 @@ Config direct_config(const char *name, int group_m)
                   T::LDS_BYTES, false, true, group_m,
                   {{gemm_direct<T, 0, false>, gemm_direct<T, 1, false>, gemm_direct<T, 2, false>},
                    {gemm_direct<T, 0, true>, gemm_direct<T, 1, true>, gemm_direct<T, 2, true>}},
-                  false, false, false};
+                  false, false, false, T::NL};
 }
 
 // Two groups of four waves taking turns; K % 8 == 0 only (no K-tail patch)
@@ -140,7 +145,7 @@ Config pingpong_config(const char *name, int group_m)
                   T::NT, T::LDS_BYTES, false, true, group_m,
                   {{gemm_pingpong<T, 0>, gemm_pingpong<T, 1>, gemm_pingpong<T, 2>},
                    {nullptr, nullptr, nullptr}},
-                  false, true, true};
+                  false, true, true, 0};
 }
 
 // Up to 8 columns; 4 waves per workgroup, KS of them splitting K for each 8-row group
@@ -152,7 +157,7 @@ Config narrow_config(const char *name)
                   KS > 1 ? (int)(T::NW * 64 * sizeof(float)) : 0, false, false, 1,
                   {{gemm_narrow<0, KS>, gemm_narrow<1, KS>, gemm_narrow<2, KS>},
                    {gemm_narrow<0, KS>, gemm_narrow<1, KS>, gemm_narrow<2, KS>}},
-                  true, false, false};
+                  true, false, false, 0};
 }
 
 const Config kConfigs[] = {
@@ -167,6 +172,8 @@ const Config kConfigs[] = {
     direct_config<D64x256>("d64x256x32_w1x4_s4", 8),
     direct_config<D64x128>("d64x128x32_w1x4_s4", 8),
     direct_config<D64x192>("d64x192x32_w2x2_s4", 8),
+    direct_config<D128L4>("d128x128x64_w2x2_l4_s4", 8),
+    direct_config<D64x192L4>("d64x192x32_w2x2_l4_s4", 8),
     pingpong_config<P256>("p256x256x32_w2x4_s4", 4),
     staged_config<T256, true, true>("s256x256x64_w2x2_av_bv", 8),
     staged_config<T128, true, true>("s128x128x64_w2x2_av_bv", 8),
@@ -263,12 +270,13 @@ int find_pingpong(int bm, int bn)
     return -1;
 }
 
-int find_direct(int bm, int bn, int bk, int waves, int k_groups)
+int find_direct(int bm, int bn, int bk, int waves, int k_groups, int loaders = 0)
 {
     for (int i = 0; i < kNumConfigs; ++i) {
         const Config &c = kConfigs[i];
         if (c.direct && !c.pingpong && c.bm == bm && c.bn == bn && c.bk == bk &&
-            c.waves_m * c.waves_n * c.k_groups == waves && c.k_groups == k_groups)
+            c.waves_m * c.waves_n * c.k_groups == waves && c.k_groups == k_groups &&
+            c.loaders == loaders)
             return i;
     }
     return -1;
@@ -320,9 +328,9 @@ int tuned_choice(const Request &r, bool av, bool bv)
 // where at most one wave of 128x128 tiles remains,
 // 64-row tiles (64x192 where a full wave of them fills the chip with K up to 1024, 64x256
 // for short K, 64x128 where 128x128 tiles would idle half the chip),
-// else 128x128 tiles: 4 waves when they fill the chip
-// with K below 4096, two k-groups for long K or with part of the chip idle (two waves per
-// SIMD hide each other's LDS reads and barrier waits).  The 4-wave tiles took over
+// else 128x128 tiles: 4 multiplying waves fed by 4 loader waves when they fill the chip,
+// two k-groups with part of the chip idle (two waves per SIMD hide each other's LDS reads
+// and barrier waits).  The 4-wave tiles took over
 // (256x256 at 8192^3) or kept (128x128 at 2048^3) their shapes once the copies lost their
 // vector instructions: with one wave per SIMD nothing else hid them.
 // The 256x256x64 tile took over one wave of big tiles from the 256x256x32 one once the
@@ -398,9 +406,12 @@ int choose(const Request &r)
         // tile.  From K = 2048 the k-group 128x128 tile leads (1000x3000x2048 + bias +
         // GELU 19.2 against 20.2), and 240 tiles were not enough (1280x2304x1024: 9.45
         // against 9.35).
+        // The 64x192 tile with 4 loader waves: 1000x3000x777 + bias + GELU 10.5 against
+        // 10.6 us without them, 1024x3072x768 + bias + GELU 9.1 against 9.4, 4096x768x1024
+        // 8.4 against 8.6.
         if (r.K <= 1024 && t128 <= kCUs && t64x192 <= kCUs && t64x192 >= kCUs - kCUs / 32 &&
             t64x192 > t64x256 && t64x192 < t64x128)
-            return find_direct(64, 192, 32, 4, 1);
+            return find_direct(64, 192, 32, 4, 1, 4);
         // at most one wave of 128x128 tiles with short K: 64x256 tiles (3000x1000x777: 11.6
         // us against 13.2 with 128x128x32; 2048x2048x777: 11.1-11.3 against 11.2-11.8; the
         // ragged 1000x3000x777, 192 tiles of either, 11.6 against 12.2 before the 64x192
@@ -417,8 +428,11 @@ int choose(const Request &r)
             return find_direct(64, 128, 32, 4, 1);
         // short K: 32-deep stages, so the ring fills and the last stage drains sooner
         if (t128 >= kCUs / 4 && r.K < 1024) return find_direct(128, 128, 32, 4, 1);
-        if (t128 >= kCUs) return r.K >= 4096 ? find_direct(128, 128, 64, 8, 2)   // long K: k-groups
-                                             : find_direct(128, 128, 64, 4, 1);
+        // one wave of 128x128 tiles or more: 4 multiplying waves fed by 4 loader waves
+        // (interleaved on three boxes: 2048^3 18.6-19.7 us against 19.2-20.3 for the same tile
+        // without them; 2048^3 + bias + GELU 21.2 against 21.6; 2048x2048x4096 33.0 against
+        // 33.9 and 34.1 with two k-groups; 2048x2048x8192 63.0 against 63.5 with two k-groups)
+        if (t128 >= kCUs) return find_direct(128, 128, 64, 4, 1, 4);
         if (t128 >= kCUs / 4) return find_direct(128, 128, 64, 8, 2);    // part of the chip idle
     }
     // at most 8 columns: no tile contraction left; the narrow kernel reads A once
@@ -743,6 +757,7 @@ mi355gemm_status mi355gemm_config_info(int config_id, mi355gemm_config_desc *out
     out->narrow = c.narrow;
     out->k_mult8 = c.k_mult8;
     out->pingpong = c.pingpong;
+    out->loader_waves = c.loaders;
     return MI355GEMM_OK;
 }
 

@@ -231,7 +231,8 @@ typedef struct {
     int stages;                     /* LDS buffers in the K pipeline */
     int waves_m, waves_n;           /* wavefront grid over the macro-tile */
     int k_groups;                   /* wave grids splitting each K step (summed at the end) */
-    int threads;                    /* threads per workgroup: 64 * waves_m * waves_n * k_groups */
+    int threads;                    /* threads per workgroup:
+                                       64 * (waves_m * waves_n * k_groups + loader_waves) */
     int lds_bytes;                  /* LDS the configuration occupies per workgroup */
     int a_vector;                   /* 1: A loaded in 16-byte vectors (needs K % 8 == 0) */
     int bc_vector;                  /* 1: B loaded and C stored in vectors (N % 8 == 0) */
@@ -245,6 +246,9 @@ typedef struct {
                                        multiplying while the other loads its next operands
                                        (k_groups 2: the groups take alternate K stages and
                                        sum at the end; 1: each group owns half the rows) */
+    int loader_waves;               /* direct kernel: extra waves that issue every HBM -> LDS
+                                       copy while the waves_m x waves_n grid only reads LDS
+                                       and multiplies (0: the multiplying waves copy too) */
 } mi355gemm_config_desc;
 
 /* Number of compiled configurations (ids 0 .. n-1). Host-only. */
@@ -252,11 +256,11 @@ int mi355gemm_num_configs(void);
 
 /* Static name of a configuration, or NULL for an unknown id.  Host-only.  Names read
  * <d|p|s|n><BM>x<BN>x<BK>_w<waves_m>x<waves_n>[k<k_groups>]_...: d = direct HBM -> LDS kernel
- * (suffix s<stages>), p = the same loader and tiles with two wave groups taking turns
+ * (suffix [l<loader_waves>_]s<stages>), p = the same loader and tiles with two wave groups taking turns
  * (ping-pong; suffix s<stages>), s = register-staged kernel (suffix av/an: A in 16-byte /
  * 2-byte loads, bv/bn: B and C likewise), n = narrow vector-ALU kernel for N <= 8 (any
- * alignment), e.g. "d128x128x64_w2x2_s4", "p256x256x32_w2x4_s4", "s64x64x64_w2x1_av_bv",
- * "n8x8x512_w1x1k4".  The tag mirrors the candidate tag of the tutorial's schedule sweep
+ * alignment), e.g. "d128x128x64_w2x2_s4", "d128x128x64_w2x2_l4_s4", "p256x256x32_w2x4_s4",
+ * "s64x64x64_w2x1_av_bv", "n8x8x512_w1x1k4".  The tag mirrors the candidate tag of the tutorial's schedule sweep
  * (thecryptopost.io page, section 3: block_M x block_N x block_K with stages and threads). */
 const char *mi355gemm_config_name(int config_id);
 

@@ -73,7 +73,14 @@ def test_config_table_is_consistent():
             # two LDS stages of BM and BN rows of BK halves plus a 16-byte pad per row
             assert c["lds_bytes"] == c["stages"] * (c["block_m"] + c["block_n"]) * (c["block_k"] + 8) * 2
         assert c["lds_bytes"] <= g.mi355gemm_lds_budget()
-        assert c["threads"] == 64 * c["waves_m"] * c["waves_n"] * c["k_groups"]
+        assert c["threads"] == 64 * (c["waves_m"] * c["waves_n"] * c["k_groups"] + c["loader_waves"])
+        # loader waves: direct kernel, one k-group, named d..._l<loaders>_s<stages>
+        assert c["loader_waves"] in (0, 4)
+        if c["loader_waves"]:
+            assert c["direct"] and not c["pingpong"] and c["k_groups"] == 1
+            assert "_l%d_s" % c["loader_waves"] in c["name"]
+        else:
+            assert "_l" not in c["name"]
         assert c["k_groups"] in (1, 2) and (c["direct"] or c["k_groups"] == 1)
         assert c["block_m"] % (32 * c["waves_m"]) == 0 and c["block_n"] % (32 * c["waves_n"]) == 0
         assert c["block_k"] % 16 == 0
@@ -339,9 +346,10 @@ def test_attention_argument_checks(args, want):
     ((4096, 4096, 4095), "d256x256x64_w2x4_s2"),
     ((8192, 1024, 8192), "d256x128x64_w2x2k2_s3"),    # one GPU's N share of 8192^3
     ((1024, 8192, 8192), "d256x128x64_w2x2k2_s3"),    # its M share
-    ((2048, 2048, 8192), "d128x128x64_w2x2k2_s4"),    # 256 tiles, long K
-    ((2048, 2048, 2048), "d128x128x64_w2x2_s4"),      # 256 tiles, K = 2048
-    ((2048, 2048, 1024), "d128x128x64_w2x2_s4"),      # 256 tiles, K = 1024
+    ((2048, 2048, 8192), "d128x128x64_w2x2_l4_s4"),   # 256 tiles: 4 loader waves feed the
+    ((2048, 2048, 4096), "d128x128x64_w2x2_l4_s4"),   # 4 multiplying ones
+    ((2048, 2048, 2048), "d128x128x64_w2x2_l4_s4"),
+    ((2048, 2048, 1024), "d128x128x64_w2x2_l4_s4"),
     ((2048, 2048, 777), "d64x256x32_w1x4_s4"),        # one wave of 128x128 tiles, K < 1024
     ((2048, 2048, 512), "d64x256x32_w1x4_s4"),
     ((3072, 2048, 512), "d128x128x32_w2x2_s4"),       # 1.5 waves of them, K < 1024
@@ -355,11 +363,11 @@ def test_attention_argument_checks(args, want):
     ((6144, 2048, 2048), "d256x256x32_w2x4_s4"),      # 192 of 256x256, not 384 of 256x128
     ((2304, 2304, 2304), "d256x128x64_w2x2k2_s3"),    # 162 of 256x128, not 324 of 128x128
     ((3072, 2048, 2048), "d256x128x64_w2x2k2_s3"),    # 192 of 256x128, not 384 of 128x128
-    ((1000, 3000, 777), "d64x192x32_w2x2_s4"),        # a full wave of 64x192 tiles (192 of
-    ((1000, 3000, 1024), "d64x192x32_w2x2_s4"),       # 64x256 or 128x128), K <= 1024
-    ((2048, 1536, 512), "d64x192x32_w2x2_s4"),
-    ((4096, 768, 1024), "d64x192x32_w2x2_s4"),
-    ((1024, 3072, 768), "d64x192x32_w2x2_s4"),
+    ((1000, 3000, 777), "d64x192x32_w2x2_l4_s4"),        # a full wave of 64x192 tiles (192 of
+    ((1000, 3000, 1024), "d64x192x32_w2x2_l4_s4"),       # 64x256 or 128x128), K <= 1024
+    ((2048, 1536, 512), "d64x192x32_w2x2_l4_s4"),
+    ((4096, 768, 1024), "d64x192x32_w2x2_l4_s4"),
+    ((1024, 3072, 768), "d64x192x32_w2x2_l4_s4"),
     ((1000, 3000, 2048), "d128x128x64_w2x2k2_s4"),    # the same tile counts, longer K
     ((1280, 2304, 1024), "d128x128x64_w2x2k2_s4"),    # 240 tiles of 64x192: not enough
     ((3000, 1000, 777), "d64x256x32_w1x4_s4"),        # 282 of 64x192: a second round
@@ -374,10 +382,10 @@ def test_selector_rules_pick_the_measured_winners(shape, want):
 
 
 @pytest.mark.parametrize("shape,ptr_off,want", [
-    ((2048, 2047, 2048), 0, "d128x128x64_w2x2_s4"),   # odd N: direct on the first 2040 columns
+    ((2048, 2047, 2048), 0, "d128x128x64_w2x2_l4_s4"),  # odd N: direct on the first 2040 columns
     ((8192, 8191, 8192), 0, "d256x256x32_w2x2_s4"),
-    ((1000, 3001, 777), 0, "d64x192x32_w2x2_s4"),
-    ((2048, 2048, 2048), 2, "d128x128x64_w2x2_s4"),   # B and C only 2-byte aligned
+    ((1000, 3001, 777), 0, "d64x192x32_w2x2_l4_s4"),
+    ((2048, 2048, 2048), 2, "d128x128x64_w2x2_l4_s4"),  # B and C only 2-byte aligned
     ((8192, 63, 8192), 0, "s64x64x64_w2x1_av_bn"),    # N < 64: no direct launch to split
     ((64, 775, 64), 0, "s64x64x64_w2x1_av_bn"),       # too few tiles (7 of 64x128)
     ((512, 1031, 64), 0, "d64x128x32_w1x4_s4"),       # 72 tiles of 64x128
@@ -417,13 +425,14 @@ def test_forced_narrow_config_rejects_more_than_8_columns():
 
 def test_installed_choice_overrides_the_selector_for_its_exact_key_only():
     k32, k64 = g.config_id("d128x128x32_w2x2_s4"), g.config_id("d128x128x64_w2x2_s4")
+    rule = g.config_id("d128x128x64_w2x2_l4_s4")
     g.clear_choices()
     try:
-        assert _select(2048, 2048, 2048) == k64                      # the rules
+        assert _select(2048, 2048, 2048) == rule                     # the rules
         g.set_choice(2048, 2048, 2048, "none", True, True, "d128x128x32_w2x2_s4")
         assert _select(2048, 2048, 2048) == k32
-        assert _select(2048, 2048, 2048, epi=2) == k64                # other epilogue
-        assert _select(2048, 2048, 2056) == k64                       # other shape
+        assert _select(2048, 2048, 2048, epi=2) == rule               # other epilogue
+        assert _select(2048, 2048, 2056) == rule                      # other shape
         assert _select(2048, 2048, 2048, A=P2) != k32                 # other A class
         g.set_choice(2048, 2048, 2048, "none", True, True, k64)       # same key: replaced
         assert _select(2048, 2048, 2048) == k64
@@ -432,10 +441,10 @@ def test_installed_choice_overrides_the_selector_for_its_exact_key_only():
         staged = g.config_id("s64x64x64_w2x1_an_bn")
         g.set_choice(1000, 3001, 777, "bias_gelu", False, False, staged)
         assert _select(1000, 3001, 777, epi=2) == staged
-        ragged = g.config_id("d64x192x32_w2x2_s4")
+        ragged = g.config_id("d64x192x32_w2x2_l4_s4")
         assert _select(1000, 3000, 777, epi=2) == ragged              # class 1: the rules
         g.clear_choices()
-        assert _select(2048, 2048, 2048) == k64
+        assert _select(2048, 2048, 2048) == rule
         assert _select(1000, 3001, 777, epi=2) == ragged
     finally:
         g.clear_choices()

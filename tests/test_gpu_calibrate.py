@@ -47,16 +47,18 @@ def test_calibrate_installs_a_family_member_and_the_call_uses_it(shape, epi):
 
 
 def test_calibrate_with_a_one_member_tile_area_installs_nothing():
-    """1000x3000x777 takes the 64x192 tile, the only configuration of its tile area: the
+    """256^3 takes the 64x128 tile, the only configuration of its tile area: the
     calibration has nothing to time, installs nothing, and the call still matches the
     oracle."""
-    M, N, K = 1000, 3000, 777
+    M, N, K = 256, 256, 256
     A, B, bias = workloads.make_inputs(M, N, K, "uniform", with_bias=True, seed=13)
     Ad, Bd, biasd = A.cuda(), B.cuda(), bias.cuda()
     rule = g.select(Ad, Bd, biasd, "bias_gelu")
-    assert g.mi355gemm_config_name(rule) == "d64x192x32_w2x2_s4"
+    assert g.mi355gemm_config_name(rule) == "d64x128x32_w1x4_s4"
+    assert [c["name"] for c in g.configs() if c["direct"] and c["block_m"] * c["block_n"] == 64 * 128] \
+        == ["d64x128x32_w1x4_s4"]
     name, med = tune.calibrate(Ad, Bd, biasd, "bias_gelu", ms=2.0, rounds=2, prewarm_ms=10.0)
-    assert name == "d64x192x32_w2x2_s4" and med == {}
+    assert name == "d64x128x32_w1x4_s4" and med == {}
     assert g.select(Ad, Bd, biasd, "bias_gelu") == rule
     got = g.gemm(Ad, Bd, biasd, "bias_gelu")
     torch.cuda.synchronize()

@@ -109,7 +109,7 @@ def test_members_cover_the_calibration_family():
     """The member list the full-size tests below walk is the selector's choice plus every
     direct configuration of its tile area (every workload's K is a multiple of 8, so the
     ping-pong kernel counts): several at 2048^3 and 8192^3, one where the area has a
-    single configuration (256^3 on 64x128, the ragged shape on 64x192)."""
+    single configuration (256^3 on 64x128)."""
     areas = {}
     for c in g.configs():
         if c["direct"]:
