@@ -38,6 +38,7 @@ using D64x128 = DTile<64, 128, 32, 1, 4, 1, 4>;     // 4 waves of 64x32, 40 KiB
 using D64x192 = DTile<64, 192, 32, 2, 2, 1, 4>;     // 4 waves of 32x96, 64 KiB
 using D128L4 = DTile<128, 128, 64, 2, 2, 1, 4, 1, 4>;   // 4 waves of 64x64 + 4 loader waves
 using D64x192L4 = DTile<64, 192, 32, 2, 2, 1, 4, 1, 4>; // 4 waves of 32x96 + 4 loader waves
+using D128k32L4 = DTile<128, 128, 32, 2, 2, 1, 4, 1, 4>; // the same on a 64 KiB ring
 // ping-pong tile: BM, BN, BK, waves of a group (M x N), stages
 using P256 = PTile<256, 256, 32, 1, 4, 4>;          // 2 groups x 4 waves of 128x64, 128 KiB
 // attention: head dim, keys per block, waves (32 query rows each), LDS stages
@@ -70,6 +71,7 @@ MI355_DIRECT(D64x128)
 MI355_DIRECT(D64x192)
 MI355_DIRECT(D128L4)
 MI355_DIRECT(D64x192L4)
+MI355_DIRECT(D128k32L4)
 #undef MI355_DIRECT
 #define MI355_PINGPONG(T)                                     \
     template __global__ void gemm_pingpong<T, 0>(GemmArgs);   \
@@ -174,6 +176,7 @@ const Config kConfigs[] = {
     direct_config<D64x192>("d64x192x32_w2x2_s4", 8),
     direct_config<D128L4>("d128x128x64_w2x2_l4_s4", 8),
     direct_config<D64x192L4>("d64x192x32_w2x2_l4_s4", 8),
+    direct_config<D128k32L4>("d128x128x32_w2x2_l4_s4", 8),
     pingpong_config<P256>("p256x256x32_w2x4_s4", 4),
     staged_config<T256, true, true>("s256x256x64_w2x2_av_bv", 8),
     staged_config<T128, true, true>("s128x128x64_w2x2_av_bv", 8),
@@ -429,10 +432,17 @@ int choose(const Request &r)
         // short K: 32-deep stages, so the ring fills and the last stage drains sooner
         if (t128 >= kCUs / 4 && r.K < 1024) return find_direct(128, 128, 32, 4, 1);
         // one wave of 128x128 tiles or more: 4 multiplying waves fed by 4 loader waves
-        // (interleaved on three boxes: 2048^3 18.6-19.7 us against 19.2-20.3 for the same tile
-        // without them; 2048^3 + bias + GELU 21.2 against 21.6; 2048x2048x4096 33.0 against
-        // 33.9 and 34.1 with two k-groups; 2048x2048x8192 63.0 against 63.5 with two k-groups)
-        if (t128 >= kCUs) return find_direct(128, 128, 64, 4, 1, 4);
+        // (interleaved: 2048^3 18.5-19.7 us against 19.2-20.3 for the same tile without them;
+        // 2048x2048x4096 32.6-34.9 against 33.4-35.7, and 33.7-35.8 with two k-groups;
+        // 2048x2048x8192 63.0 against 63.5 with two k-groups).  On some boxes the 64-deep
+        // tiles on their 128 KiB ring run slow, and the 32-deep one on a 64 KiB ring does
+        // not: 2048^3 19.6-20.6 us against 21.5-23.3, with bias + GELU 22.0-22.7 against
+        // 24.7-28.5, where on the others it trails by 7% (19.7 against 18.5) and 2.5% with
+        // GELU.  Below K = 4096 the rules take the 32-deep tile, which is never far from
+        // the best; from K = 4096 the 64-deep one leads on both kinds of box (34.9 against
+        // 37.9 and 32.6 against 36.1).  Calibration picks per box between them.
+        if (t128 >= kCUs) return r.K >= 4096 ? find_direct(128, 128, 64, 4, 1, 4)
+                                             : find_direct(128, 128, 32, 4, 1, 4);
         if (t128 >= kCUs / 4) return find_direct(128, 128, 64, 8, 2);    // part of the chip idle
     }
     // at most 8 columns: no tile contraction left; the narrow kernel reads A once

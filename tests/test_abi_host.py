@@ -347,9 +347,9 @@ def test_attention_argument_checks(args, want):
     ((8192, 1024, 8192), "d256x128x64_w2x2k2_s3"),    # one GPU's N share of 8192^3
     ((1024, 8192, 8192), "d256x128x64_w2x2k2_s3"),    # its M share
     ((2048, 2048, 8192), "d128x128x64_w2x2_l4_s4"),   # 256 tiles: 4 loader waves feed the
-    ((2048, 2048, 4096), "d128x128x64_w2x2_l4_s4"),   # 4 multiplying ones
-    ((2048, 2048, 2048), "d128x128x64_w2x2_l4_s4"),
-    ((2048, 2048, 1024), "d128x128x64_w2x2_l4_s4"),
+    ((2048, 2048, 4096), "d128x128x64_w2x2_l4_s4"),   # 4 multiplying ones; 64-deep stages
+    ((2048, 2048, 2048), "d128x128x32_w2x2_l4_s4"),   # from K = 4096, 32-deep below
+    ((2048, 2048, 1024), "d128x128x32_w2x2_l4_s4"),
     ((2048, 2048, 777), "d64x256x32_w1x4_s4"),        # one wave of 128x128 tiles, K < 1024
     ((2048, 2048, 512), "d64x256x32_w1x4_s4"),
     ((3072, 2048, 512), "d128x128x32_w2x2_s4"),       # 1.5 waves of them, K < 1024
@@ -382,10 +382,10 @@ def test_selector_rules_pick_the_measured_winners(shape, want):
 
 
 @pytest.mark.parametrize("shape,ptr_off,want", [
-    ((2048, 2047, 2048), 0, "d128x128x64_w2x2_l4_s4"),  # odd N: direct on the first 2040 columns
+    ((2048, 2047, 2048), 0, "d128x128x32_w2x2_l4_s4"),  # odd N: direct on the first 2040 columns
     ((8192, 8191, 8192), 0, "d256x256x32_w2x2_s4"),
     ((1000, 3001, 777), 0, "d64x192x32_w2x2_l4_s4"),
-    ((2048, 2048, 2048), 2, "d128x128x64_w2x2_l4_s4"),  # B and C only 2-byte aligned
+    ((2048, 2048, 2048), 2, "d128x128x32_w2x2_l4_s4"),  # B and C only 2-byte aligned
     ((8192, 63, 8192), 0, "s64x64x64_w2x1_av_bn"),    # N < 64: no direct launch to split
     ((64, 775, 64), 0, "s64x64x64_w2x1_av_bn"),       # too few tiles (7 of 64x128)
     ((512, 1031, 64), 0, "d64x128x32_w1x4_s4"),       # 72 tiles of 64x128
@@ -425,7 +425,7 @@ def test_forced_narrow_config_rejects_more_than_8_columns():
 
 def test_installed_choice_overrides_the_selector_for_its_exact_key_only():
     k32, k64 = g.config_id("d128x128x32_w2x2_s4"), g.config_id("d128x128x64_w2x2_s4")
-    rule = g.config_id("d128x128x64_w2x2_l4_s4")
+    rule = g.config_id("d128x128x32_w2x2_l4_s4")
     g.clear_choices()
     try:
         assert _select(2048, 2048, 2048) == rule                     # the rules

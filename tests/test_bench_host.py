@@ -66,7 +66,8 @@ def test_traffic_lookup_covers_the_calibration_family_only_for_the_measured_code
     import bench
     h = bench.kernel_sources_hash()
     for name in ("d128x128x64_w2x2_s4", "d128x128x32_w2x2_s4", "d128x128x64_w2x2k2_s4",
-                 "d128x128x64_w2x4_s4", "d64x256x32_w1x4_s4", "d128x128x64_w2x2_l4_s4"):
+                 "d128x128x64_w2x4_s4", "d64x256x32_w1x4_s4", "d128x128x64_w2x2_l4_s4",
+                 "d128x128x32_w2x2_l4_s4"):
         got = bench.traffic_for(name)
         measured = (bench.TRAFFIC["sources_sha256_16"] == h if name == bench.TRAFFIC["kernel_config"]
                     else bench.TRAFFIC_OTHER["sources_sha256_16"] == h)
