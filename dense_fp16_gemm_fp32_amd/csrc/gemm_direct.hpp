@@ -597,8 +597,10 @@ __global__ void __launch_bounds__(T::NT) gemm_direct(GemmArgs p)
             if constexpr (q == T::QB) {
                 // stage kt+1 has landed once at most the copies issued after it are in
                 // flight (stages kt+2 .. kt+STAGES-2 and the early part of kt+STAGES-1);
-                // this wave's reads of stage kt-1 were issued before the barrier
-                wait_counts<T::VM_WAIT, 15>();
+                // and this wave's LDS reads have completed: every read of stage kt's slot
+                // is issued before this barrier, and the copy that refills the slot only
+                // after the next one, so no copy can overtake a read still queued
+                wait_counts<T::VM_WAIT, 0>();
                 if (k_tail && kt + 1 == nk - 1) w.patch_tail(nxt);
                 workgroup_barrier();
             }
@@ -637,9 +639,10 @@ __global__ void __launch_bounds__(T::NT) gemm_direct(GemmArgs p)
     // copy waits, and the loader waves run their own loop, which crosses the same
     // barriers in the same order (the prologue's, then one per stage).  Before the
     // barrier of stage kt's k-step QB (the one after which stage kt+1 is read) a loader
-    // wave waits for its copies of stage kt+1; after it, it issues the copy of stage
-    // kt+STAGES into the slot of stage kt, whose reads were all issued before that
-    // barrier -- the order the multiplying waves keep themselves without loader waves.
+    // wave waits for its copies of stage kt+1 and every multiplying wave for its LDS
+    // reads, all of stage kt's slot among them; after it, the loader issues the copy of
+    // stage kt+STAGES into that slot -- the order the multiplying waves keep themselves
+    // without loader waves.
     auto mult_stage = [&](auto Jc, int kt) {
         constexpr int J = decltype(Jc)::value;
         St &cur = ring[J];
@@ -650,7 +653,13 @@ __global__ void __launch_bounds__(T::NT) gemm_direct(GemmArgs p)
             constexpr int rbuf = (J * T::Q + q + T::PF) % T::NBUF;
             constexpr bool ahead = q + T::PF >= T::Q;
             constexpr int rq = (q + T::PF) % T::Q;
-            if constexpr (q == T::QB) workgroup_barrier();   // stage kt+1 has landed
+            if constexpr (q == T::QB) {
+                // this wave's reads of stage kt's slot have completed before the loader
+                // waves, past the barrier, issue the copy that refills it; stage kt+1 has
+                // landed once the barrier is crossed
+                wait_counts<63, 0>();
+                workgroup_barrier();
+            }
             static_for<T::NMFMA>([&](auto mc) {
                 constexpr int m = decltype(mc)::value;
                 w.mfma_one(buf, m);
