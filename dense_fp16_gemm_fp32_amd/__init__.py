@@ -44,7 +44,7 @@ class ConfigDesc(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int) for n in (
         "block_m", "block_n", "block_k", "stages", "waves_m", "waves_n", "k_groups", "threads",
         "lds_bytes", "a_vector", "bc_vector", "group_m", "direct", "narrow", "k_mult8",
-        "pingpong", "loader_waves")]
+        "pingpong", "loader_waves", "mfma_block")]
 
     def as_dict(self) -> dict:
         return {n: getattr(self, n) for n, _ in self._fields_}

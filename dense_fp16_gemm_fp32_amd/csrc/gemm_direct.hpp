@@ -46,8 +46,11 @@ namespace mi355 {
 // LOADERS: 0, or the number of extra wavefronts that issue every HBM -> LDS copy while the
 // NW multiplying waves only read LDS and issue MFMAs (the loader waves share the SIMDs
 // with them, one more wave per SIMD for LOADERS = 4).
+// MF: the MFMA block, 32 (v_mfma_f32_32x32x16_f16, 16-deep k-steps) or 16
+// (v_mfma_f32_16x16x32_f16, 32-deep k-steps: wave tiles in multiples of 16, so four waves
+// can split 192 columns into 48 each and read every B fragment once).
 template <int BM_, int BN_, int BK_, int WAVES_M_, int WAVES_N_, int KGROUPS_, int STAGES_,
-          int PF_ = 1, int LOADERS_ = 0>
+          int PF_ = 1, int LOADERS_ = 0, int MF_ = 32>
 struct DTile {
     static constexpr int BM = BM_, BN = BN_, BK = BK_;
     static constexpr int WAVES_M = WAVES_M_, WAVES_N = WAVES_N_;
@@ -59,10 +62,15 @@ struct DTile {
     static constexpr int NTC = 64 * NW;              // threads of the multiplying waves
     static constexpr int NT = 64 * (NW + NL);
     static constexpr int WTM = BM / WAVES_M, WTN = BN / WAVES_N;
-    static constexpr int FM = WTM / 32, FN = WTN / 32;
+    static constexpr int MF = MF_;                   // MFMA block edge
+    static constexpr int KS = MF == 32 ? 16 : 32;    // depth of one MFMA k-step
+    static constexpr int NG = MF == 32 ? 4 : 1;      // 4-column register quads per block and lane
+    static constexpr int MFS = MF == 32 ? 5 : 4;     // log2(MF)
+    using AccT = std::conditional_t<MF == 32, f32x16, f32x4>;
+    static constexpr int FM = WTM / MF, FN = WTN / MF;
     static constexpr int NMFMA = FM * FN;            // MFMAs per k-step per wave
     static constexpr int NREAD = FM + 2 * FN;        // LDS reads per k-step per wave
-    static constexpr int KK = BK / 16;               // 16-deep k-steps per stage
+    static constexpr int KK = BK / KS;               // k-steps per stage
     static constexpr int Q = KK / KGROUPS;           // k-steps per stage per wave
     static constexpr int CA = BK / 8;                // 16-byte chunks per A row
     static constexpr int CB = BN / 8;                // 16-byte chunks per B row
@@ -88,8 +96,11 @@ struct DTile {
     // k-group exchange at the end: every wave hands half of its 32x32 fp32 blocks (4 KiB
     // each) to its partner in the other group
     static constexpr int RED_BYTES = KGROUPS > 1 ? NW * (NMFMA / 2) * 4096 : 0;
-    static_assert(WTM % 32 == 0 && WTN % 32 == 0, "wave tile must be whole 32x32 blocks");
+    static_assert(MF == 32 || MF == 16, "MFMA blocks of 32x32 or 16x16");
+    static_assert(WTM % MF == 0 && WTN % MF == 0, "wave tile must be whole MFMA blocks");
     static_assert(BK == 32 || BK == 64, "A swizzle assumes 4 or 8 chunks per row");
+    static_assert(BK % KS == 0, "stage of whole k-steps");
+    static_assert(MF == 32 || KGROUPS == 1, "k-group exchange written for 32x32 blocks");
     static_assert(CB % 8 == 0, "B swizzle assumes rows of a multiple of 128 bytes");
     static_assert(A_BYTES % (1024 * NI) == 0 && B_BYTES % (1024 * NI) == 0,
                   "stage must split into whole 1 KiB loads per wave");
@@ -114,10 +125,14 @@ struct __attribute__((aligned(16))) Stage {
 
 // A chunk swizzle: rows of CA chunks; 16 B units within 256 B are (row % RP, chunk), so
 // XOR the chunk with (row / RP) % CA to spread 16 consecutive rows over all 16 units.
+// With 16x16 MFMA blocks a read covers 16 rows x 4 chunks instead of 32 rows x 2, and on
+// 64-byte rows (CA = 4) the rows are taken two at a time: (row / 2) % 4.  Measured with
+// rocprofv3's SQ_LDS_BANK_CONFLICT on those reads: 4 conflict cycles per instruction with
+// (row / 4) % 4, none with (row / 2) % 4; on 128-byte rows (row / 2) % 8 has none either way.
 template <class T>
 __device__ __forceinline__ int swz_a(int row)
 {
-    constexpr int RP = 16 / T::CA;
+    constexpr int RP = (T::MF == 16 && T::CA == 4) ? 2 : 16 / T::CA;
     return (row / RP) % T::CA;
 }
 
@@ -128,11 +143,14 @@ __device__ __forceinline__ int swz_a(int row)
 //   CB % 16 == 8 -- rows alternate between groups 0 and 8, so only rows k and k + 2
 //                   collide: XOR bit 2 of the chunk with bit 1 of k.  The chunk stays in
 //                   its aligned group of 8, which a row of CB chunks holds whole.
-template <int CB = 16>
+// With 16x16 MFMA blocks (MF = 16) the lanes of one read are four 16-lane groups on k-rows
+// 8 apart (each 4 rows x 2 chunks), and groups 8 rows apart would meet in the same bank
+// groups: bit 1 of the chunk is XORed with bit 3 of k as well.
+template <int CB = 16, int MF = 32>
 __device__ __forceinline__ int swz_b(int k)
 {
     static_assert(CB % 8 == 0, "B rows of a multiple of 128 bytes");
-    return CB % 16 == 0 ? 4 * (k & 3) : 4 * ((k >> 1) & 1);
+    return (CB % 16 == 0 ? 4 * (k & 3) : 4 * ((k >> 1) & 1)) ^ (MF == 16 ? 2 * ((k >> 3) & 1) : 0);
 }
 
 // s_waitcnt immediates for gfx9: vmcnt bits [3:0] and [15:14], expcnt [6:4], lgkmcnt [11:8].
@@ -210,8 +228,8 @@ struct DirectWave {
                               // one half per register: packed only when patched, so the
                               // loads stay in flight until then
     uint32_t tail_mask;       // bit g: piece g of the last stage straddles K
-    u32x2 bias_raw[T::FN][4]; // bias of this lane's accumulator columns (bias epilogues)
-    f32x16 acc[T::FM][T::FN];
+    u32x2 bias_raw[T::FN][T::NG]; // bias of this lane's accumulator columns (bias epilogues)
+    typename T::AccT acc[T::FM][T::FN];
     f16x8 af[T::NBUF][T::FM];
     s16x4 bl[T::NBUF][T::FN], bh[T::NBUF][T::FN];
 
@@ -247,40 +265,45 @@ struct DirectWave {
         for (int g = 0; g < T::GB; ++g) {
             const int s = (g * T::NI + issuer) * 64 + lane;
             const int row = s / T::CB;
-            const int c = (s % T::CB) ^ swz_b<T::CB>(row);
+            const int c = (s % T::CB) ^ swz_b<T::CB, T::MF>(row);
             b_off[g] = masked_offset((uint32_t)(row * ldb + 8 * c) * 2u, 8 * c < cols_valid);
         }
-        // A fragment: row wm*WTM + i*32 + r32, logical chunk 2*kk + h -> physical chunk
-        // ^ swz_a(row); swz_a depends on the row only through r32 (WTM and 32 are
+        // Operand lane map of both MFMA shapes: lane l holds the 8 k-values 8 * (l / MF) ..
+        // +7 of the k-step for row (A) or column (B) l % MF of the block.
+        // A fragment: row wm*WTM + i*MF + rlo, logical chunk (KS/8)*kk + kgrp -> physical
+        // chunk ^ swz_a(row); swz_a depends on the row only through rlo (WTM and MF are
         // multiples of 16 * rows-per-256-bytes).  This wave's k-steps are kk = kg +
         // KGROUPS * q.
-        const int h = lane >> 5;
-        const int r32 = lane & 31;
-        const int sa = swz_a<T>(r32);
+        const int kgrp = lane >> T::MFS;
+        const int rlo = lane & (T::MF - 1);
+        const int sa = swz_a<T>(rlo);
 #pragma unroll
-        for (int i = 0; i < T::FM; ++i) a_row_byte[i] = (wm * T::WTM + i * 32 + r32) * T::BK * 2;
+        for (int i = 0; i < T::FM; ++i) a_row_byte[i] = (wm * T::WTM + i * T::MF + rlo) * T::BK * 2;
 #pragma unroll
         for (int q = 0; q < T::Q; ++q) {
             const int kk = kg + T::KGROUPS * q;
-            a_chunk_byte[q] = ((2 * kk + h) ^ sa) * 16;
-            b_k_byte[q] = (16 * kk) * T::BN * 2;
+            a_chunk_byte[q] = (((T::KS / 8) * kk + kgrp) ^ sa) * 16;
+            b_k_byte[q] = (T::KS * kk) * T::BN * 2;
         }
         // B fragment (transposing read): lane i of each 16-lane group points at k-row i/4
-        // of its group's 4-row band and columns 4*(i%4) .. +3 of its 16-column half; lane j
-        // then receives B[band + 0..3][half + j].  Band = 16*kk + 8*h + 4*t, t = 0 or 1.
+        // of its group's 4-row band and columns 4*(i%4) .. +3 of its 16 columns; lane j
+        // then receives B[band + 0..3][col + j].  Band = KS*kk + 8*kgrp + 4*t, t = 0 or 1;
+        // the 16 columns are the block's (MF = 16) or its half (lane / 16) % 2 (MF = 32).
         const int i16 = lane & 15;
-        const int sb = swz_b<T::CB>(i16 >> 2);
+        // the k-row of this lane: 8 * kgrp + i16 / 4 (+ KS * kk + 4 t, multiples of 8 and 4);
+        // for MF = 32 the swizzle reads only its two low bits
+        const int sb = swz_b<T::CB, T::MF>(T::MF == 32 ? (i16 >> 2) : 8 * kgrp + (i16 >> 2));
 #pragma unroll
         for (int j = 0; j < T::FN; ++j) {
-            const int n = wn * T::WTN + j * 32 + 16 * ((lane >> 4) & 1) + 4 * (i16 & 3);
+            const int n = wn * T::WTN + j * T::MF + (T::MF == 32 ? 16 * ((lane >> 4) & 1) : 0) + 4 * (i16 & 3);
             b_col_byte[j] = (((n >> 3) ^ sb) * 16) + 8 * ((n >> 2) & 1);
         }
-        b_row_byte = (8 * h + (i16 >> 2)) * T::BN * 2;
+        b_row_byte = (8 * kgrp + (i16 >> 2)) * T::BN * 2;
 #pragma unroll
         for (int i = 0; i < T::FM; ++i)
 #pragma unroll
             for (int j = 0; j < T::FN; ++j)
-                acc[i][j] = f32x16{};
+                acc[i][j] = typename T::AccT{};
     }
 
     // The bias values this lane's accumulator columns need, loaded at the start so the
@@ -288,12 +311,12 @@ struct DirectWave {
     __device__ __forceinline__ void load_bias(const GemmArgs &p)
     {
         const __amdgpu_buffer_rsrc_t b_rs = make_rsrc(p.bias + n0, (uint32_t)(N - n0) * 2u);
-        const int half = lane >> 5;
+        const int kgrp = lane >> T::MFS;
 #pragma unroll
         for (int j = 0; j < T::FN; ++j)
 #pragma unroll
-            for (int g = 0; g < 4; ++g) {
-                const int n = wn * T::WTN + j * 32 + 8 * g + 4 * half;
+            for (int g = 0; g < T::NG; ++g) {
+                const int n = wn * T::WTN + j * T::MF + 8 * g + 4 * kgrp;
                 bias_raw[j][g] = __builtin_amdgcn_raw_buffer_load_b64(b_rs, (uint32_t)n * 2u, 0, 0);
             }
     }
@@ -411,7 +434,10 @@ struct DirectWave {
         const int i = m / T::FN, j = m % T::FN;
         const f16x8 b = __builtin_bit_cast(
             f16x8, __builtin_shufflevector(bl[buf][j], bh[buf][j], 0, 1, 2, 3, 4, 5, 6, 7));
-        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(b, af[buf][i], acc[i][j], 0, 0, 0);
+        if constexpr (T::MF == 32)
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(b, af[buf][i], acc[i][j], 0, 0, 0);
+        else
+            acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(b, af[buf][i], acc[i][j], 0, 0, 0);
     }
 };
 
@@ -442,21 +468,22 @@ __device__ __forceinline__ int c_phys(int c, int r)
 
 // Bias, GELU and fp16 rounding of accumulator block rows I0 <= i < I1 of this wave,
 // written into the LDS copy of the tile.  Accumulator layout of v_mfma_f32_32x32x16_f16
-// with the B fragment as the first operand: register r of lane l holds
-// C[32 i + l % 32][32 j + 8 (r / 4) + 4 (l / 32) + r % 4] of the wave's sub-tile.
-// bias_raw[j][g] holds the four bias values of this lane's columns in register quad g of
-// block column j (loaded by DirectWave::load_bias at the start of the kernel).
+// and v_mfma_f32_16x16x32_f16 (MF = 32, 16) with the B fragment as the first operand:
+// register 4 g + e of lane l holds C[MF i + l % MF][MF j + 8 g + 4 (l / MF) + e] of the
+// wave's sub-tile (g < 4 for MF = 32, g = 0 for MF = 16).  bias_raw[j][g] holds the four
+// bias values of this lane's columns in register quad g of block column j (loaded by
+// DirectWave::load_bias at the start of the kernel).
 template <class T, int I0, int I1, int EPI>
-__device__ __forceinline__ void tile_to_lds(const f32x16 (&acc)[T::FM][T::FN],
-                                            const u32x2 (&bias_raw)[T::FN][4], int row0,
+__device__ __forceinline__ void tile_to_lds(const typename T::AccT (&acc)[T::FM][T::FN],
+                                            const u32x2 (&bias_raw)[T::FN][T::NG], int row0,
                                             int col0, int lane, char *ctile)
 {
-    const int half = lane >> 5;
+    const int half = lane >> T::MFS;   // the k-group of the operand map: 4-column offset
 #pragma unroll
     for (int j = 0; j < T::FN; ++j) {
 #pragma unroll
-        for (int g = 0; g < 4; ++g) {
-            const int n = col0 + j * 32 + 8 * g + 4 * half;   // first of 4 columns, tile-relative
+        for (int g = 0; g < T::NG; ++g) {
+            const int n = col0 + j * T::MF + 8 * g + 4 * half;   // first of 4 columns, tile-relative
             float bv[4] = {0.f, 0.f, 0.f, 0.f};
             if constexpr (EPI != 0) {
                 const f16x4 h = __builtin_bit_cast(f16x4, bias_raw[j][g]);
@@ -466,14 +493,16 @@ __device__ __forceinline__ void tile_to_lds(const f32x16 (&acc)[T::FM][T::FN],
             const int c = n >> 3;
 #pragma unroll
             for (int i = I0; i < I1; ++i) {
-                const int r = row0 + i * 32 + (lane & 31);
+                const int r = row0 + i * T::MF + (lane & (T::MF - 1));
                 uint32_t hb[4];
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
                     const f16 h = (f16)epilogue_op<EPI>(acc[i][j][4 * g + e], bv[e]);
                     hb[e] = __builtin_bit_cast(uint16_t, h);
                 }
-                char *dst = ctile + (r * T::BN + 8 * c_phys<T>(c, r) + 4 * half) * 2;
+                // the 4 columns' place in their 16-byte chunk: bit 2 of n (= half for MF = 32)
+                const int sub = T::MF == 32 ? 4 * half : (n & 4);
+                char *dst = ctile + (r * T::BN + 8 * c_phys<T>(c, r) + sub) * 2;
                 *reinterpret_cast<u32x2 *>(dst) = u32x2{hb[0] | (hb[1] << 16), hb[2] | (hb[3] << 16)};
             }
         }

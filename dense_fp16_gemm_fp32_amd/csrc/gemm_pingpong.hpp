@@ -43,6 +43,8 @@ struct PTile {
     static constexpr int STAGES = STAGES_;
     static constexpr int NW = 8, NT = 512, NWG = 4;  // waves, threads, waves per group
     static constexpr int NL = 0, NTC = NT;           // no loader waves: every thread stores C
+    static constexpr int MF = 32, NG = 4, MFS = 5;   // 32x32 MFMA blocks, 4 register quads
+    using AccT = f32x16;
     static constexpr int ROWS_G = BM / 2;            // rows one group computes
     static constexpr int WTM = ROWS_G / WM, WTN = BN / WN;
     static constexpr int FM = WTM / 32, FN = WTN / 32;

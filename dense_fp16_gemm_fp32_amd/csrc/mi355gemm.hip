@@ -39,6 +39,8 @@ using D64x192 = DTile<64, 192, 32, 2, 2, 1, 4>;     // 4 waves of 32x96, 64 KiB
 using D128L4 = DTile<128, 128, 64, 2, 2, 1, 4, 1, 4>;   // 4 waves of 64x64 + 4 loader waves
 using D64x192L4 = DTile<64, 192, 32, 2, 2, 1, 4, 1, 4>; // 4 waves of 32x96 + 4 loader waves
 using D128k32L4 = DTile<128, 128, 32, 2, 2, 1, 4, 1, 4>; // the same on a 64 KiB ring
+using D64x192FL4 = DTile<64, 192, 32, 1, 4, 1, 4, 1, 4, 16>;  // 4 waves of 64x48 (16x16 blocks) + 4 loaders
+using D64x192FbL4 = DTile<64, 192, 64, 1, 4, 1, 3, 1, 4, 16>; // the same on 64-deep stages, 96 KiB
 // ping-pong tile: BM, BN, BK, waves of a group (M x N), stages
 using P256 = PTile<256, 256, 32, 1, 4, 4>;          // 2 groups x 4 waves of 128x64, 128 KiB
 // attention: head dim, keys per block, waves (32 query rows each), LDS stages
@@ -72,6 +74,8 @@ MI355_DIRECT(D64x192)
 MI355_DIRECT(D128L4)
 MI355_DIRECT(D64x192L4)
 MI355_DIRECT(D128k32L4)
+MI355_DIRECT(D64x192FL4)
+MI355_DIRECT(D64x192FbL4)
 #undef MI355_DIRECT
 #define MI355_PINGPONG(T)                                     \
     template __global__ void gemm_pingpong<T, 0>(GemmArgs);   \
@@ -116,6 +120,7 @@ struct Config {
     bool k_mult8;     // needs K % 8 == 0 (no kernel for the K-tail case)
     bool pingpong;    // two wave groups taking turns
     int loaders;      // extra waves issuing every HBM -> LDS copy (direct kernel), else 0
+    int mfma_block;   // MFMA block edge: 32 (32x32x16) or 16 (16x16x32); 0 for the narrow kernel
 };
 
 template <class T, bool AV, bool BV>
@@ -125,7 +130,7 @@ Config staged_config(const char *name, int group_m)
                   T::LDS_BYTES, AV, BV, group_m,
                   {{gemm_staged<T, AV, BV, 0>, gemm_staged<T, AV, BV, 1>, gemm_staged<T, AV, BV, 2>},
                    {gemm_staged<T, AV, BV, 0>, gemm_staged<T, AV, BV, 1>, gemm_staged<T, AV, BV, 2>}},
-                  false, false, false, 0};
+                  false, false, false, 0, 32};
 }
 
 template <class T>
@@ -136,7 +141,7 @@ Config direct_config(const char *name, int group_m)
                   T::LDS_BYTES, false, true, group_m,
                   {{gemm_direct<T, 0, false>, gemm_direct<T, 1, false>, gemm_direct<T, 2, false>},
                    {gemm_direct<T, 0, true>, gemm_direct<T, 1, true>, gemm_direct<T, 2, true>}},
-                  false, false, false, T::NL};
+                  false, false, false, T::NL, T::MF};
 }
 
 // Two groups of four waves taking turns; K % 8 == 0 only (no K-tail patch)
@@ -147,7 +152,7 @@ Config pingpong_config(const char *name, int group_m)
                   T::NT, T::LDS_BYTES, false, true, group_m,
                   {{gemm_pingpong<T, 0>, gemm_pingpong<T, 1>, gemm_pingpong<T, 2>},
                    {nullptr, nullptr, nullptr}},
-                  false, true, true, 0};
+                  false, true, true, 0, 32};
 }
 
 // Up to 8 columns; 4 waves per workgroup, KS of them splitting K for each 8-row group
@@ -159,7 +164,7 @@ Config narrow_config(const char *name)
                   KS > 1 ? (int)(T::NW * 64 * sizeof(float)) : 0, false, false, 1,
                   {{gemm_narrow<0, KS>, gemm_narrow<1, KS>, gemm_narrow<2, KS>},
                    {gemm_narrow<0, KS>, gemm_narrow<1, KS>, gemm_narrow<2, KS>}},
-                  true, false, false, 0};
+                  true, false, false, 0, 0};
 }
 
 const Config kConfigs[] = {
@@ -177,6 +182,8 @@ const Config kConfigs[] = {
     direct_config<D128L4>("d128x128x64_w2x2_l4_s4", 8),
     direct_config<D64x192L4>("d64x192x32_w2x2_l4_s4", 8),
     direct_config<D128k32L4>("d128x128x32_w2x2_l4_s4", 8),
+    direct_config<D64x192FL4>("d64x192x32_w1x4_l4_s4_mf16", 8),
+    direct_config<D64x192FbL4>("d64x192x64_w1x4_l4_s3_mf16", 8),
     pingpong_config<P256>("p256x256x32_w2x4_s4", 4),
     staged_config<T256, true, true>("s256x256x64_w2x2_av_bv", 8),
     staged_config<T128, true, true>("s128x128x64_w2x2_av_bv", 8),
@@ -273,13 +280,13 @@ int find_pingpong(int bm, int bn)
     return -1;
 }
 
-int find_direct(int bm, int bn, int bk, int waves, int k_groups, int loaders = 0)
+int find_direct(int bm, int bn, int bk, int waves, int k_groups, int loaders = 0, int mfma = 32)
 {
     for (int i = 0; i < kNumConfigs; ++i) {
         const Config &c = kConfigs[i];
         if (c.direct && !c.pingpong && c.bm == bm && c.bn == bn && c.bk == bk &&
             c.waves_m * c.waves_n * c.k_groups == waves && c.k_groups == k_groups &&
-            c.loaders == loaders)
+            c.loaders == loaders && c.mfma_block == mfma)
             return i;
     }
     return -1;
@@ -329,7 +336,7 @@ int tuned_choice(const Request &r, bool av, bool bv)
 // one round, 256x128 tiles with two k-groups where they fill exactly one or where 128x128
 // tiles would need a partial second round;
 // where at most one wave of 128x128 tiles remains,
-// 64-row tiles (64x192 where a full wave of them fills the chip with K up to 1024, 64x256
+// 64-row tiles (64x192 where a full wave of them fills the chip with K up to 2048, 64x256
 // for short K, 64x128 where 128x128 tiles would idle half the chip),
 // else 128x128 tiles: 4 multiplying waves fed by 4 loader waves when they fill the chip,
 // two k-groups with part of the chip idle (two waves per SIMD hide each other's LDS reads
@@ -401,20 +408,22 @@ int choose(const Request &r)
         if (t256x128 == kCUs || (t128 > kCUs && r.K >= 1024)) return find_direct(256, 128, 64, 8, 2);
         const int64_t t64x256 = tiles(r, 64, 256), t64x128 = tiles(r, 64, 128),
                       t64x192 = tiles(r, 64, 192);
-        // K up to 1024 and a full wave of 64x192 tiles (at most 1/32 of the CUs idle) where
+        // K up to 2048 and a full wave of 64x192 tiles (at most 1/32 of the CUs idle) where
         // the 128x128, 64x256 and 64x128 tiles fill less of the chip or need a second
         // round: 1000x3000x777 + bias + GELU 256 tiles, 10.2 us against 10.9 for 192 of
         // 64x256; 2048x1536x512 5.8 against 6.3; 1024x3072x768 + bias + GELU 8.7 against
         // 9.4 with 128x128x32; 4096x768x1024 8.5 against 8.9 with the k-group 128x128
-        // tile.  From K = 2048 the k-group 128x128 tile leads (1000x3000x2048 + bias +
-        // GELU 19.2 against 20.2), and 240 tiles were not enough (1280x2304x1024: 9.45
-        // against 9.35).
-        // The 64x192 tile with 4 loader waves: 1000x3000x777 + bias + GELU 10.5 against
-        // 10.6 us without them, 1024x3072x768 + bias + GELU 9.1 against 9.4, 4096x768x1024
-        // 8.4 against 8.6.
-        if (r.K <= 1024 && t128 <= kCUs && t64x192 <= kCUs && t64x192 >= kCUs - kCUs / 32 &&
+        // tile; 240 tiles were not enough (1280x2304x1024: 9.45 against 9.35).  The tile
+        // is 4 waves of 64x48 on 16x16 MFMA blocks fed by 4 loader waves (each B fragment
+        // read once: ragged + GELU 10.0-10.2 us against 10.2-10.6 for 4 waves of 32x96 on
+        // 32x32 blocks; without epilogue 8.7 against 9.4), on 32-deep stages up to K =
+        // 1024 and 64-deep ones beyond (1000x3000x1536 13.6 against 14.0 for the k-group
+        // 128x128 tile, 1000x3000x2048 + bias + GELU 19.1 against 19.6, 2048x1536x2048
+        // 16.4 against 16.7).  From K = 4096 the k-group 128x128 tile leads
+        // (1000x3000x4096: 31.9 against 32.9).
+        if (r.K <= 2048 && t128 <= kCUs && t64x192 <= kCUs && t64x192 >= kCUs - kCUs / 32 &&
             t64x192 > t64x256 && t64x192 < t64x128)
-            return find_direct(64, 192, 32, 4, 1, 4);
+            return r.K <= 1024 ? find_direct(64, 192, 32, 4, 1, 4, 16) : find_direct(64, 192, 64, 4, 1, 4, 16);
         // at most one wave of 128x128 tiles with short K: 64x256 tiles (3000x1000x777: 11.6
         // us against 13.2 with 128x128x32; 2048x2048x777: 11.1-11.3 against 11.2-11.8; the
         // ragged 1000x3000x777, 192 tiles of either, 11.6 against 12.2 before the 64x192
@@ -768,6 +777,7 @@ mi355gemm_status mi355gemm_config_info(int config_id, mi355gemm_config_desc *out
     out->k_mult8 = c.k_mult8;
     out->pingpong = c.pingpong;
     out->loader_waves = c.loaders;
+    out->mfma_block = c.mfma_block;
     return MI355GEMM_OK;
 }
 

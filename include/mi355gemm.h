@@ -249,6 +249,9 @@ typedef struct {
     int loader_waves;               /* direct kernel: extra waves that issue every HBM -> LDS
                                        copy while the waves_m x waves_n grid only reads LDS
                                        and multiplies (0: the multiplying waves copy too) */
+    int mfma_block;                 /* MFMA block edge of the wave tiles: 32
+                                       (v_mfma_f32_32x32x16_f16) or 16
+                                       (v_mfma_f32_16x16x32_f16); 0 for the narrow kernel */
 } mi355gemm_config_desc;
 
 /* Number of compiled configurations (ids 0 .. n-1). Host-only. */
@@ -256,7 +259,7 @@ int mi355gemm_num_configs(void);
 
 /* Static name of a configuration, or NULL for an unknown id.  Host-only.  Names read
  * <d|p|s|n><BM>x<BN>x<BK>_w<waves_m>x<waves_n>[k<k_groups>]_...: d = direct HBM -> LDS kernel
- * (suffix [l<loader_waves>_]s<stages>), p = the same loader and tiles with two wave groups taking turns
+ * (suffix [l<loader_waves>_]s<stages>[_mf16], the last for 16x16 MFMA blocks), p = the same loader and tiles with two wave groups taking turns
  * (ping-pong; suffix s<stages>), s = register-staged kernel (suffix av/an: A in 16-byte /
  * 2-byte loads, bv/bn: B and C likewise), n = narrow vector-ALU kernel for N <= 8 (any
  * alignment), e.g. "d128x128x64_w2x2_s4", "d128x128x64_w2x2_l4_s4", "p256x256x32_w2x4_s4",

@@ -63,6 +63,7 @@ def test_config_table_is_consistent():
             assert c["threads"] == 256
             assert c["lds_bytes"] == (4 * 64 * 4 if c["k_groups"] > 1 else 0)
             assert c["a_vector"] == 0 and c["bc_vector"] == 0 and c["direct"] == 0
+            assert c["mfma_block"] == 0
             continue
         if c["direct"]:
             # ring of STAGES buffers of the A (BM x BK) and B (BK x BN) tiles, XOR-swizzled;
@@ -82,7 +83,10 @@ def test_config_table_is_consistent():
         else:
             assert "_l" not in c["name"]
         assert c["k_groups"] in (1, 2) and (c["direct"] or c["k_groups"] == 1)
-        assert c["block_m"] % (32 * c["waves_m"]) == 0 and c["block_n"] % (32 * c["waves_n"]) == 0
+        mf = c["mfma_block"]
+        assert mf in (16, 32) and (mf == 32 or (c["direct"] and c["k_groups"] == 1))
+        assert ("_mf16" in c["name"]) == (mf == 16)
+        assert c["block_m"] % (mf * c["waves_m"]) == 0 and c["block_n"] % (mf * c["waves_n"]) == 0
         assert c["block_k"] % 16 == 0
         # ping-pong: the direct loader with two groups of 4 waves, K % 8 == 0 only
         assert c["k_mult8"] == c["pingpong"]
@@ -363,12 +367,15 @@ def test_attention_argument_checks(args, want):
     ((6144, 2048, 2048), "d256x256x32_w2x4_s4"),      # 192 of 256x256, not 384 of 256x128
     ((2304, 2304, 2304), "d256x128x64_w2x2k2_s3"),    # 162 of 256x128, not 324 of 128x128
     ((3072, 2048, 2048), "d256x128x64_w2x2k2_s3"),    # 192 of 256x128, not 384 of 128x128
-    ((1000, 3000, 777), "d64x192x32_w2x2_l4_s4"),        # a full wave of 64x192 tiles (192 of
-    ((1000, 3000, 1024), "d64x192x32_w2x2_l4_s4"),       # 64x256 or 128x128), K <= 1024
-    ((2048, 1536, 512), "d64x192x32_w2x2_l4_s4"),
-    ((4096, 768, 1024), "d64x192x32_w2x2_l4_s4"),
-    ((1024, 3072, 768), "d64x192x32_w2x2_l4_s4"),
-    ((1000, 3000, 2048), "d128x128x64_w2x2k2_s4"),    # the same tile counts, longer K
+    ((1000, 3000, 777), "d64x192x32_w1x4_l4_s4_mf16"),   # a full wave of 64x192 tiles (192
+    ((1000, 3000, 1024), "d64x192x32_w1x4_l4_s4_mf16"),  # of 64x256 or 128x128): 32-deep
+    ((2048, 1536, 512), "d64x192x32_w1x4_l4_s4_mf16"),   # stages up to K = 1024,
+    ((4096, 768, 1024), "d64x192x32_w1x4_l4_s4_mf16"),
+    ((1024, 3072, 768), "d64x192x32_w1x4_l4_s4_mf16"),
+    ((1000, 3000, 1536), "d64x192x64_w1x4_l4_s3_mf16"),  # 64-deep ones up to 2048
+    ((1000, 3000, 2048), "d64x192x64_w1x4_l4_s3_mf16"),
+    ((2048, 1536, 2048), "d64x192x64_w1x4_l4_s3_mf16"),
+    ((1000, 3000, 4096), "d128x128x64_w2x2k2_s4"),    # the same tile counts, longer K
     ((1280, 2304, 1024), "d128x128x64_w2x2k2_s4"),    # 240 tiles of 64x192: not enough
     ((3000, 1000, 777), "d64x256x32_w1x4_s4"),        # 282 of 64x192: a second round
     ((256, 256, 256), "d64x128x32_w1x4_s4"),          # 8 tiles of 64x128
@@ -384,7 +391,7 @@ def test_selector_rules_pick_the_measured_winners(shape, want):
 @pytest.mark.parametrize("shape,ptr_off,want", [
     ((2048, 2047, 2048), 0, "d128x128x32_w2x2_l4_s4"),  # odd N: direct on the first 2040 columns
     ((8192, 8191, 8192), 0, "d256x256x32_w2x2_s4"),
-    ((1000, 3001, 777), 0, "d64x192x32_w2x2_l4_s4"),
+    ((1000, 3001, 777), 0, "d64x192x32_w1x4_l4_s4_mf16"),
     ((2048, 2048, 2048), 2, "d128x128x32_w2x2_l4_s4"),  # B and C only 2-byte aligned
     ((8192, 63, 8192), 0, "s64x64x64_w2x1_av_bn"),    # N < 64: no direct launch to split
     ((64, 775, 64), 0, "s64x64x64_w2x1_av_bn"),       # too few tiles (7 of 64x128)
@@ -441,7 +448,7 @@ def test_installed_choice_overrides_the_selector_for_its_exact_key_only():
         staged = g.config_id("s64x64x64_w2x1_an_bn")
         g.set_choice(1000, 3001, 777, "bias_gelu", False, False, staged)
         assert _select(1000, 3001, 777, epi=2) == staged
-        ragged = g.config_id("d64x192x32_w2x2_l4_s4")
+        ragged = g.config_id("d64x192x32_w1x4_l4_s4_mf16")
         assert _select(1000, 3000, 777, epi=2) == ragged              # class 1: the rules
         g.clear_choices()
         assert _select(2048, 2048, 2048) == rule
