@@ -83,32 +83,36 @@ __device__ __forceinline__ void tile_coords(int bid, int tiles_m, int tiles_n, i
 }
 
 // ---------------------------------------------------------------- epilogue ----------
-// GELU(x) = x * Phi(x) with Phi the standard normal CDF.  With h = Phi(-|x|) = erfc(z)/2,
-// z = |x| / sqrt 2, Phi(x) is 1 - h for x >= 0 and h for x < 0, so
+// GELU(x) = x * Phi(x) with Phi the standard normal CDF.  With h = Phi(-|x|), Phi(x) is
+// 1 - h for x >= 0 and h for x < 0, so
 //   GELU(x) = max(x, 0) - |x| h
-// for both signs: one erfc evaluation, no cancellation on the negative side, and no
-// select.  erfc(z) for z >= 0 uses the rational approximation of Abramowitz and Stegun,
-// Handbook of Mathematical Functions, formula 7.1.26 (after Hastings):
-// erfc(z) = t (a1 + t (a2 + t (a3 + t (a4 + t a5)))) exp(-z^2) with t = 1 / (1 + p z),
-// absolute error at most 1.5e-7.  The polynomial approximates erfc(z) exp(z^2), so the
-// relative error stays of that order in the tail as well, far below the 2^-11 relative
-// step of the fp16 result.  exp and the reciprocal are the hardware v_exp_f32 / v_rcp_f32.
+// for both signs: no cancellation on the negative side and no select.  h = 2^P(|x|) with
+// P a degree-7 polynomial fitted to log2 Phi(-z) on [0, 6] (least squares on Chebyshev
+// nodes; gelu_poly.py derives the coefficients).  In fp32 Horner form P is within 8e-6 of
+// log2 Phi(-z) there, so h is within 6e-6 relative, far below the 2^-11 relative step of
+// the fp16 result.  The leading coefficient is negative and P falls from -29.9 at z = 6
+// on, so for x <= -6 the result |x| h rounds to zero in fp16 as x Phi(x) does; Horner's
+// rule overflows to -inf for large z, and 2^-inf is 0.  One transcendental (the hardware
+// v_exp_f32) and no reciprocal.
 __device__ __forceinline__ float gelu_erf(float x)
 {
-    // the coefficients below are a1..a5 halved (exact in binary), so the polynomial times
-    // exp(-z^2) is h = erfc(z) / 2 = Phi(-|x|) directly, and p is premultiplied by 1/sqrt(2).
-    constexpr float p = 0.3275911f * 0.70710678118654752f;
-    constexpr float a1 = 0.5f * 0.254829592f, a2 = 0.5f * -0.284496736f, a3 = 0.5f * 1.421413741f,
-                    a4 = 0.5f * -1.453152027f, a5 = 0.5f * 1.061405429f;
-    constexpr float kHalfLog2e = 0.72134752044448170f;   // log2(e) / 2: exp(-z^2) = 2^(-x^2 log2(e) / 2)
-    // x capped at the largest finite float before taking |x|: for x = +inf the last step
-    // then gives inf - 3.4e38 * 0 = inf (uncapped, inf * 0 = NaN); x = -inf keeps |x| =
-    // inf, so -inf * 0 = NaN, as x * Phi(x) evaluates in IEEE arithmetic; a NaN x reaches
-    // the result through h; finite x are unchanged
+    constexpr float c0 = -9.999943376e-01f, c1 = -1.151269197e+00f, c2 = -4.584097862e-01f,
+                    c3 = -5.402068794e-02f, c4 = 8.539461531e-03f, c5 = -9.388679173e-04f,
+                    c6 = 6.268139987e-05f, c7 = -1.889626219e-06f;
+    const float z = fabsf(x);
+    float q = fmaf(c7, z, c6);
+    q = fmaf(q, z, c5);
+    q = fmaf(q, z, c4);
+    q = fmaf(q, z, c3);
+    q = fmaf(q, z, c2);
+    q = fmaf(q, z, c1);
+    q = fmaf(q, z, c0);
+    const float h = __builtin_amdgcn_exp2f(q);                  // Phi(-|x|)
+    // the multiplier |x| is capped at the largest finite float for x = +inf: h is 0 there,
+    // and the result is inf - 3.4e38 * 0 = inf (uncapped, inf * 0 = NaN).  x = -inf keeps
+    // |x| = inf, so -inf * 0 = NaN, as x * Phi(x) evaluates in IEEE arithmetic; a NaN x
+    // reaches the result through h; finite x are unchanged.
     const float ax = fabsf(fminf(x, 3.4028234663852886e38f));
-    const float t = __builtin_amdgcn_rcpf(fmaf(p, ax, 1.0f));
-    const float poly = t * fmaf(t, fmaf(t, fmaf(t, fmaf(t, a5, a4), a3), a2), a1);
-    const float h = poly * __builtin_amdgcn_exp2f(-(x * x) * kHalfLog2e);   // Phi(-|x|)
     return fmaf(-ax, h, fmaxf(x, 0.0f));
 }
 
