@@ -317,23 +317,26 @@ def test_rejects_bad_tensors():
 
 # ---- several workgroups per compute unit ------------------------------------------------
 
-def test_many_workgroups_per_cu_bitexact_every_config():
-    """4096 x 4096 x 1024 gives every tile shape several workgroups per compute unit (64
+@pytest.mark.parametrize("K", [1024, 1019])
+def test_many_workgroups_per_cu_bitexact_every_config(K):
+    """4096 x 4096 x K gives every tile shape several workgroups per compute unit (64
     of 256 x 256 up to 2048 of 64 x 128 per 256 CUs), so workgroups of the 64 KiB-ring
     tiles share a CU, its LDS and its memory pipes, and each ring slot is refilled 8 or
     more times per tile.  A copy that overtook a fragment read still queued for its slot
-    would corrupt operands.  Integer inputs: every partial sum is an integer below 2^24,
-    exact in fp32 in any order, so every configuration must give the oracle's bits, on
-    two launches in a row (the second starting while the first drains)."""
+    would corrupt operands.  K = 1019 runs the K-tail variant: the last stage's straddling
+    A chunk is patched in LDS (by the loader waves where the tile has them) between the
+    copy landing and the barrier that releases it.  Integer inputs: every partial sum is
+    an integer below 2^24, exact in fp32 in any order, so every configuration must give
+    the oracle's bits, on two launches in a row (the second starting while the first
+    drains)."""
     M = N = 4096
-    K = 1024
     A, B = _small_int_inputs(M, N, K)
     ref = oracle.gemm(A, B)
     Ad, Bd = _dev(A), _dev(B)
     for cfg in all_configs():
         if not cfg["direct"] or not _compatible(cfg, M, N, K):
             continue
-        print("many workgroups", cfg["name"], flush=True)
+        print("many workgroups", cfg["name"], K, flush=True)
         outs = [torch.empty((M, N), dtype=torch.float16, device=DEV) for _ in range(2)]
         for o in outs:
             g.gemm(Ad, Bd, out=o, config=cfg["id"])
