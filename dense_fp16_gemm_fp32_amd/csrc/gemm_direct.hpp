@@ -516,23 +516,22 @@ __device__ __forceinline__ void tile_to_lds(const typename T::AccT (&acc)[T::FM]
 // 8192^3 unchanged (interleaved on one box); the non-temporal hint alone did not help.
 constexpr int kStoreWriteThrough = 1 | 16;
 
-// All threads: copy the LDS tile to C, 16 bytes per lane.  Rows past M fall outside the
-// C descriptor's range, 8-column chunks past N are pushed out of range (N % 8 == 0 here,
-// so a chunk is either wholly inside or wholly outside).
+// All threads, the loader waves included: copy the LDS tile to C, 16 bytes per lane.  Rows
+// past M fall outside the C descriptor's range, 8-column chunks past N are pushed out of
+// range (N % 8 == 0 here, so a chunk is either wholly inside or wholly outside).
 template <class T>
 __device__ __forceinline__ void lds_to_c(const GemmArgs &p, int m0, int n0, int rows_valid,
                                          const char *ctile)
 {
     constexpr int CW = T::BN / 8;
-    constexpr int PER = T::BM * CW / T::NTC;
-    static_assert(T::BM * CW % T::NTC == 0, "tile must split evenly over the threads");
-    if (T::NL > 0 && (int)threadIdx.x >= T::NTC) return;   // loader waves store nothing
+    constexpr int PER = T::BM * CW / T::NT;
+    static_assert(T::BM * CW % T::NT == 0, "tile must split evenly over the threads");
     const int cols_valid = p.N - n0;
     const __amdgpu_buffer_rsrc_t c_rs =
         make_rsrc(p.C + (int64_t)m0 * p.ldc + n0, span_bytes(rows_valid, p.ldc, cols_valid));
 #pragma unroll
     for (int k = 0; k < PER; ++k) {
-        const int q = threadIdx.x + k * T::NTC;
+        const int q = threadIdx.x + k * T::NT;
         const int r = q / CW, c = q % CW;
         const u32x4 v = *reinterpret_cast<const u32x4 *>(ctile + (r * T::BN + 8 * c_phys<T>(c, r)) * 2);
         const uint32_t off = masked_offset((uint32_t)(r * p.ldc + 8 * c) * 2u, 8 * c < cols_valid);
