@@ -494,16 +494,15 @@ __device__ __forceinline__ void tile_to_lds(const typename T::AccT (&acc)[T::FM]
 #pragma unroll
             for (int i = I0; i < I1; ++i) {
                 const int r = row0 + i * T::MF + (lane & (T::MF - 1));
-                uint32_t hb[4];
+                // built as one vector, so that each pair of halves lands in one register
+                // (v_fma_mixlo_f16 / v_fma_mixhi_f16) with no shift-and-or packing
+                f16x4 hv;
 #pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const f16 h = (f16)epilogue_op<EPI>(acc[i][j][4 * g + e], bv[e]);
-                    hb[e] = __builtin_bit_cast(uint16_t, h);
-                }
+                for (int e = 0; e < 4; ++e) hv[e] = (f16)epilogue_op<EPI>(acc[i][j][4 * g + e], bv[e]);
                 // the 4 columns' place in their 16-byte chunk: bit 2 of n (= half for MF = 32)
                 const int sub = T::MF == 32 ? 4 * half : (n & 4);
                 char *dst = ctile + (r * T::BN + 8 * c_phys<T>(c, r) + sub) * 2;
-                *reinterpret_cast<u32x2 *>(dst) = u32x2{hb[0] | (hb[1] << 16), hb[2] | (hb[3] << 16)};
+                *reinterpret_cast<f16x4 *>(dst) = hv;
             }
         }
     }
