@@ -184,6 +184,43 @@ def test_random_parity_every_config_and_epilogue(shape):
             assert_parity(C, refs[e], "%s %s %s" % (cfg["name"], shape, e))
 
 
+def _seeded_shapes(n=40, seed=20261203):
+    """Shapes drawn from a fixed seed: M and K anywhere in [1, 700) and [1, 1500), N a
+    multiple of 8 (the direct kernels' column granularity) seven times in ten and any
+    value otherwise."""
+    rng = np.random.default_rng(seed)
+    shapes = []
+    for _ in range(n):
+        M = int(rng.integers(1, 700))
+        K = int(rng.integers(1, 1500))
+        N = int(rng.integers(1, 88)) * 8 if rng.random() < 0.7 else int(rng.integers(1, 700))
+        shapes.append((M, N, K))
+    return shapes
+
+
+RANDOM_SHAPES = _seeded_shapes()
+
+
+@pytest.mark.parametrize("shape", RANDOM_SHAPES, ids=["%dx%dx%d" % s for s in RANDOM_SHAPES])
+def test_seeded_random_shapes_every_config_and_epilogue(shape):
+    """Breadth beyond the hand-picked shapes: every configuration that can serve the shape,
+    and the selector's own choice (which splits columns past a multiple of 8 off to the
+    narrow kernel), with every epilogue, against the oracle."""
+    M, N, K = shape
+    A, B, bias = workloads.make_inputs(M, N, K, "normal", with_bias=True, seed=3 * M + 5 * N + 7 * K)
+    refs = {e: oracle.gemm(A, B, bias, e) for e in EPIS}
+    for e in EPIS:
+        print("selector", shape, e, flush=True)
+        assert_parity(_run(A, B, bias, e), refs[e], "selector %s %s" % (shape, e))
+    for cfg in all_configs():
+        if not _compatible(cfg, M, N, K):
+            continue
+        for e in EPIS:
+            print("config", cfg["name"], shape, e, flush=True)
+            C = _run(A, B, bias, e, config=cfg["id"])
+            assert_parity(C, refs[e], "%s %s %s" % (cfg["name"], shape, e))
+
+
 # ---- the workloads at full size, in the launch configuration the benchmark uses --------
 
 def _workload_cases():
